@@ -1,0 +1,111 @@
+"""Pins of the input generator and the algorithmic byte counter against the
+numbers the pages print (fixtures under tests/golden/, each citing its page).
+"""
+import collections
+import os
+
+import numpy as np
+import pytest
+
+import workloads as W
+from heterogeneous_adapters_amd import traffic
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read(name):
+    rows = []
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _lru_hit_rate(n_adapters, slots, s, requests, seed):
+    zs = W.ZipfSampler(n_adapters, s, seed)
+    lru, hits = collections.OrderedDict(), 0
+    for _ in range(requests):
+        a = zs.sample()
+        if a in lru:
+            hits += 1
+            lru.move_to_end(a)
+        else:
+            if len(lru) >= slots:
+                lru.popitem(last=False)
+            lru[a] = True
+    return hits / requests
+
+
+@pytest.mark.parametrize("row", _read("mlsa_lru_hit_rates.txt"))
+def test_zipf_sampler_reproduces_lru_hit_rates(row):
+    """The bounded-Zipf sampler drives an LRU cache to the page's hit rates."""
+    s, slots, pct = float(row[0]), int(row[1]), int(row[2])
+    h = _lru_hit_rate(500, slots, s, 200_000, 7)
+    assert round(100 * h) == pct, (s, slots, h)
+
+
+def test_zipf_ids_properties():
+    ids = W.zipf_ids(20000, 50, 1.1, 3)
+    assert ids.min() >= 0 and ids.max() < 50
+    counts = np.bincount(ids, minlength=50)
+    # popularity decreases with id (law 1/i^s): id 0 is the hottest and the
+    # ratio of the first two is near 2^1.1
+    assert counts.argmax() == 0
+    assert abs(counts[0] / counts[1] - 2 ** 1.1) < 0.15
+    assert np.array_equal(ids, W.zipf_ids(20000, 50, 1.1, 3))
+
+
+MEM = {k: v for k, v in _read("mlsa_memory_arithmetic.txt")}
+LLAMA3_8B = [(4096, 4096), (4096, 1024), (4096, 1024), (4096, 4096), (4096, 14336),
+             (4096, 14336), (14336, 4096)]
+
+
+def _approx(key, value):
+    txt = MEM[key]
+    assert txt.startswith("~")
+    want = float(txt[1:])
+    digits = len(txt[1:].split("e")[0].replace(".", ""))
+    assert float(f"{value:.{digits}g}") == pytest.approx(want, rel=1e-12), (key, value, want)
+
+
+def test_memory_arithmetic_matches_page():
+    assert traffic.adapter_params(1, LLAMA3_8B) == int(MEM["params_per_unit_rank_per_layer"])
+    assert traffic.adapter_params(16, LLAMA3_8B) == int(MEM["params_per_layer_r16"])
+    _approx("params_total_r16", 32 * traffic.adapter_params(16, LLAMA3_8B))
+    _approx("bytes_total_r16", 2 * 32 * traffic.adapter_params(16, LLAMA3_8B))
+    _approx("bytes_total_r64", 2 * 32 * traffic.adapter_params(64, LLAMA3_8B))
+    _approx("params_attention_only_r16", 32 * traffic.adapter_params(16, LLAMA3_8B[:4]))
+    _approx("bytes_attention_only_r16", 2 * 32 * traffic.adapter_params(16, LLAMA3_8B[:4]))
+    _approx("bytes_100_adapters_r16", 100 * 2 * 32 * traffic.adapter_params(16, LLAMA3_8B))
+    _approx("bytes_32_slots_r64", 32 * 2 * 32 * traffic.adapter_params(64, LLAMA3_8B))
+    _approx("bytes_32_slots_r8", 32 * 2 * 32 * traffic.adapter_params(8, LLAMA3_8B))
+
+
+def test_algorithmic_bytes_counts_distinct_adapters_once():
+    ranks = np.array([8, 16, 64, 32], np.int32)
+    # 64 tokens on one adapter read that adapter once; 4 distinct read 4 sets
+    one = traffic.split_bytes(np.zeros(64, np.int32), ranks, 4096, 4096, 2)
+    many = traffic.split_bytes(np.arange(64, dtype=np.int32) % 4, ranks, 4096, 4096, 2)
+    act = 64 * 4096 * 2
+    assert one[0] == act + 8 * 4096 * 2 and one[1] == 2 * act + 8 * 4096 * 2
+    assert many[0] == act + 120 * 4096 * 2 and many[1] == 2 * act + 120 * 4096 * 2
+    # invalid and base-only tokens move no adapter weights and no activations
+    ids = np.array([-1, 7, 2, 2], np.int32)
+    s, e, m = traffic.split_bytes(ids, ranks, 256, 512, 2)
+    assert s == (2 * 256 + 64 * 256) * 2 and e == (2 * 2 * 512 + 64 * 512) * 2
+    assert traffic.algorithmic_flops(ids, ranks, 256, 512) == 2 * 2 * 64 * 768
+
+
+def test_page_tables_cover_pool_once():
+    ranks = np.array([8, 16, 24, 64, 1], np.int32)
+    shapes = [("a", 300, 700), ("b", 1000, 64)]
+    for scatter in (False, True):
+        tabs, npg = W.plan_tables(ranks, shapes, 128, scatter, 5)
+        allp = np.concatenate([np.concatenate([t.a_pages, t.b_pages]) for t in tabs])
+        assert np.array_equal(np.sort(allp), np.arange(npg))
+        for t in tabs:
+            G = (ranks + 15) // 16
+            assert np.array_equal(np.diff(t.a_indptr), G * ((t.d_in + 127) // 128))
+            assert np.array_equal(np.diff(t.b_indptr), G * ((t.d_out + 127) // 128))
