@@ -1,0 +1,72 @@
+// Kernel argument blocks and launchers of liblora (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lora_plan.h"
+
+namespace lora {
+
+constexpr int kSegScanThreads = 1024;
+// LDS per work-group: the shrink needs max(8 token rows x 1024 fp32 columns,
+// three waves' partial MFMA tiles = 3 x 8 tiles x 64 lanes x 4 floats);
+// the expand needs v of up to 64 tokens x 128 ranks in fp32.
+constexpr int kShrinkSmem = (kValuTokens * kKSlice * 4 > 3 * 8 * 64 * 4 * 4) ? kValuTokens * kKSlice * 4 : 3 * 8 * 64 * 4 * 4;
+constexpr int kExpandSmem = kExpandTokens * 128 * 4;
+static_assert(kValuTokens * kKSlice * 4 <= kShrinkSmem, "shrink LDS");
+
+// One projection as the kernels see it.
+struct KProj {
+  const void* X;
+  const void* Yb;
+  void* Y;
+  float* v;                 // shrink output / expand input: [slices][v_stride] fp32
+  const int32_t* a_indptr;
+  const int32_t* a_pages;
+  const int32_t* b_indptr;
+  const int32_t* b_pages;
+  int64_t ldx, ldyb, ldy;
+  int32_t d_in, d_out;
+  int32_t nq;   // shrink slices written: ceil(d_in / 1024)
+  int32_t njs;  // expand column slices: ceil(d_out / 256)
+  int32_t nv;   // v slices the expand sums
+  int32_t pad;
+};
+
+struct KArgs {
+  KProj p[kProjsPerLaunch];
+  const int32_t* perm;
+  const int32_t* seg_indptr;
+  const int32_t* seg_adapter;
+  const int32_t* v_indptr;
+  const int32_t* shr_ptr;
+  const int32_t* exp_ptr;
+  int32_t* counts;
+  const int32_t* rank;
+  const float* alpha;
+  const void* pool;
+  int64_t v_stride;
+  int32_t num_pages;
+  int32_t pw_log2;
+  int32_t T;
+  int32_t np;
+};
+
+struct SegOut {
+  int32_t* perm;
+  int32_t* seg_indptr;
+  int32_t* seg_adapter;
+  int32_t* v_indptr;
+  int32_t* shr_ptr;
+  int32_t* exp_ptr;
+  int32_t* counts;
+};
+
+hipError_t launch_build_segments(const int32_t* ids, int T, int N, const int32_t* rank, int32_t* hist,
+                                 const SegOut& out, hipStream_t stream);
+hipError_t launch_shrink(const KArgs& K, int dtype, int grid, hipStream_t stream);
+hipError_t launch_expand(const KArgs& K, int dtype, int grid, hipStream_t stream);
+hipError_t occupancy(int dtype, int* shrink_blocks, int* expand_blocks);
+
+}  // namespace lora

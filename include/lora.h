@@ -1,0 +1,236 @@
+/*
+ * lora.h -- C ABI of liblora.so, the MI355X (gfx950) multi-LoRA adapter
+ * branch over a paged pool of heterogeneous-rank adapters.
+ *
+ * Sources (the three web pages this library follows):
+ *   [MLSP] "Multi-LoRA Serving in Production: Architecture, Dynamic Adapter
+ *          Swapping, and GPU Memory Management" (llms.blog)
+ *   [MLSA] "Multi-LoRA Serving Architecture: Serving Hundreds of Fine-Tuned
+ *          Adapters on One GPU with vLLM and S-LoRA (2026)"
+ *   [LAST] "LoRA Adapters at Serve Time with vLLM Multi-LoRA"
+ *
+ * What the library computes, for every token t of a mixed batch whose
+ * adapter is a = ids[t] (the adapted-layer equation of [MLSP] "The
+ * Mathematical Anatomy of Heterogeneous Batches"):
+ *
+ *     Y[t] = Y_base[t] + (alpha_a / r_a) * (X[t] A_a) B_a
+ *
+ * A_a is d_in x r_a and B_a is r_a x d_out.  The base product X W0 is not
+ * computed here: the caller passes it as Y_base.  A_a B_a is never formed
+ * ([LAST] "Architecture of Multi-LoRA in vLLM"), each adapter is read at its
+ * own rank with no padding to the largest rank in the batch ([MLSP] "Multi-
+ * Size Batched Gather Kernels (MBGMV and MBGMM)"), and the weights are read
+ * straight from a pool of fixed-size pages through page tables ([MLSP]
+ * "Unified Paging Architecture"; [MLSA] "S-LoRA unified paging").
+ *
+ * General rules
+ *  - Pointers are device pointers unless a comment says "host".  The caller
+ *    owns every buffer; the library allocates no memory and keeps no state
+ *    between calls except cached device properties (reentrant).
+ *  - Every call enqueues asynchronously on `stream` (a hipStream_t passed as
+ *    void*; NULL = the default stream) and never synchronises the device.
+ *  - Host-side argument checks run before anything is enqueued; on error the
+ *    call returns a negative status and enqueues nothing.  Data-dependent
+ *    conditions found on the device (bad ids, bad ranks, page ids outside
+ *    the pool) never abort: they are recorded in the segment counters
+ *    (see lora_segments_t.counts) and the affected rows keep Y_base.
+ *  - No exception crosses this interface.
+ *
+ * Element types: LORA_DTYPE_BF16 -> X, Y_base, Y and the pool hold bf16;
+ * LORA_DTYPE_F32 -> all fp32 (validation mode).  Rank-r intermediates,
+ * alpha and every accumulation are fp32; Y is Y_base + s*acc computed in
+ * fp32 and rounded once (round to nearest even) to the element type.
+ */
+#ifndef LORA_H
+#define LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lora_status_t;
+#define LORA_OK 0
+#define LORA_ERR_INVALID_ARG (-1) /* null pointer, negative size, bad stride */
+#define LORA_ERR_RANK (-2)        /* a rank outside [1, LORA_MAX_RANK] (validator) */
+#define LORA_ERR_PAGE_RANGE (-3)  /* page id outside the pool (validator) */
+#define LORA_ERR_WORKSPACE (-4)   /* workspace or segment buffer too small */
+#define LORA_ERR_HIP (-5)         /* a HIP runtime call or kernel launch failed */
+#define LORA_ERR_UNSUPPORTED (-6) /* unknown dtype, page geometry, too many projections */
+#define LORA_ERR_ALIGNMENT (-7)   /* pointer or leading dimension not 16-byte aligned */
+
+#define LORA_DTYPE_F32 0
+#define LORA_DTYPE_BF16 1
+
+#define LORA_PAGE_ROWS 16    /* ranks per page ("16-row pages") */
+#define LORA_MAX_RANK 128
+#define LORA_KSLICE 1024     /* input columns per shrink partial sum */
+#define LORA_MAX_ADAPTERS (1 << 20)
+
+/* Adapter set: one rank and one alpha per adapter, shared by every layer and
+ * projection (each sequence's adapter has its own rank r_i, [MLSP]
+ * "Mathematical Anatomy").  rank[] and alpha[] are device arrays of
+ * num_adapters entries. */
+typedef struct {
+  const int32_t* rank;
+  const float* alpha;
+  int32_t num_adapters;
+} lora_adapters_t;
+
+/* The physical page pool ([MLSP] "Unified Paging Architecture": fixed-size
+ * pages; adapter weights sliced along their rank dimension).  Page p is the
+ * 16 x page_width block of elements starting at base + p*16*page_width.
+ * base must be 16-byte aligned; page_width a power of two in [64, 65536]. */
+typedef struct {
+  void* base;
+  int32_t num_pages;
+  int32_t page_width;
+  int32_t dtype; /* LORA_DTYPE_* */
+} lora_pool_t;
+
+/* One adapted projection (one layer's q_proj, say) of the batch.
+ *
+ * X      : [T][ldx]  row-major activations, ldx >= d_in
+ * Y_base : [T][ldyb] base output X W0, ldyb >= d_out
+ * Y      : [T][ldy]  output; may alias Y_base (then ldy must equal ldyb)
+ * d_in, d_out : multiples of 8; ldx, ldyb, ldy multiples of 8 elements;
+ *               X, Y_base, Y 16-byte aligned.
+ *
+ * Page tables (CSR over adapters, int32 device arrays), in the orientation of
+ * [MLSA] "Context and Background" (A is r x d_in, B is d_out x r), sliced into
+ * 16-rank groups g and page_width-wide blocks c of the feature dimension:
+ *   A: page a_pages[a_indptr[a] + g*ceil(d_in/PW) + c] holds ranks 16g..16g+15
+ *      (rows) x inputs c*PW..c*PW+PW-1 (columns): element (rank k, input i)
+ *      at in-page offset (k-16g)*PW + (i-c*PW).
+ *   B: page b_pages[b_indptr[a] + g*ceil(d_out/PW) + c] holds outputs
+ *      c*PW..c*PW+PW-1 (rows) x ranks 16g..16g+15 (columns): element
+ *      (output j, rank k) at in-page offset (j-c*PW)*16 + (k-16g).
+ * Adapter a owns ceil(r_a/16)*ceil(d/PW) slots of each table.  Page rows or
+ * columns beyond r_a or d are never read. */
+typedef struct {
+  const void* X;
+  int64_t ldx;
+  const void* Y_base;
+  int64_t ldyb;
+  void* Y;
+  int64_t ldy;
+  int32_t d_in;
+  int32_t d_out;
+  const int32_t* a_indptr;
+  const int32_t* a_pages;
+  const int32_t* b_indptr;
+  const int32_t* b_pages;
+} lora_proj_t;
+
+/* Segments: the batch's tokens grouped by adapter ([MLSP] "Segmented Gather
+ * Matrix-Vector Multiplication (SGMV)": requests grouped by target adapter),
+ * plus the work plan the kernels walk.  All arrays are device memory carved
+ * from one caller buffer by lora_segments_init (host fields T and
+ * num_adapters record the capacity).  S_max = min(T, num_adapters).
+ *   perm[T]               grouped valid tokens (ascending token index inside a
+ *                         group, groups in ascending adapter id), then the
+ *                         tokens that use no adapter, ascending
+ *   seg_indptr[S_max+1]   token range of segment s in perm
+ *   seg_adapter[S_max]    adapter of segment s
+ *   v_indptr[S_max+1]     offset of segment s in the ragged rank-r
+ *                         intermediate v: v[v_indptr[s] + i*r + k]
+ *   shr_ptr[S_max+1], exp_ptr[S_max+1]   work-plan prefix sums (internal)
+ *   counts[8]             {S, n_invalid, T_valid, V_total, shrink items,
+ *                         expand items, device error flags, reserved}
+ * A token is valid when 0 <= ids[t] < num_adapters and its adapter's rank is
+ * in [1, 128].  ids[t] == -1 marks a base-model token ([MLSA] "What vLLM
+ * actually gives you": base-model requests share the server); other invalid
+ * tokens are counted in n_invalid.  Neither kind gets an adapter term. */
+typedef struct {
+  int32_t T;
+  int32_t num_adapters;
+  int32_t* perm;
+  int32_t* seg_indptr;
+  int32_t* seg_adapter;
+  int32_t* v_indptr;
+  int32_t* shr_ptr;
+  int32_t* exp_ptr;
+  int32_t* counts;
+} lora_segments_t;
+
+#define LORA_COUNT_S 0
+#define LORA_COUNT_INVALID 1
+#define LORA_COUNT_T_VALID 2
+#define LORA_COUNT_V_TOTAL 3
+#define LORA_COUNT_FLAGS 6
+#define LORA_FLAG_PAGE_RANGE 1 /* a page id outside the pool was skipped (read as 0) */
+
+/* Bytes of the device buffer that holds segments for T tokens and
+ * num_adapters adapters. */
+size_t lora_segments_size(int32_t T, int32_t num_adapters);
+
+/* Fill *out with pointers carved from `buf` (device, `bytes` long, 16-byte
+ * aligned).  Enqueues nothing.  Errors: INVALID_ARG, WORKSPACE. */
+lora_status_t lora_segments_init(void* buf, size_t bytes, int32_t T, int32_t num_adapters,
+                                 lora_segments_t* out);
+
+/* Workspace bytes for lora_build_segments and lora_apply with n_projs
+ * projections whose largest input width is max_d_in. */
+size_t lora_workspace_size(int32_t T, int32_t num_adapters, int32_t n_projs, int32_t max_d_in);
+
+/* Number of shrink partial slices for an input width: ceil(d_in / 1024). */
+int32_t lora_v_slices(int32_t d_in);
+
+/* Group the batch's tokens by adapter and build the work plan (a
+ * deterministic stable counting sort; [MLSP] SGMV grouping).  ids: device
+ * [T].  segs: laid out by lora_segments_init with capacity >= (T, N).  The
+ * result depends only on ids and ranks; build once per batch and reuse for
+ * every layer and projection.  Errors: INVALID_ARG, WORKSPACE, HIP. */
+lora_status_t lora_build_segments(const int32_t* ids, int32_t T, const lora_adapters_t* adapters,
+                                  const lora_segments_t* segs, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* Shrink ([MLSP] SGMV: v_i = x_i A_i, the rank-r intermediate) for one
+ * projection.  v: device fp32 [lora_v_slices(d_in)][v_stride]; slice q holds
+ * the partial sum over inputs q*1024 .. min((q+1)*1024, d_in)-1 in the ragged
+ * layout of v_indptr; v = sum of the slices in ascending q.  v_stride >=
+ * T*128.  Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED, HIP. */
+lora_status_t lora_shrink(const lora_proj_t* proj, const lora_adapters_t* adapters,
+                          const lora_segments_t* segs, const lora_pool_t* pool, float* v,
+                          int64_t v_stride, void* stream);
+
+/* Expand ([MLSP] SGMV: y_i = v_i B_i scaled by alpha_i/r_i and added to the
+ * base output) for one projection.  v as written by lora_shrink (v_slices
+ * slices, summed in ascending order) or any v with v_slices = 1.  Rows of
+ * tokens without an adapter receive Y_base.  Errors as lora_shrink. */
+lora_status_t lora_expand(const lora_proj_t* proj, const lora_adapters_t* adapters,
+                          const lora_segments_t* segs, const lora_pool_t* pool, const float* v,
+                          int32_t v_slices, int64_t v_stride, void* stream);
+
+/* The fused adapter branch for n_projs projections of one batch: shrink then
+ * expand, two kernel launches per group of up to 16 projections.
+ *   ids != NULL, segs != NULL : build segments into *segs, then apply
+ *   ids != NULL, segs == NULL : build segments inside the workspace
+ *   ids == NULL, segs != NULL : reuse prebuilt segments
+ * projs: host array of n_projs descriptors.  T must equal the segments' T.
+ * ws: device workspace of lora_workspace_size(T, N, n_projs, max d_in) bytes.
+ * Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED, WORKSPACE, HIP. */
+lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_t T,
+                         const lora_proj_t* projs, int32_t n_projs,
+                         const lora_adapters_t* adapters, const lora_pool_t* pool, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Host-side check of page tables (all arguments host copies): every adapter
+ * owns exactly ceil(r/16)*ceil(d/PW) slots and every page id lies in
+ * [0, num_pages) ([MLSA] "Trade-offs, Gotchas": validate shape and rank
+ * before admission).  Returns OK, RANK, PAGE_RANGE or INVALID_ARG. */
+lora_status_t lora_validate_tables(int32_t num_adapters, const int32_t* rank_host, int32_t d_in,
+                                   int32_t d_out, int32_t page_width, int32_t num_pages,
+                                   const int32_t* a_indptr_host, const int32_t* a_pages_host,
+                                   const int32_t* b_indptr_host, const int32_t* b_pages_host);
+
+/* Static string for a status code. */
+const char* lora_status_string(lora_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_H */

@@ -19,7 +19,9 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-from .build import LIB_PATH, build
+from . import build as _build
+
+LIB_PATH = _build.LIB_PATH
 
 DT_F32, DT_BF16 = 0, 1
 _lib = None
@@ -33,7 +35,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            build()
+            _build.build()
         L = ctypes.CDLL(LIB_PATH)
         L.oracle_segments.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
         L.oracle_segments.restype = ctypes.c_int

@@ -1,0 +1,159 @@
+"""Host-side tests of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status codes
+before touching the device (these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from heterogeneous_adapters_amd import lora
+from heterogeneous_adapters_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora.h")
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(lora_[a-z_]+)\s*\(", txt, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    assert os.path.exists(LIB_PATH), "run __graft_entry__.build() first"
+    L = ctypes.CDLL(LIB_PATH)
+    fns = header_functions()
+    assert set(fns) >= {"lora_build_segments", "lora_shrink", "lora_expand", "lora_apply",
+                        "lora_workspace_size", "lora_status_string"}
+    assert set(fns) == set(lora.EXPORTS)
+    for f in fns:
+        assert hasattr(L, f), f
+
+
+def test_status_strings():
+    L = lora.lib()
+    for code in range(-7, 1):
+        assert lora.lora_status_string(code) not in ("", "unknown status")
+    assert lora.lora_status_string(-99) == "unknown status"
+    assert L.lora_v_slices(1) == 1 and L.lora_v_slices(1024) == 1 and L.lora_v_slices(1025) == 2
+    assert L.lora_v_slices(11008) == 11 and L.lora_v_slices(0) == 0
+
+
+def test_sizes():
+    L = lora.lib()
+    assert L.lora_segments_size(-1, 4) == 0 and L.lora_segments_size(4, 0) == 0
+    s = L.lora_segments_size(1024, 1000)
+    assert s >= 4 * (1024 + 4 * 1001 + 1000 + 8)
+    w = L.lora_workspace_size(1024, 1000, 3, 4096)
+    assert w >= s + 3 * 4 * 1024 * 128 * 4
+    # projections beyond one launch reuse the same v area
+    assert L.lora_workspace_size(8, 4, 16, 256) == L.lora_workspace_size(8, 4, 40, 256)
+
+
+class _Buf:
+    """Host buffers whose addresses stand in for device pointers; every call
+    below fails host-side validation, so nothing is dereferenced."""
+
+    def __init__(self):
+        self.a = np.zeros(4096, np.float32)
+        self.base = self.a.ctypes.data
+        assert self.base % 16 == 0
+
+    def p(self, off=0):
+        return self.base + off
+
+
+def _descs(b, **kw):
+    d = dict(T=8, N=4, d_in=64, d_out=64, pw=64, dtype=lora.LORA_DTYPE_BF16)
+    d.update(kw)
+    ad = lora.lora_adapters_t(b.p(), b.p(64), d["N"])
+    pool = lora.lora_pool_t(kw.get("pool_base", b.p()), 4, d["pw"], d["dtype"])
+    proj = lora.lora_proj_t(kw.get("X", b.p()), kw.get("ldx", d["d_in"]), b.p(), d["d_out"],
+                            kw.get("Y", b.p(256)), kw.get("ldy", d["d_out"]), d["d_in"], d["d_out"],
+                            b.p(), b.p(), b.p(), b.p())
+    seg = lora.lora_segments_t()
+    assert lora.lib().lora_segments_init(ctypes.c_void_p(b.p()), 1 << 14, d["T"], d["N"], ctypes.byref(seg)) == 0
+    return ad, pool, proj, seg
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(d_in=60), -1), (dict(d_out=12), -1), (dict(ldx=32), -1), (dict(X=0), -1),
+    (dict(pw=96), -6), (dict(pw=32), -6), (dict(dtype=7), -6),
+    (dict(X="mis"), -7), (dict(ldy=68), -7), (dict(pool_base="mis"), -7),
+])
+def test_shrink_expand_apply_reject_bad_arguments(case, code):
+    b = _Buf()
+    kw = dict(case)
+    if kw.get("X") == "mis":
+        kw["X"] = b.p(2)
+    if kw.get("pool_base") == "mis":
+        kw["pool_base"] = b.p(4)
+    ad, pool, proj, seg = _descs(b, **kw)
+    L = lora.lib()
+    r = ctypes.byref
+    v = ctypes.c_void_p(b.p())
+    assert L.lora_shrink(r(proj), r(ad), r(seg), r(pool), v, 8 * 128, None) == code
+    assert L.lora_expand(r(proj), r(ad), r(seg), r(pool), v, 1, 8 * 128, None) == code
+    arr = (lora.lora_proj_t * 1)(proj)
+    assert L.lora_apply(None, r(seg), 8, arr, 1, r(ad), r(pool), v, 1 << 30, None) == code
+
+
+def test_other_rejections():
+    b = _Buf()
+    ad, pool, proj, seg = _descs(b)
+    L = lora.lib()
+    r = ctypes.byref
+    v = ctypes.c_void_p(b.p())
+    # v_stride below T * 128
+    assert L.lora_shrink(r(proj), r(ad), r(seg), r(pool), v, 8 * 127, None) == -1
+    # v_slices < 1
+    assert L.lora_expand(r(proj), r(ad), r(seg), r(pool), v, 0, 8 * 128, None) == -1
+    arr = (lora.lora_proj_t * 1)(proj)
+    # neither ids nor segments; T mismatch; workspace too small
+    assert L.lora_apply(None, None, 8, arr, 1, r(ad), r(pool), v, 1 << 30, None) == -1
+    assert L.lora_apply(None, r(seg), 7, arr, 1, r(ad), r(pool), v, 1 << 30, None) == -1
+    assert L.lora_apply(None, r(seg), 8, arr, 1, r(ad), r(pool), v, 64, None) == -4
+    # adapters without rank array; too many adapters for the segment buffer
+    bad = lora.lora_adapters_t(None, b.p(), 4)
+    assert L.lora_apply(None, r(seg), 8, arr, 1, r(bad), r(pool), v, 1 << 30, None) == -1
+    big = lora.lora_adapters_t(b.p(), b.p(), 5)
+    assert L.lora_build_segments(v, 8, r(big), r(seg), v, 1 << 20, None) == -4
+    assert L.lora_build_segments(v, 9, r(ad), r(seg), v, 1 << 20, None) == -4
+    assert L.lora_build_segments(None, 8, r(ad), r(seg), v, 1 << 20, None) == -1
+    assert L.lora_build_segments(v, 8, r(ad), r(seg), v, 4, None) == -4
+    # Y aliasing Y_base with another leading dimension
+    p2 = lora.lora_proj_t(b.p(), 64, b.p(512), 64, b.p(512), 72, 64, 64, b.p(), b.p(), b.p(), b.p())
+    assert L.lora_shrink(r(p2), r(ad), r(seg), r(pool), v, 8 * 128, None) == -1
+    # segment buffer: misaligned / too small
+    s2 = lora.lora_segments_t()
+    assert L.lora_segments_init(ctypes.c_void_p(b.p(4)), 1 << 14, 8, 4, r(s2)) == -7
+    assert L.lora_segments_init(ctypes.c_void_p(b.p()), 16, 8, 4, r(s2)) == -4
+
+
+def test_validate_tables():
+    import workloads as W
+    ranks = np.array([8, 16, 40, 1], np.int32)
+    tabs, npg = W.plan_tables(ranks, [("p", 300, 700)], 128, True, 3)
+    t = tabs[0]
+    ok = lora.lora_validate_tables(ranks, 300, 700, 128, npg, t.a_indptr, t.a_pages, t.b_indptr, t.b_pages)
+    assert ok == 0
+    bad = t.a_pages.copy()
+    bad[3] = npg
+    assert lora.lora_validate_tables(ranks, 300, 700, 128, npg, t.a_indptr, bad, t.b_indptr, t.b_pages) == -3
+    r2 = ranks.copy()
+    r2[1] = 129
+    assert lora.lora_validate_tables(r2, 300, 700, 128, npg, t.a_indptr, t.a_pages, t.b_indptr, t.b_pages) == -2
+    # table sized for another rank
+    r3 = ranks.copy()
+    r3[0] = 20
+    assert lora.lora_validate_tables(r3, 300, 700, 128, npg, t.a_indptr, t.a_pages, t.b_indptr, t.b_pages) == -1
+
+
+def test_binding_refuses_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(lora, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(lora, "_lib", None)
+    with pytest.raises(ImportError):
+        lora.lib()

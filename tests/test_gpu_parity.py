@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Segments and every integer output must be bit-exact.  Y must agree within the
+row-wise infinity-norm relative error 1e-2 in bf16 mode and 1e-5 in fp32 mode
+(error measure: max over rows of max_j |Y - Y_ref| / max_j |Y_ref|).
+Closed forms, isolation, permutation and determinism are checked bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from heterogeneous_adapters_amd import batch, lora
+
+pytestmark = pytest.mark.gpu
+TOL = {"bf16": 1e-2, "f32": 1e-5}
+
+
+def rowwise_rel(Y, Yref):
+    Y = np.asarray(Y, np.float64)
+    Yref = np.asarray(Yref, np.float64)
+    if len(Y) == 0:
+        return 0.0
+    den = np.maximum(np.abs(Yref).max(axis=1), 1e-30)
+    return float((np.abs(Y - Yref).max(axis=1) / den).max())
+
+
+def gpu_apply(w, in_place=False, pool=None, ids=None, via="apply"):
+    """Run the whole branch on the GPU; returns host Y per projection and
+    the segment arrays."""
+    b = batch.to_device(w, pool=pool)
+    if ids is not None:
+        b.ids = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
+    segs = lora.Segments(w.T, w.N)
+    projs = [b.proj(p, in_place) for p in range(w.n_projs)]
+    max_din = max(t.d_in for t in w.tables)
+    ws = lora.workspace(w.T, w.N, w.n_projs, max_din)
+    if via == "apply":
+        lora.lora_apply(b.ids, segs, w.T, projs, b.adapters, b.pool, ws)
+    else:
+        lora.lora_build_segments(b.ids, b.adapters, segs, ws)
+        for p, pr in enumerate(projs):
+            nq = lora.lora_v_slices(w.tables[p].d_in)
+            stride = max(w.T, 1) * lora.LORA_MAX_RANK
+            v = torch.empty(nq * stride, dtype=torch.float32, device="cuda")
+            lora.lora_shrink(pr, b.adapters, segs, b.pool, v, stride)
+            lora.lora_expand(pr, b.adapters, segs, b.pool, v, nq, stride)
+    torch.cuda.synchronize()
+    out = [batch.device_to_host(b.Y_base[p] if in_place else b.Y[p]) for p in range(w.n_projs)]
+    return out, segs.arrays()
+
+
+def oracle_Y(w, p, ids=None, pool=None):
+    return oracle.apply(w.X[p], w.Y_base[p], w.ids if ids is None else ids, w.ranks, w.alpha, w.tables[p],
+                        w.pool if pool is None else pool, w.page_width, w.dtype)
+
+
+def check_segments(got, want):
+    assert got["S"] == want["S"]
+    assert got["n_invalid"] == want["n_invalid"]
+    assert got["T_valid"] == want["T_valid"]
+    assert got["V_total"] == want["V_total"]
+    for k in ("perm", "seg_indptr", "seg_adapter", "v_indptr"):
+        assert np.array_equal(got[k], want[k]), k
+    assert got["flags"] == 0
+
+
+# ----------------------------------------------------------------- runtime
+def test_one_hip_runtime_mapped():
+    lora.lib()
+    torch.zeros(1, device="cuda")
+    maps = lora.hip_runtimes_mapped()
+    assert len(maps) == 1, maps
+
+
+# ---------------------------------------------------------------- segments
+def _segments_gpu(ids, ranks):
+    T, N = len(ids), len(ranks)
+    ad = lora.Adapters(torch.from_numpy(np.asarray(ranks, np.int32)).cuda(),
+                       torch.ones(N, dtype=torch.float32, device="cuda"))
+    segs = lora.Segments(T, N)
+    ws = lora.workspace(T, N, 0, 0)
+    lora.lora_build_segments(torch.from_numpy(np.asarray(ids, np.int32)).cuda(), ad, segs, ws)
+    return segs.arrays()
+
+
+@pytest.mark.parametrize("k", [0, 1, 2, 3, 4])
+def test_segments_bit_exact_configs(k):
+    ids, ranks, _, _ = W.draw_ids_and_ranks(k)
+    print(f"segments config {k}: T={len(ids)} N={len(ranks)}", flush=True)
+    check_segments(_segments_gpu(ids, ranks), oracle.segments(ids, ranks))
+
+
+@pytest.mark.parametrize("case", ["T1", "all_base", "invalid_mix", "bad_rank", "one_adapter_long",
+                                  "many_adapters", "ragged_chunks"])
+def test_segments_bit_exact_edges(case):
+    rng = np.random.default_rng(hash(case) % 2 ** 31)
+    if case == "T1":
+        ids, ranks = np.array([2], np.int32), np.array([8, 8, 8], np.int32)
+    elif case == "all_base":
+        ids, ranks = np.full(37, -1, np.int32), np.array([16, 8], np.int32)
+    elif case == "invalid_mix":
+        ranks = rng.choice([8, 16, 64], 20).astype(np.int32)
+        ids = rng.integers(-5, 25, 3000).astype(np.int32)
+    elif case == "bad_rank":
+        ranks = rng.choice([0, 8, 129, 16], 30).astype(np.int32)
+        ids = rng.integers(0, 30, 2500).astype(np.int32)
+    elif case == "one_adapter_long":
+        ranks = np.array([32], np.int32)
+        ids = np.zeros(5000, np.int32)
+    elif case == "many_adapters":
+        ranks = rng.choice([8, 16, 32, 64], 5000).astype(np.int32)
+        ids = rng.integers(0, 5000, 700).astype(np.int32)
+    else:
+        ranks = rng.choice([1, 24, 128], 7).astype(np.int32)
+        ids = rng.integers(0, 7, 2 * 1024 + 17).astype(np.int32)
+    print(f"segments edge {case}: T={len(ids)} N={len(ranks)}", flush=True)
+    check_segments(_segments_gpu(ids, ranks), oracle.segments(ids, ranks))
+
+
+# ------------------------------------------------------------------- apply
+PARITY_CASES = {
+    "cfg0": (0, {}),
+    "cfg1": (1, {}),
+    "cfg2": (2, {}),
+    "cfg2_f32": (2, dict(dtype="f32")),
+    "cfg3": (3, {}),
+    "tails_bf16": (2, dict(T=300, N=7, ranks_override=[1, 4, 24, 40, 17, 128, 8], page_width=256,
+                           projs=(("a", 1000, 744), ("b", 2056, 520)))),
+    "tails_f32": (2, dict(T=300, N=7, ranks_override=[1, 4, 24, 40, 17, 128, 8], page_width=64,
+                          dtype="f32", projs=(("a", 1000, 744), ("b", 520, 2056)))),
+    "hot_segments": (2, dict(T=700, N=3, ranks_override=[8, 64, 128], page_width=512,
+                             projs=(("a", 4096, 1032),))),
+    "pw64_contig": (1, dict(T=96, N=5, page_width=64, projs=(("q", 512, 512),))),
+}
+
+
+@pytest.mark.parametrize("name", list(PARITY_CASES))
+def test_apply_matches_oracle(name):
+    k, kw = PARITY_CASES[name]
+    w = W.make_workload(k, kw, keep_dense=False)
+    print(f"apply parity {name}: T={w.T} N={w.N} dtype={w.dtype} projs={[(t.d_in, t.d_out) for t in w.tables]}",
+          flush=True)
+    Ys, seg = gpu_apply(w)
+    check_segments(seg, oracle.segments(w.ids, w.ranks))
+    for p in range(w.n_projs):
+        ref = oracle_Y(w, p)
+        got = W.as_f64(Ys[p], w.dtype)
+        assert np.isfinite(got).all()
+        err = rowwise_rel(got, W.as_f64(ref, w.dtype))
+        print(f"  proj {p}: rowwise rel err {err:.3e}", flush=True)
+        assert err < TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_shrink_expand_entry_points(dtype):
+    w = W.make_workload(2, dict(T=200, N=6, dtype=dtype, ranks_override=[8, 16, 64, 24, 1, 32],
+                                projs=(("a", 2048, 1000),), page_width=256), keep_dense=False)
+    Y1, seg = gpu_apply(w, via="apply")
+    Y2, _ = gpu_apply(w, via="split")
+    assert np.array_equal(Y1[0], Y2[0])
+    # shrink alone: sum of the partial slices against the oracle's v
+    b = batch.to_device(w)
+    segs = lora.Segments(w.T, w.N)
+    ws = lora.workspace(w.T, w.N, 1, 2048)
+    lora.lora_build_segments(b.ids, b.adapters, segs, ws)
+    stride = w.T * 128
+    v = torch.zeros(2 * stride, dtype=torch.float32, device="cuda")
+    lora.lora_shrink(b.proj(0), b.adapters, segs, b.pool, v, stride)
+    torch.cuda.synchronize()
+    vh = v.cpu().numpy().reshape(2, stride)
+    V = seg["V_total"]
+    vg = vh[0, :V] + vh[1, :V]
+    vo = oracle.shrink(w.X[0], oracle.segments(w.ids, w.ranks), w.ranks, w.tables[0], w.pool,
+                       w.page_width, w.dtype)
+    tol = 1e-5 if dtype == "f32" else 1e-3
+    assert np.abs(vg - vo).max() <= tol * np.abs(vo).max()
+    # expand alone, fed the oracle's v as one slice
+    vin = torch.zeros(stride, dtype=torch.float32, device="cuda")
+    vin[:V] = torch.from_numpy(vo)
+    lora.lora_expand(b.proj(0), b.adapters, segs, b.pool, vin, 1, stride)
+    torch.cuda.synchronize()
+    got = W.as_f64(batch.device_to_host(b.Y[0]), w.dtype)
+    assert rowwise_rel(got, W.as_f64(oracle_Y(w, 0), w.dtype)) < TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_one_hot_closed_form_exact_on_gpu(dtype):
+    """One-hot A and B: each sum has a single non-zero term, so the GPU must
+    agree with the oracle bit for bit on both the MBGMV and MBGMM paths."""
+    w = W.make_workload(2, dict(T=120, N=4, dtype=dtype, ranks_override=[8, 16, 5, 64],
+                                ids_override=np.r_[np.zeros(60), np.ones(30), np.full(20, 2), np.full(10, 3)]
+                                .astype(np.int32)[np.random.default_rng(0).permutation(120)],
+                                projs=(("a", 1536, 768),), page_width=256), keep_dense=False)
+    rng = np.random.default_rng(9)
+    pool = w.pool.copy()
+    tb = w.tables[0]
+    fill = W.BF16_NAN if dtype == "bf16" else np.float32(np.nan)
+    for a in range(w.N):
+        r = int(w.ranks[a])
+        A = np.zeros((1536, r), np.float32)
+        B = np.zeros((r, 768), np.float32)
+        A[rng.permutation(1536)[:r], np.arange(r)] = 1.0
+        B[np.arange(r), rng.permutation(768)[:r]] = 1.0
+        if dtype == "bf16":
+            A, B = W.f32_to_bf16_bits(A), W.f32_to_bf16_bits(B)
+        pool[tb.a_pages[tb.a_indptr[a]:tb.a_indptr[a + 1]]] = W.pack_a_pages(A, w.page_width, fill)
+        pool[tb.b_pages[tb.b_indptr[a]:tb.b_indptr[a + 1]]] = W.pack_b_pages(B, w.page_width, fill)
+    pool_d = batch.host_to_device(pool, dtype, "cuda")
+    Y, _ = gpu_apply(w, pool=pool_d)
+    assert np.array_equal(Y[0], oracle_Y(w, 0, pool=pool))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_isolation_bit_exact_on_gpu(dtype):
+    w = W.make_workload(2, dict(T=256, N=8, dtype=dtype, projs=(("a", 1024, 2048),), page_width=512),
+                        keep_dense=False)
+    b = int(np.bincount(w.ids).argmax())
+    tb = w.tables[0]
+    pages = np.concatenate([tb.a_pages[tb.a_indptr[b]:tb.a_indptr[b + 1]],
+                            tb.b_pages[tb.b_indptr[b]:tb.b_indptr[b + 1]]])
+    pool2 = w.pool.copy()
+    if dtype == "bf16":
+        pool2[pages] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(pool2[pages]) * np.float32(-3.0))
+    else:
+        pool2[pages] *= np.float32(-3.0)
+    Y0, _ = gpu_apply(w)
+    Y1, _ = gpu_apply(w, pool=batch.host_to_device(pool2, dtype, "cuda"))
+    other = w.ids != b
+    assert np.array_equal(Y0[0][other], Y1[0][other])
+    assert not np.array_equal(Y0[0][~other], Y1[0][~other])
+
+
+def test_permutation_and_determinism_on_gpu():
+    w = W.make_workload(2, dict(T=400, N=6, projs=(("a", 2048, 1024),), page_width=1024), keep_dense=False)
+    Y0, _ = gpu_apply(w)
+    Y0b, _ = gpu_apply(w)
+    assert np.array_equal(Y0[0], Y0b[0])
+    perm = np.random.default_rng(4).permutation(w.T)
+    w2 = W.make_workload(2, dict(T=400, N=6, projs=(("a", 2048, 1024),), page_width=1024), keep_dense=False)
+    w2.ids = w.ids[perm]
+    w2.X = [w.X[0][perm]]
+    w2.Y_base = [w.Y_base[0][perm]]
+    Y1, _ = gpu_apply(w2)
+    assert np.array_equal(Y1[0], Y0[0][perm])
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_base_only_and_invalid_tokens(in_place):
+    w = W.make_workload(2, dict(T=160, N=5, projs=(("a", 1024, 512),), page_width=256), keep_dense=False)
+    ids = w.ids.copy()
+    ids[::7] = -1
+    ids[3::11] = 99
+    Y, seg = gpu_apply(w, in_place=in_place, ids=ids)
+    want = oracle.segments(ids, w.ranks)
+    check_segments(seg, want)
+    excl = (ids < 0) | (ids >= w.N)
+    assert np.array_equal(Y[0][excl], w.Y_base[0][excl])
+    err = rowwise_rel(W.as_f64(Y[0], w.dtype), W.as_f64(oracle_Y(w, 0, ids=ids), w.dtype))
+    assert err < TOL[w.dtype]
+
+
+def test_in_place_equals_out_of_place():
+    w = W.make_workload(2, dict(T=333, N=9, projs=(("a", 2048, 3000),), page_width=1024), keep_dense=False)
+    Y0, _ = gpu_apply(w, in_place=False)
+    Y1, _ = gpu_apply(w, in_place=True)
+    assert np.array_equal(Y0[0], Y1[0])
+
+
+def test_many_projections_in_one_call():
+    """More projections than one launch holds: the call is split in groups."""
+    w = W.make_workload(2, dict(T=64, N=5, projs=(("a", 256, 512),), layers=19, page_width=256),
+                        keep_dense=False)
+    Ys, _ = gpu_apply(w)
+    for p in range(w.n_projs):
+        assert rowwise_rel(W.as_f64(Ys[p], w.dtype), W.as_f64(oracle_Y(w, p), w.dtype)) < TOL[w.dtype]
