@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-LIB_PATH = os.path.join(HERE, "liblora.so")
+# LORA_LIB_PATH selects another build of the library (tuning experiments)
+LIB_PATH = os.environ.get("LORA_LIB_PATH", os.path.join(HERE, "liblora.so"))
 SOURCES = [os.path.join(CSRC, "lora_kernels.hip"), os.path.join(CSRC, "lora_abi.cpp")]
 ARCH = os.environ.get("LORA_OFFLOAD_ARCH", "gfx950")
 
@@ -32,9 +33,10 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), out: str = None) -> str:
     tl = torch_lib_dir()
-    tmp = LIB_PATH + ".tmp"
+    out = out or os.path.join(HERE, "liblora.so")
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # no packed-fp32 VALU instructions in device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -51,8 +53,8 @@ def build(verbose: bool = False, extra=()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode})")
     if verbose and err.strip():
         sys.stderr.write(err + "\n")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

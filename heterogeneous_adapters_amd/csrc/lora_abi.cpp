@@ -30,7 +30,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int smax_of(int32_t T, int32_t N) { return std::max(0, std::min(T, N)); }
 
 struct SegSizes {
-  size_t perm, seg_indptr, seg_adapter, v_indptr, shr_ptr, exp_ptr, counts, total;
+  size_t perm, seg_indptr, seg_adapter, v_indptr, shr_ptr, exp_ptr, shr_item, exp_item, seg_desc, counts, total;
 };
 
 SegSizes seg_sizes(int32_t T, int32_t N) {
@@ -42,8 +42,12 @@ SegSizes seg_sizes(int32_t T, int32_t N) {
   z.v_indptr = z.seg_indptr;
   z.shr_ptr = z.seg_indptr;
   z.exp_ptr = z.seg_indptr;
+  z.shr_item = align_up(sizeof(int32_t) * (size_t)shrink_item_capacity(T));
+  z.exp_item = align_up(sizeof(int32_t) * (size_t)expand_item_capacity(T));
+  z.seg_desc = align_up(sizeof(int32_t) * 8 * std::max<size_t>(sm, 1));
   z.counts = align_up(sizeof(int32_t) * 8);
-  z.total = z.perm + z.seg_indptr + z.seg_adapter + z.v_indptr + z.shr_ptr + z.exp_ptr + z.counts;
+  z.total = z.perm + z.seg_indptr + z.seg_adapter + z.v_indptr + z.shr_ptr + z.exp_ptr + z.shr_item +
+            z.exp_item + z.seg_desc + z.counts;
   return z;
 }
 
@@ -64,7 +68,7 @@ lora_status_t check_adapters(const lora_adapters_t* ad) {
 
 lora_status_t check_segs(const lora_segments_t* s) {
   if (!s || !s->perm || !s->seg_indptr || !s->seg_adapter || !s->v_indptr || !s->shr_ptr ||
-      !s->exp_ptr || !s->counts)
+      !s->exp_ptr || !s->shr_item || !s->exp_item || !s->seg_desc || !s->counts)
     return LORA_ERR_INVALID_ARG;
   if (s->T < 0 || s->num_adapters < 1) return LORA_ERR_INVALID_ARG;
   return LORA_OK;
@@ -127,13 +131,15 @@ lora_status_t device_info(const DeviceInfo** out) {
   return LORA_OK;
 }
 
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 int grid_for(int resident, int64_t bound) {
   int64_t g = std::min<int64_t>(resident, std::max<int64_t>(bound, 1));
   g = (g + 7) / 8 * 8;
   return (int)std::max<int64_t>(g, 8);
 }
 
-KProj make_kproj(const lora_proj_t& p, float* v, int nv) {
+KProj make_kproj(const lora_proj_t& p, float* v, int nv, int dtype) {
   KProj k;
   memset(&k, 0, sizeof k);
   k.X = p.X;
@@ -150,7 +156,7 @@ KProj make_kproj(const lora_proj_t& p, float* v, int nv) {
   k.d_in = p.d_in;
   k.d_out = p.d_out;
   k.nq = lora_v_slices(p.d_in);
-  k.njs = ceil_div_i(p.d_out, kExpandCols);
+  k.njs = ceil_div_i(p.d_out, expand_cols(dtype == LORA_DTYPE_BF16));
   k.nv = nv;
   return k;
 }
@@ -163,6 +169,9 @@ void fill_common(KArgs& K, const lora_segments_t* s, const lora_adapters_t* ad, 
   K.v_indptr = s->v_indptr;
   K.shr_ptr = s->shr_ptr;
   K.exp_ptr = s->exp_ptr;
+  K.shr_item = s->shr_item;
+  K.exp_item = s->exp_item;
+  K.seg_desc = reinterpret_cast<const int4*>(s->seg_desc);
   K.counts = s->counts;
   K.rank = ad->rank;
   K.alpha = ad->alpha;
@@ -179,21 +188,25 @@ lora_status_t run(const KArgs& K, int dtype, bool do_shrink, bool do_expand, hip
   const int di = dtype == LORA_DTYPE_BF16 ? 1 : 0;
   int64_t bs = 0, be = 0;
   for (int p = 0; p < K.np; ++p) {
-    bs += (int64_t)K.p[p].nq * (9LL * K.T + 1);
-    be += (int64_t)K.p[p].njs * (2LL * K.T + 2);
+    bs += (int64_t)K.p[p].nq * shrink_item_capacity(K.T);
+    be += (int64_t)K.p[p].njs * (expand_item_capacity(K.T) + K.T);
   }
-  if (do_shrink && launch_shrink(K, dtype, grid_for(d->cus * d->occ_shrink[di], bs), stream) != hipSuccess)
+  // items are per wave: kWaves items per work-group
+  if (do_shrink && launch_shrink(K, dtype, grid_for(d->cus * d->occ_shrink[di], ceil_div64(bs, kWaves)), stream) !=
+                       hipSuccess)
     return LORA_ERR_HIP;
-  if (do_expand && launch_expand(K, dtype, grid_for(d->cus * d->occ_expand[di], be), stream) != hipSuccess)
+  if (do_expand && launch_expand(K, dtype, grid_for(d->cus * d->occ_expand[di], ceil_div64(be, kWaves)), stream) !=
+                       hipSuccess)
     return LORA_ERR_HIP;
   return LORA_OK;
 }
 
 lora_status_t build_into(const int32_t* ids, int32_t T, const lora_adapters_t* ad, const lora_segments_t* segs,
                          int32_t* hist, hipStream_t stream) {
-  SegOut o{segs->perm, segs->seg_indptr, segs->seg_adapter, segs->v_indptr, segs->shr_ptr, segs->exp_ptr,
-           segs->counts};
-  return launch_build_segments(ids, T, ad->num_adapters, ad->rank, hist, o, stream) == hipSuccess
+  SegOut o{segs->perm,     segs->seg_indptr, segs->seg_adapter, segs->v_indptr,
+           segs->shr_ptr,  segs->exp_ptr,    segs->shr_item,    segs->exp_item,
+           segs->seg_desc, segs->counts};
+  return launch_build_segments(ids, T, ad->num_adapters, ad->rank, ad->alpha, hist, o, stream) == hipSuccess
              ? LORA_OK
              : LORA_ERR_HIP;
 }
@@ -237,6 +250,9 @@ lora_status_t lora_segments_init(void* buf, size_t bytes, int32_t T, int32_t num
   out->v_indptr = reinterpret_cast<int32_t*>(p); p += z.v_indptr;
   out->shr_ptr = reinterpret_cast<int32_t*>(p); p += z.shr_ptr;
   out->exp_ptr = reinterpret_cast<int32_t*>(p); p += z.exp_ptr;
+  out->shr_item = reinterpret_cast<int32_t*>(p); p += z.shr_item;
+  out->exp_item = reinterpret_cast<int32_t*>(p); p += z.exp_item;
+  out->seg_desc = reinterpret_cast<int32_t*>(p); p += z.seg_desc;
   out->counts = reinterpret_cast<int32_t*>(p);
   return LORA_OK;
 }
@@ -270,7 +286,7 @@ lora_status_t lora_shrink(const lora_proj_t* proj, const lora_adapters_t* adapte
   KArgs K;
   memset(&K, 0, sizeof K);
   fill_common(K, segs, adapters, pool, v_stride);
-  K.p[0] = make_kproj(*proj, v, lora_v_slices(proj->d_in));
+  K.p[0] = make_kproj(*proj, v, lora_v_slices(proj->d_in), pool->dtype);
   K.np = 1;
   return run(K, pool->dtype, true, false, static_cast<hipStream_t>(stream));
 }
@@ -286,7 +302,7 @@ lora_status_t lora_expand(const lora_proj_t* proj, const lora_adapters_t* adapte
   KArgs K;
   memset(&K, 0, sizeof K);
   fill_common(K, segs, adapters, pool, v_stride);
-  K.p[0] = make_kproj(*proj, const_cast<float*>(v), v_slices);
+  K.p[0] = make_kproj(*proj, const_cast<float*>(v), v_slices, pool->dtype);
   K.np = 1;
   return run(K, pool->dtype, false, true, static_cast<hipStream_t>(stream));
 }
@@ -336,7 +352,7 @@ lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_
     K.np = std::min(kProjsPerLaunch, n_projs - base);
     for (int i = 0; i < K.np; ++i) {
       float* v = reinterpret_cast<float*>(vbase + (size_t)i * vpp);
-      K.p[i] = make_kproj(projs[base + i], v, lora_v_slices(projs[base + i].d_in));
+      K.p[i] = make_kproj(projs[base + i], v, lora_v_slices(projs[base + i].d_in), pool->dtype);
     }
     if (lora_status_t e = run(K, pool->dtype, true, true, st)) return e;
   }

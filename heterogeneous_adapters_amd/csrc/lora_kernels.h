@@ -9,13 +9,6 @@
 namespace lora {
 
 constexpr int kSegScanThreads = 1024;
-// LDS per work-group: the shrink needs max(8 token rows x 1024 fp32 columns,
-// three waves' partial MFMA tiles = 3 x 8 tiles x 64 lanes x 4 floats);
-// the expand needs v of up to 64 tokens x 128 ranks in fp32.
-constexpr int kShrinkSmem = (kValuTokens * kKSlice * 4 > 3 * 8 * 64 * 4 * 4) ? kValuTokens * kKSlice * 4 : 3 * 8 * 64 * 4 * 4;
-constexpr int kExpandSmem = kExpandTokens * 128 * 4;
-static_assert(kValuTokens * kKSlice * 4 <= kShrinkSmem, "shrink LDS");
-
 // One projection as the kernels see it.
 struct KProj {
   const void* X;
@@ -28,8 +21,8 @@ struct KProj {
   const int32_t* b_pages;
   int64_t ldx, ldyb, ldy;
   int32_t d_in, d_out;
-  int32_t nq;   // shrink slices written: ceil(d_in / 1024)
-  int32_t njs;  // expand column slices: ceil(d_out / 256)
+  int32_t nq;   // shrink slices written: ceil(d_in / 512)
+  int32_t njs;  // expand column blocks: ceil(d_out / expand_cols)
   int32_t nv;   // v slices the expand sums
   int32_t pad;
 };
@@ -42,6 +35,9 @@ struct KArgs {
   const int32_t* v_indptr;
   const int32_t* shr_ptr;
   const int32_t* exp_ptr;
+  const int32_t* shr_item;
+  const int32_t* exp_item;
+  const int4* seg_desc;  // per segment: {a, r, t0, n}, {v_offset, shr_ptr, exp_ptr, alpha bits}
   int32_t* counts;
   const int32_t* rank;
   const float* alpha;
@@ -60,11 +56,14 @@ struct SegOut {
   int32_t* v_indptr;
   int32_t* shr_ptr;
   int32_t* exp_ptr;
+  int32_t* shr_item;
+  int32_t* exp_item;
+  int32_t* seg_desc;
   int32_t* counts;
 };
 
-hipError_t launch_build_segments(const int32_t* ids, int T, int N, const int32_t* rank, int32_t* hist,
-                                 const SegOut& out, hipStream_t stream);
+hipError_t launch_build_segments(const int32_t* ids, int T, int N, const int32_t* rank, const float* alpha,
+                                 int32_t* hist, const SegOut& out, hipStream_t stream);
 hipError_t launch_shrink(const KArgs& K, int dtype, int grid, hipStream_t stream);
 hipError_t launch_expand(const KArgs& K, int dtype, int grid, hipStream_t stream);
 hipError_t occupancy(int dtype, int* shrink_blocks, int* expand_blocks);

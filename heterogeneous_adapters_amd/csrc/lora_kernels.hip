@@ -43,10 +43,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 struct Bf16 {
   typedef uint16_t T;
   static constexpr int kEpv = 8;  // elements per 16-byte vector
+  static constexpr int kShrinkBlocks = 3;  // occupancy targets (work-groups per CU)
+  static constexpr int kExpandBlocks = 3;
 };
 struct F32 {
   typedef float T;
   static constexpr int kEpv = 4;
+  static constexpr int kShrinkBlocks = 2;
+  static constexpr int kExpandBlocks = 2;
 };
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -63,6 +67,21 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 }
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Loads of metadata that no kernel of the call writes (segments, page
+// tables), through the constant address space so that wave-uniform
+// addresses become scalar loads.
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ int cld(const int32_t* p) { return *(const __attribute__((address_space(4))) int32_t*)(p); }
+__device__ __forceinline__ int4 cld4(const int4* p) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i v = *(const __attribute__((address_space(4))) v4i*)(p);
+  return make_int4(v.x, v.y, v.z, v.w);
+}
+#else
+__device__ int cld(const int32_t* p);
+__device__ int4 cld4(const int4* p);
+#endif
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // 8-wide bf16 dot product accumulated in fp32 (v_dot2_f32_bf16).
@@ -147,56 +166,94 @@ __device__ __forceinline__ int find_segment(const int32_t* ptr, int S, int u) {
 }
 
 // Wave64 reduce-scatter of 32 per-lane values: afterwards lanes 2i and 2i+1
-// hold the sum over all 64 lanes of value i (32 cross-lane exchanges
-// instead of 32 full butterflies).
+// hold the sum over all 64 lanes of value i.  Each step halves the values a
+// lane keeps while summing over one more lane bit: bit 5 with
+// v_permlane32_swap (lane l <-> l^32 between two registers), bit 4 with
+// v_permlane16_swap (l <-> l^16), bit 3 with a DPP row rotation by 8, bit 2
+// with a swizzle, bits 1 and 0 with DPP quad permutations.  Exchanges are
+// commutative adds, so a value's sum is the same whichever lane holds it.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppQuadXor2 = 0x4e;  // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor1 = 0xb1;  // quad_perm [1,0,3,2]
+
 __device__ __forceinline__ float wave_reduce_scatter32(float (&v)[32], int lane) {
+  float a[16];
 #pragma unroll
-  for (int step = 0; step < 5; ++step) {
-    const int half = 16 >> step;
-    const int mask = 32 >> step;
-    const bool upper = (lane & mask) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = upper ? v[i] : v[i + half];
-      const float keep = upper ? v[i + half] : v[i];
-      v[i] = keep + __shfl_xor(send, mask);
-    }
+  for (int i = 0; i < 16; ++i) {  // lanes with bit 5 clear keep value i, set keep i+16
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 16]), false, false);
+    a[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  return v[0] + __shfl_xor(v[0], 1);
+  float b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {   // bit 4 clear keeps a[i], set keeps a[i+8]
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[i + 8]), false, false);
+    b[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  const bool u3 = (lane & 8) != 0, u2 = (lane & 4) != 0, u1 = (lane & 2) != 0;
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {   // bit 3
+    const float send = u3 ? b[i] : b[i + 4];
+    c[i] = (u3 ? b[i + 4] : b[i]) + dpp_f<kDppRowRor8>(send);
+  }
+  float d[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {   // bit 2
+    const float send = u2 ? c[i] : c[i + 2];
+    d[i] = (u2 ? c[i + 2] : c[i]) +
+           __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(send), (4 << 10) | 0x1f));
+  }
+  const float send = u1 ? d[0] : d[1];  // bit 1
+  const float e = (u1 ? d[1] : d[0]) + dpp_f<kDppQuadXor2>(send);
+  return e + dpp_f<kDppQuadXor1>(e);    // bit 0
 }
 
-// XCD-aware item walk: item range [0, total) is cut into 8 contiguous parts,
-// part x served by the work-groups with blockIdx.x % 8 == x.
-struct ItemWalk {
+// ================================================================ work walk
+// XCD-aware wave walk: the item range [0, total) is cut into 8 contiguous
+// parts, part x served by the waves of the work-groups with blockIdx.x % 8
+// == x (work-groups are dealt to the XCDs round robin), so items that share
+// an adapter slice are read through the same L2.  Every wave walks its own
+// items: no work-group barrier couples the waves.
+struct WaveWalk {
   int i, end, stride;
-  __device__ ItemWalk(int total) {
+  __device__ WaveWalk(int total, int wave) {
     const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
     const int x = blockIdx.x % nx;
-    const int per = gridDim.x / nx;
     const int lo = (int)(((int64_t)total * x) / nx);
     end = (int)(((int64_t)total * (x + 1)) / nx);
-    i = lo + (int)(blockIdx.x / nx);
-    stride = per;
+    i = lo + (int)(blockIdx.x / nx) * kWaves + wave;
+    stride = (gridDim.x / nx) * kWaves;
   }
 };
 
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // ================================================================ shrink
-// MBGMV item: (segment s, rank group g, token chunk of <= 8 tokens, slice q).
-// The chunk's token rows (the gathered activations of [MLSP] SGMV) are staged
-// in LDS; wave w takes page rows 4w..4w+3 of the 16-rank group, each lane
-// streams 16-byte vectors of those rows (a wave reads 1 KiB contiguous per
-// row and instruction) and the 64 lanes' partial dot products are reduced
-// across the wave.
+// MBGMV item (one wave): (segment, rank group g, <= 2 tokens, 512-column
+// slice q).  Each lane streams one 16-byte vector (8 bf16 / 4 fp32 columns)
+// of each of the group's 16 page rows -- a wave reads 1 KiB contiguous per
+// row -- together with the same columns of the tokens' activation rows (the
+// gathered activations of [MLSP] SGMV), forms partial dot products, and the
+// 64 lanes are reduced across the wave.  All loads are issued before the
+// first product, so an item costs one memory round trip after its page
+// lookup.
 template <class E>
-__device__ void shrink_valu(const KArgs& K, const KProj& P, int q, int s, int local, char* smem) {
+__device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int q, int4 d0, int4 d1, int local, int lane) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
-  constexpr int NCH = kKSlice / (64 * EPV);
+  constexpr int NVEC = kKSlice / (64 * EPV);  // vectors per lane and row (bf16 1, fp32 2)
   constexpr int NV = kValuTokens;
-  const int a = K.seg_adapter[s];
-  const int r = K.rank[a];
-  const int t0 = K.seg_indptr[s];
-  const int n = K.seg_indptr[s + 1] - t0;
+  const int a = d0.x, r = d0.y, t0 = d0.z, n = d0.w;
   const int nch = ceil_div_i(n, NV);
   const int g = local / nch;
   const int tb = (local - g * nch) * NV;
@@ -204,67 +261,67 @@ __device__ void shrink_valu(const KArgs& K, const KProj& P, int q, int s, int lo
   const int col0 = q * kKSlice;
   const int ncols = min(kKSlice, P.d_in - col0);
   const int pw = 1 << K.pw_log2;
-
-  T* xs = reinterpret_cast<T*>(smem);  // [NV][kKSlice]
-  constexpr int VPR = kKSlice / EPV;
-  for (int idx = threadIdx.x; idx < nt * VPR; idx += kThreads) {
-    const int tt = idx / VPR;
-    const int c = (idx - tt * VPR) * EPV;
-    uint4 val = zero4();
-    if (c < ncols) val = ldg16(reinterpret_cast<const T*>(P.X) + (int64_t)K.perm[t0 + tb + tt] * P.ldx + col0 + c);
-    *reinterpret_cast<uint4*>(xs + tt * kKSlice + c) = val;
-  }
-  __syncthreads();
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rows = min(16, r - g * 16);
-  const int row0 = wave * 4;
+  const int slot0 = P.a_indptr[a] + g * ((P.d_in + pw - 1) >> K.pw_log2);
+  const T* X = reinterpret_cast<const T*>(P.X);
+
+  // per-lane page pointers (the row addresses stay in vector registers)
+  const T* pg[NVEC];
+  int off[NVEC];
+  bool ok[NVEC];
+#pragma unroll
+  for (int v = 0; v < NVEC; ++v) {
+    const int c = v * 64 * EPV + lane * EPV;
+    const int col = col0 + c;
+    ok[v] = c < ncols;
+    off[v] = col & (pw - 1);
+    pg[v] = ok[v] ? page_ptr<E>(K, P.a_pages[slot0 + (col >> K.pw_log2)]) : nullptr;
+  }
+  uint4 w[16][NVEC];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+    for (int v = 0; v < NVEC; ++v)
+      w[rr][v] = (pg[v] != nullptr && rr < rows) ? ldg16(pg[v] + rr * pw + off[v]) : zero4();
+  uint4 x[NV][NVEC];
+#pragma unroll
+  for (int tt = 0; tt < NV; ++tt) {
+    const int64_t row = tt < nt ? (int64_t)K.perm[t0 + tb + tt] * P.ldx + col0 : -1;
+#pragma unroll
+    for (int v = 0; v < NVEC; ++v)
+      x[tt][v] = (row >= 0 && ok[v]) ? ldg16(X + row + v * 64 * EPV + lane * EPV) : zero4();
+  }
+  static_assert(16 * NV == 32, "one 32-value wave reduction per item");
   float acc[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
-  if (row0 < rows) {
-    const int ncolA = (P.d_in + pw - 1) >> K.pw_log2;
-    const int slot0 = P.a_indptr[a] + g * ncolA;
+  for (int rr = 0; rr < 16; ++rr)
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = i * 64 * EPV + lane * EPV;
-      if (c < ncols) {
-        const int col = col0 + c;
-        const T* pg = page_ptr<E>(K, P.a_pages[slot0 + (col >> K.pw_log2)]);
-        uint4 w[4];
+    for (int tt = 0; tt < NV; ++tt) {
+      float s = 0.0f;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          w[rr] = (pg != nullptr && row0 + rr < rows) ? ldg16(pg + (row0 + rr) * pw + (col & (pw - 1))) : zero4();
-        uint4 x[NV];
-#pragma unroll
-        for (int tt = 0; tt < NV; ++tt) x[tt] = *reinterpret_cast<const uint4*>(xs + tt * kKSlice + c);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-          for (int tt = 0; tt < NV; ++tt) acc[rr * NV + tt] = dot16(w[rr], x[tt], acc[rr * NV + tt], E());
-      }
+      for (int v = 0; v < NVEC; ++v) s = dot16(w[rr][v], x[tt][v], s, E());
+      acc[rr * NV + tt] = s;
     }
-  }
   const float sum = wave_reduce_scatter32(acc, lane);
   const int vi = lane >> 1;
-  const int rr = vi / NV, tt = vi - rr * NV;
-  if (row0 < rows && (lane & 1) == 0 && row0 + rr < rows && tt < nt)
-    P.v[(int64_t)q * K.v_stride + K.v_indptr[s] + (int64_t)(tb + tt) * r + g * 16 + row0 + rr] = sum;
+  const int rr = vi / NV, tt = vi % NV;
+  if ((lane & 1) == 0 && rr < rows && tt < nt)
+    P.v[(int64_t)q * K.v_stride + d1.x + (int64_t)(tb + tt) * r + g * 16 + rr] = sum;
 }
 
-// MBGMM item: (segment s, token chunk, slice q), every rank group at once so
-// each activation byte is read once.  C[rank][token] += A^T[rank][col] *
-// X^T[col][token]; wave w covers columns 256w..256w+255 of the slice and the
-// four partial tiles are summed through LDS in wave order.
-template <class E, int GM, int NTT>
-__device__ void shrink_mfma_body(const KArgs& K, const KProj& P, int q, int s, int a, int r, int t0,
-                                 int tb, int nt, char* smem) {
+// MBGMM item (one wave): (segment, token chunk, slice q), every rank group at
+// once so each activation byte is read once.  C[rank][token] +=
+// A^T[rank][col] * X^T[col][token] over the slice's 512 columns, with the
+// operands of SIF K steps requested before the first of their MFMAs.
+template <class E, int GM, int NTT, int SIF>
+__device__ __forceinline__ void shrink_mfma_body(const KArgs& K, const KProj& P, int q, int a, int r, int t0, int voff,
+                                 int tb, int nt, int lane) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
   constexpr int STEP = 4 * EPV;
-  constexpr int WCOLS = kKSlice / 4;
-  constexpr int NSTEP = WCOLS / STEP;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, qq = lane >> 4;
+  constexpr int NSTEP = kKSlice / STEP;
+  static_assert(NSTEP % SIF == 0, "steps in flight divide the slice");
+  const int li = lane & 15, qq = lane >> 4;
   const int G = rank_groups(r);
   const int col0 = q * kKSlice;
   const int ncols = min(kKSlice, P.d_in - col0);
@@ -272,14 +329,22 @@ __device__ void shrink_mfma_body(const KArgs& K, const KProj& P, int q, int s, i
   const int ncolA = (P.d_in + pw - 1) >> K.pw_log2;
   const T* X = reinterpret_cast<const T*>(P.X);
 
+  const bool one_page = pw >= kKSlice;  // the slice lies in one page of each group
+  const int abase = cld(P.a_indptr + a);
   int slot[GM];
+  bool rok[GM];
+  const T* pg1[GM];
 #pragma unroll
-  for (int g = 0; g < GM; ++g) slot[g] = P.a_indptr[a] + g * ncolA;
-  int xrow[NTT];  // row offsets of the tile's tokens, -1 past the segment
+  for (int g = 0; g < GM; ++g) {
+    slot[g] = abase + g * ncolA;
+    rok[g] = g < G && g * 16 + li < r;
+    pg1[g] = (one_page && g < G) ? page_ptr<E>(K, cld(P.a_pages + slot[g] + (col0 >> K.pw_log2))) : nullptr;
+  }
+  int64_t xrow[NTT];
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) {
     const int tok = tt * 16 + li;
-    xrow[tt] = tok < nt ? K.perm[t0 + tb + tok] : -1;
+    xrow[tt] = tok < nt ? (int64_t)K.perm[t0 + tb + tok] * P.ldx : -1;
   }
   f4 acc[GM][NTT];
 #pragma unroll
@@ -287,304 +352,404 @@ __device__ void shrink_mfma_body(const KArgs& K, const KProj& P, int q, int s, i
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[g][tt] = f4{0.f, 0.f, 0.f, 0.f};
 
-  if (wave * WCOLS < ncols) {
-#pragma unroll 2
-    for (int st = 0; st < NSTEP; ++st) {
-      const int c = wave * WCOLS + st * STEP + qq * EPV;
+#pragma unroll 1
+  for (int st0 = 0; st0 < NSTEP; st0 += SIF) {
+    uint4 av[SIF][GM], xv[SIF][NTT];
+#pragma unroll
+    for (int j = 0; j < SIF; ++j) {
+      const int c = (st0 + j) * STEP + qq * EPV;
       const bool ok = c < ncols;
       const int col = col0 + c;
-      uint4 av[GM], xv[NTT];
 #pragma unroll
       for (int g = 0; g < GM; ++g) {
-        av[g] = zero4();
-        if (g < G && ok && g * 16 + li < r) {
-          const T* pg = page_ptr<E>(K, P.a_pages[slot[g] + (col >> K.pw_log2)]);
-          if (pg != nullptr) av[g] = ldg16(pg + li * pw + (col & (pw - 1)));
+        av[j][g] = zero4();
+        if (ok && rok[g]) {
+          const T* pg = one_page ? pg1[g] : page_ptr<E>(K, P.a_pages[slot[g] + (col >> K.pw_log2)]);
+          if (pg != nullptr) av[j][g] = ldg16(pg + li * pw + (col & (pw - 1)));
         }
       }
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) xv[tt] = (ok && xrow[tt] >= 0) ? ldg16(X + (int64_t)xrow[tt] * P.ldx + col) : zero4();
+      for (int tt = 0; tt < NTT; ++tt) xv[j][tt] = (ok && xrow[tt] >= 0) ? ldg16(X + xrow[tt] + col) : zero4();
+    }
+#pragma unroll
+    for (int j = 0; j < SIF; ++j)
 #pragma unroll
       for (int g = 0; g < GM; ++g)
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) mma(acc[g][tt], av[g], xv[tt], E());
-    }
+        for (int tt = 0; tt < NTT; ++tt) mma(acc[g][tt], av[j][g], xv[j][tt], E());
   }
-
-  float* red = reinterpret_cast<float*>(smem);  // [3][GM*NTT][64][4], GM*NTT <= 8
-  if (wave > 0) {
+  float* vout = P.v + (int64_t)q * K.v_stride + voff;
 #pragma unroll
-    for (int g = 0; g < GM; ++g)
+  for (int g = 0; g < GM; ++g) {
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt)
-        *reinterpret_cast<f4*>(red + (((wave - 1) * GM * NTT + g * NTT + tt) * 64 + lane) * 4) = acc[g][tt];
-  }
-  __syncthreads();
-  if (wave == 0) {
-    float* vout = P.v + (int64_t)q * K.v_stride + K.v_indptr[s];
+    for (int tt = 0; tt < NTT; ++tt) {
+      const int tok = tt * 16 + li;
+      const int k0 = g * 16 + qq * 4;
+      if (g < G && tok < nt) {
+        float* dst = vout + (int64_t)(tb + tok) * r + k0;
 #pragma unroll
-    for (int g = 0; g < GM; ++g) {
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        f4 c = acc[g][tt];
-#pragma unroll
-        for (int w = 0; w < 3; ++w) c += *reinterpret_cast<const f4*>(red + ((w * GM * NTT + g * NTT + tt) * 64 + lane) * 4);
-        const int tok = tt * 16 + li;
-        const int k0 = g * 16 + qq * 4;
-        if (g < G && tok < nt) {
-          float* dst = vout + (int64_t)(tb + tok) * r + k0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (k0 + i < r) dst[i] = c[i];
-        }
+        for (int i = 0; i < 4; ++i)
+          if (k0 + i < r) dst[i] = acc[g][tt][i];
       }
     }
   }
 }
 
 template <class E>
-__device__ void shrink_mfma(const KArgs& K, const KProj& P, int q, int s, int local, char* smem) {
-  const int a = K.seg_adapter[s];
-  const int r = K.rank[a];
-  const int t0 = K.seg_indptr[s];
-  const int n = K.seg_indptr[s + 1] - t0;
+__device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int q, int4 d0, int4 d1, int local, int lane) {
+  const int a = d0.x, r = d0.y, t0 = d0.z, n = d0.w;
   const int G = rank_groups(r);
   const int tch = 16 * mfma_token_tiles(G);
   const int tb = local * tch;
   const int nt = min(tch, n - tb);
-  if (G <= 1) shrink_mfma_body<E, 1, 8>(K, P, q, s, a, r, t0, tb, nt, smem);
-  else if (G == 2) shrink_mfma_body<E, 2, 4>(K, P, q, s, a, r, t0, tb, nt, smem);
-  else if (G <= 4) shrink_mfma_body<E, 4, 2>(K, P, q, s, a, r, t0, tb, nt, smem);
-  else shrink_mfma_body<E, 8, 1>(K, P, q, s, a, r, t0, tb, nt, smem);
+  if (G <= 1) shrink_mfma_body<E, 1, 4, 4>(K, P, q, a, r, t0, d1.x, tb, nt, lane);
+  else if (G == 2) shrink_mfma_body<E, 2, 2, 4>(K, P, q, a, r, t0, d1.x, tb, nt, lane);
+  else if (G <= 4) shrink_mfma_body<E, 4, 1, 4>(K, P, q, a, r, t0, d1.x, tb, nt, lane);
+  else shrink_mfma_body<E, 8, 1, 1>(K, P, q, a, r, t0, d1.x, tb, nt, lane);
 }
 
 template <class E>
-__global__ __launch_bounds__(kThreads) void shrink_kernel(KArgs K) {
-  __shared__ __attribute__((aligned(16))) char smem[kShrinkSmem];
+__global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArgs K) {
   const int S = K.counts[LORA_COUNT_S];
   const int U = K.counts[4];
   if (S <= 0) return;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   int total = 0;
   for (int p = 0; p < K.np; ++p) total += K.p[p].nq * U;
-  for (ItemWalk it(total); it.i < it.end; it.i += it.stride) {
-    int rem = it.i, p = 0;
-    while (rem >= K.p[p].nq * U) { rem -= K.p[p].nq * U; ++p; }
-    const KProj& P = K.p[p];
-    const int q = rem / U;
-    const int u = rem - q * U;
-    const int s = find_segment(K.shr_ptr, S, u);
-    const int local = u - K.shr_ptr[s];
-    const int n = K.seg_indptr[s + 1] - K.seg_indptr[s];
-    if (is_mfma_segment(n)) shrink_mfma<E>(K, P, q, s, local, smem);
-    else shrink_valu<E>(K, P, q, s, local, smem);
-    __syncthreads();
+  // Two walks over the same items, MBGMM items in the first and MBGMV items
+  // in the second, so the register footprints of the two paths never share
+  // a loop body.
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    for (WaveWalk it(total, wave); it.i < it.end; it.i += it.stride) {
+      int rem = it.i, p = 0;
+      while (rem >= K.p[p].nq * U) { rem -= K.p[p].nq * U; ++p; }
+      const int q = rem / U;
+      const int u = rem - q * U;
+      const int s = cld(K.shr_item + u);
+      const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
+      if (is_mfma_segment(d0.w) != (pass == 0)) continue;
+      const int local = u - d1.y;
+      if (pass == 0) shrink_mfma<E>(K, K.p[p], q, d0, d1, local, lane);
+      else shrink_valu<E>(K, K.p[p], q, d0, d1, local, lane);
+    }
   }
 }
 
 // ================================================================ expand
-// MBGMV expand item: (segment s of < 16 tokens, 256-column slice).  v of the
-// segment (slices summed in ascending order) sits in LDS; every thread owns
-// one output column j, reads the 16 ranks of B for j in each rank group as
-// 16-byte vectors, and produces Y for all the segment's tokens.
+// v of tokens [tb, tb+nt) of a segment into the wave's LDS rows of G*16
+// floats, ranks >= r zero-filled.  The chunk's v is nt*r contiguous floats in
+// every partial slice; in passes of 1024 elements each lane sums 16 of them
+// over the slices (ascending slice order), two slices' loads in flight.
+__device__ __forceinline__ void stage_v(const KArgs& K, const KProj& P, int voff, int r, int tb, int nt,
+                                        float* vs, int lane) {
+  constexpr int M = 16;
+  const int rs = rank_groups(r) * 16;
+  const int ne = nt * r;
+  const float* src = P.v + voff + (int64_t)tb * r;
+  for (int e0 = 0; e0 < ne; e0 += 64 * M) {
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+    int q = 0;
+    for (; q + 2 <= P.nv; q += 2) {
+      float x[2][M];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const int e = e0 + lane + 64 * m;
+          x[j][m] = e < ne ? src[(int64_t)(q + j) * K.v_stride + e] : 0.0f;
+        }
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[m] = (acc[m] + x[0][m]) + x[1][m];
+    }
+    if (q < P.nv) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int e = e0 + lane + 64 * m;
+        if (e < ne) acc[m] += src[(int64_t)q * K.v_stride + e];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int e = e0 + lane + 64 * m;
+      if (e < ne) {
+        const int t = e / r;
+        vs[t * rs + (e - t * r)] = acc[m];
+      }
+    }
+  }
+  for (int idx = lane; idx < nt * (rs - r); idx += 64) {  // zero the rank padding of every row
+    const int t = idx / (rs - r);
+    vs[t * rs + r + (idx - t * (rs - r))] = 0.0f;
+  }
+  wave_sync();
+}
+
+// B element k (rank within the group) of lane-local column c, from the 8
+// vectors a lane holds per rank group.
+__device__ __forceinline__ float b_elem(const uint4 (&b)[8], int c, int k, Bf16) {
+  const uint32_t u = (&b[0].x)[(c * 16 + k) >> 1];
+  return (k & 1) ? bf_hi(u) : bf_lo(u);
+}
+__device__ __forceinline__ float b_elem(const uint4 (&b)[8], int c, int k, F32) {
+  return __uint_as_float((&b[0].x)[c * 16 + k]);
+}
+
+// MBGMV expand item (one wave): (segment, <= 8 tokens, column block).  Each
+// lane owns CPL adjacent output columns (4 in bf16, 2 in fp32) whose 16-rank
+// rows are adjacent in the B page: 128 contiguous bytes per lane and rank
+// group, 8 KiB per wave.  The next group's B is fetched while the current
+// one is consumed; Y_base of the tokens is fetched before v is staged.
 template <class E>
-__device__ void expand_valu(const KArgs& K, const KProj& P, int js, int s, char* smem) {
+__device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, int jb, int4 d0, int4 d1, int local, float* vs,
+                            int lane) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
-  const int a = K.seg_adapter[s];
-  const int r = K.rank[a];
-  const int t0 = K.seg_indptr[s];
-  const int n = K.seg_indptr[s + 1] - t0;
-  const float scale = K.alpha[a] / (float)r;
-  float* vs = reinterpret_cast<float*>(smem);  // [n][r]
-  const float* vsrc = P.v + K.v_indptr[s];
-  for (int idx = threadIdx.x; idx < n * r; idx += kThreads) {
-    float sum = 0.0f;
-    for (int q = 0; q < P.nv; ++q) sum += vsrc[(int64_t)q * K.v_stride + idx];
-    vs[idx] = sum;
-  }
-  __syncthreads();
-  const int j = js * kExpandCols + threadIdx.x;
-  if (j >= P.d_out) return;
-  const int pw = 1 << K.pw_log2;
-  const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
-  const int slot0 = P.b_indptr[a] + (j >> K.pw_log2);
+  constexpr int CPL = 8 / (int)sizeof(T);
+  constexpr int CB = 64 * CPL;
+  constexpr int MT = kValuExpandTokens;
+  const int a = d0.x, r = d0.y;
+  const int tb = local * MT;
+  const int t0 = d0.z + tb;
+  const int n = min(MT, d0.w - tb);
+  const float scale = __int_as_float(d1.w) / (float)r;
   const int G = rank_groups(r);
-  float acc[kMfmaMinTokens];
-#pragma unroll
-  for (int tt = 0; tt < kMfmaMinTokens; ++tt) acc[tt] = 0.0f;
-  for (int g = 0; g < G; ++g) {
-    const T* pg = page_ptr<E>(K, P.b_pages[slot0 + g * ncolB]);
+  const int pw = 1 << K.pw_log2;
+  const int j0 = jb * CB + lane * CPL;
+  const bool live = j0 < P.d_out;
+  const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
+  const bool one_page = pw >= CB;  // the block lies in one page of each group
+  const int bbase = cld(P.b_indptr + a);
+  const int slot0 = bbase + (j0 >> K.pw_log2);
+  const int uslot0 = bbase + ((jb * CB) >> K.pw_log2);
+  auto load_group = [&](int g, uint4 (&b)[8]) {
     const int kmax = min(16, r - g * 16);
-    float b[16];
-    if (pg != nullptr) {
-      const T* row = pg + (j & (pw - 1)) * 16;
+    const T* pg = !live ? nullptr
+                 : one_page ? page_ptr<E>(K, cld(P.b_pages + uslot0 + g * ncolB))
+                            : page_ptr<E>(K, P.b_pages[slot0 + g * ncolB]);
+    const T* row = pg == nullptr ? nullptr : pg + (j0 & (pw - 1)) * 16;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
 #pragma unroll
       for (int v = 0; v < 16 / EPV; ++v) {
         const int kv = v * EPV;
-        uint4 raw = (kv + EPV <= kmax) ? ldg16(row + kv) : (kv < kmax ? load_partial<E>(row + kv, kmax - kv) : zero4());
-        const T* e = reinterpret_cast<const T*>(&raw);
-#pragma unroll
-        for (int i = 0; i < EPV; ++i) b[kv + i] = to_f(e[i]);
+        const T* src = row + c * 16 + kv;
+        b[c * (16 / EPV) + v] = (row == nullptr || kv >= kmax) ? zero4()
+                               : (kv + EPV <= kmax ? ldg16(src) : load_partial<E>(src, kmax - kv));
       }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) b[k] = 0.0f;
-    }
-#pragma unroll
-    for (int tt = 0; tt < kMfmaMinTokens; ++tt) {
-      if (tt < n) {
-        const float* vt = vs + tt * r + g * 16;
-        float sacc = acc[tt];
-        if (kmax == 16) {
-#pragma unroll
-          for (int k = 0; k < 16; ++k) sacc = fmaf(vt[k], b[k], sacc);
-        } else {
-          for (int k = 0; k < kmax; ++k) sacc = fmaf(vt[k], b[k], sacc);
-        }
-        acc[tt] = sacc;
-      }
-    }
-  }
+  };
+  uint4 bcur[8], bnext[8];
+  load_group(0, bcur);
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
   T* Y = reinterpret_cast<T*>(P.Y);
+  float yb[MT][CPL];
 #pragma unroll
-  for (int tt = 0; tt < kMfmaMinTokens; ++tt) {
+  for (int tt = 0; tt < MT; ++tt) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) yb[tt][c] = 0.0f;
+    if (tt < n && live) {
+      const T* src = Yb + (int64_t)cld(K.perm + t0 + tt) * P.ldyb + j0;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) yb[tt][c] = to_f(src[c]);
+    }
+  }
+  stage_v(K, P, d1.x, r, tb, n, vs, lane);
+  const int rs = G * 16;
+  float acc[MT][CPL];
+#pragma unroll
+  for (int tt = 0; tt < MT; ++tt)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[tt][c] = 0.0f;
+  for (int g = 0; g < G; ++g) {
+    if (g + 1 < G) load_group(g + 1, bnext);
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      float b[CPL][4];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[c][i] = b_elem(bcur, c, k4 * 4 + i, E());
+#pragma unroll
+      for (int tt = 0; tt < MT; ++tt) {
+        if (tt < n) {
+          const f4 vv = *reinterpret_cast<const f4*>(vs + tt * rs + g * 16 + k4 * 4);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[tt][c] = fmaf(vv[i], b[c][i], acc[tt][c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) bcur[v] = bnext[v];
+  }
+  if (!live) return;
+#pragma unroll
+  for (int tt = 0; tt < MT; ++tt) {
     if (tt < n) {
-      const int64_t row = K.perm[t0 + tt];
-      from_f(Y + row * P.ldy + j, to_f(Yb[row * P.ldyb + j]) + scale * acc[tt]);
+      T* dst = Y + (int64_t)cld(K.perm + t0 + tt) * P.ldy + j0;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) from_f(dst + c, yb[tt][c] + scale * acc[tt][c]);
     }
   }
 }
 
-// MBGMM expand item: (segment s, chunk of <= 64 tokens, 256-column slice).
+// MBGMM expand item (one wave): (segment, one 16-token tile, column block).
 // C[col][token] += B^T[col][rank] * v^T[rank][token]; B pages hold the 16
 // ranks of an output column contiguously, so each lane's operand is one
-// 16-byte load.  Wave w covers columns 64w..64w+63 (four 16-column tiles).
+// 16-byte load.  The block is done in quarters of four 16-column tiles, each
+// with all its B operands and Y_base values requested before the MFMAs.
 template <class E>
-__device__ void expand_mfma(const KArgs& K, const KProj& P, int js, int s, int local, char* smem) {
+__device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int jb, int4 d0, int4 d1, int local, float* vs,
+                            int lane) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
   constexpr int KSTEP = 4 * EPV;
-  const int a = K.seg_adapter[s];
-  const int r = K.rank[a];
-  const int t0 = K.seg_indptr[s];
-  const int n = K.seg_indptr[s + 1] - t0;
-  const float scale = K.alpha[a] / (float)r;
-  const int tb = local * kExpandTokens;
-  const int nt = min(kExpandTokens, n - tb);
-  float* vs = reinterpret_cast<float*>(smem);  // [nt][r]
-  const float* vsrc = P.v + K.v_indptr[s] + (int64_t)tb * r;
-  for (int idx = threadIdx.x; idx < nt * r; idx += kThreads) {
-    float sum = 0.0f;
-    for (int q = 0; q < P.nv; ++q) sum += vsrc[(int64_t)q * K.v_stride + idx];
-    vs[idx] = sum;
-  }
-  __syncthreads();
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, qq = lane >> 4;
+  constexpr int CB = 64 * (8 / (int)sizeof(T));
+  constexpr int NQ = CB / 64;      // quarters of 64 columns
+  constexpr int MAXKS = LORA_MAX_RANK / KSTEP;
+  const int a = d0.x, r = d0.y;
+  const int tb = local * kMfmaExpandTokens;
+  const int t0 = d0.z + tb;
+  const int nt = min(kMfmaExpandTokens, d0.w - tb);
+  const float scale = __int_as_float(d1.w) / (float)r;
+  const int rs = rank_groups(r) * 16;
+  stage_v(K, P, d1.x, r, tb, nt, vs, lane);
+  const int li = lane & 15, qq = lane >> 4;
   const int pw = 1 << K.pw_log2;
   const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
-  const int jw = js * kExpandCols + wave * 64;
-  f4 acc[4][4];
+  const int nks = ceil_div_i(r, KSTEP);
+  const bool one_page = pw >= CB;  // the block lies in one page of each group
+  const int bbase = cld(P.b_indptr + a);
+  const int ublk = (jb * CB) >> K.pw_log2;
+  const T* Yb = reinterpret_cast<const T*>(P.Yb);
+  T* Y = reinterpret_cast<T*>(P.Y);
+  const int64_t row = li < nt ? K.perm[t0 + li] : -1;
+  // v operands of this lane's token (li) for every K step
+  uint4 vv[MAXKS];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+  for (int ks = 0; ks < MAXKS; ++ks) {
+    const int k0 = ks * KSTEP + qq * EPV;
+    vv[ks] = (ks < nks && li < nt && k0 < r) ? pack_operand(vs + li * rs + k0, EPV, E()) : zero4();
+  }
+#pragma unroll 1
+  for (int quarter = 0; quarter < NQ; ++quarter) {
+    const int jq = jb * CB + quarter * 64;
+    if (jq >= P.d_out) break;
+    f4 acc[4];
+    uint4 bv[4][MAXKS];
+    float ybv[4][4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[ct][tt] = f4{0.f, 0.f, 0.f, 0.f};
-  if (jw < P.d_out) {
-    const int nks = ceil_div_i(r, KSTEP);
-    for (int ks = 0; ks < nks; ++ks) {
-      const int k0 = ks * KSTEP + qq * EPV;
-      const int kn = min(EPV, r - k0);  // valid ranks in this lane's vector (may be <= 0)
-      const int g = k0 >> 4;
-      uint4 bv[4], vv[4];
+    for (int ct = 0; ct < 4; ++ct) {
+      acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
+      const int j = jq + ct * 16 + li;
+      const bool jok = j < P.d_out;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int j = jw + ct * 16 + li;
-        bv[ct] = zero4();
-        if (j < P.d_out && kn > 0) {
-          const T* pg = page_ptr<E>(K, P.b_pages[P.b_indptr[a] + g * ncolB + (j >> K.pw_log2)]);
+      for (int ks = 0; ks < MAXKS; ++ks) {
+        const int k0 = ks * KSTEP + qq * EPV;
+        const int kn = min(EPV, r - k0);
+        bv[ct][ks] = zero4();
+        if (ks < nks && jok && kn > 0) {
+          const int g = k0 >> 4;
+          const T* pg;
+          if (one_page) {
+            // the lanes of one K step span at most two rank groups (uniform lookups)
+            const int g0 = (ks * KSTEP) >> 4;
+            const int gl = min(g0 + 1, rank_groups(r) - 1);
+            const T* p0 = page_ptr<E>(K, cld(P.b_pages + bbase + g0 * ncolB + ublk));
+            const T* p1 = page_ptr<E>(K, cld(P.b_pages + bbase + gl * ncolB + ublk));
+            pg = g == g0 ? p0 : p1;
+          } else {
+            pg = page_ptr<E>(K, P.b_pages[bbase + g * ncolB + (j >> K.pw_log2)]);
+          }
           if (pg != nullptr) {
             const T* src = pg + (j & (pw - 1)) * 16 + (k0 & 15);
-            bv[ct] = kn >= EPV ? ldg16(src) : load_partial<E>(src, kn);
+            bv[ct][ks] = kn >= EPV ? ldg16(src) : load_partial<E>(src, kn);
           }
         }
       }
+      const int col = jq + ct * 16 + qq * 4;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int tok = tt * 16 + li;
-        vv[tt] = (tok < nt && kn > 0) ? pack_operand(vs + tok * r + k0, kn, E()) : zero4();
-      }
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) mma(acc[ct][tt], bv[ct], vv[tt], E());
+      for (int i = 0; i < 4; ++i) ybv[ct][i] = (row >= 0 && col < P.d_out) ? to_f(Yb[row * P.ldyb + col + i]) : 0.0f;
     }
-  }
-  const T* Yb = reinterpret_cast<const T*>(P.Yb);
-  T* Y = reinterpret_cast<T*>(P.Y);
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const int tok = tt * 16 + li;
-    if (tok >= nt) continue;
-    const int64_t row = K.perm[t0 + tb + tok];
+    for (int ks = 0; ks < MAXKS; ++ks) {
+      if (ks < nks) {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int col = jw + ct * 16 + qq * 4;
-      if (col >= P.d_out) continue;
-      const T* yb = Yb + row * P.ldyb + col;
-      T* y = Y + row * P.ldy + col;
+        for (int ct = 0; ct < 4; ++ct) mma(acc[ct], bv[ct][ks], vv[ks], E());
+      }
+    }
+    if (row >= 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) from_f(y + i, to_f(yb[i]) + scale * acc[ct][tt][i]);
+      for (int ct = 0; ct < 4; ++ct) {
+        const int col = jq + ct * 16 + qq * 4;
+        if (col < P.d_out) {
+          T* y = Y + row * P.ldy + col;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) from_f(y + i, ybv[ct][i] + scale * acc[ct][i]);
+        }
+      }
     }
   }
 }
 
 // Rows of tokens without an adapter: Y = Y_base (only when Y is not Y_base).
 template <class E>
-__device__ void expand_copy(const KArgs& K, const KProj& P, int js, int chunk, int t_valid) {
+__device__ __forceinline__ void expand_copy(const KArgs& K, const KProj& P, int jb, int chunk, int t_valid, int lane) {
   typedef typename E::T T;
-  const int j = js * kExpandCols + threadIdx.x;
-  if (j >= P.d_out) return;
-  const int t_beg = t_valid + chunk * kExpandTokens;
-  const int t_end = min(K.T, t_beg + kExpandTokens);
+  constexpr int CPL = 8 / (int)sizeof(T);
+  const int j0 = jb * 64 * CPL + lane * CPL;
+  if (j0 >= P.d_out) return;
+  const int t_beg = t_valid + chunk * kValuExpandTokens;
+  const int t_end = min(K.T, t_beg + kValuExpandTokens);
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
   T* Y = reinterpret_cast<T*>(P.Y);
   for (int i = t_beg; i < t_end; ++i) {
     const int64_t row = K.perm[i];
-    Y[row * P.ldy + j] = Yb[row * P.ldyb + j];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) Y[row * P.ldy + j0 + c] = Yb[row * P.ldyb + j0 + c];
   }
 }
 
 template <class E>
-__global__ __launch_bounds__(kThreads) void expand_kernel(KArgs K) {
-  __shared__ __attribute__((aligned(16))) char smem[kExpandSmem];
+__global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArgs K) {
+  __shared__ __attribute__((aligned(16))) float vs_all[kWaves][kMfmaExpandTokens * LORA_MAX_RANK];
   const int S = K.counts[LORA_COUNT_S];
   const int t_valid = K.counts[LORA_COUNT_T_VALID];
   const int Ue = S > 0 ? K.counts[5] : 0;
-  const int ncopy = ceil_div_i(K.T - t_valid, kExpandTokens);
+  const int ncopy = ceil_div_i(K.T - t_valid, kValuExpandTokens);
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  float* vs = vs_all[wave];
   int total = 0;
   for (int p = 0; p < K.np; ++p) total += K.p[p].njs * (Ue + (K.p[p].Y != K.p[p].Yb ? ncopy : 0));
-  for (ItemWalk it(total); it.i < it.end; it.i += it.stride) {
-    int rem = it.i, p = 0;
-    int Up = Ue + (K.p[0].Y != K.p[0].Yb ? ncopy : 0);
-    while (rem >= K.p[p].njs * Up) {
-      rem -= K.p[p].njs * Up;
-      ++p;
-      Up = Ue + (K.p[p].Y != K.p[p].Yb ? ncopy : 0);
+  // Two walks over the same items: MBGMM items in the first, MBGMV and copy
+  // items in the second (separate register footprints, as in the shrink).
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    for (WaveWalk it(total, wave); it.i < it.end; it.i += it.stride) {
+      int rem = it.i, p = 0;
+      int Up = Ue + (K.p[0].Y != K.p[0].Yb ? ncopy : 0);
+      while (rem >= K.p[p].njs * Up) {
+        rem -= K.p[p].njs * Up;
+        ++p;
+        Up = Ue + (K.p[p].Y != K.p[p].Yb ? ncopy : 0);
+      }
+      const int jb = rem / Up;
+      const int u = rem - jb * Up;
+      if (u >= Ue) {
+        if (pass == 1) expand_copy<E>(K, K.p[p], jb, u - Ue, t_valid, lane);
+        continue;
+      }
+      const int s = cld(K.exp_item + u);
+      const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
+      if (is_mfma_segment(d0.w) != (pass == 0)) continue;
+      const int local = u - d1.z;
+      if (pass == 0) expand_mfma<E>(K, K.p[p], jb, d0, d1, local, vs, lane);
+      else expand_valu<E>(K, K.p[p], jb, d0, d1, local, vs, lane);
+      wave_sync();  // the wave's LDS rows are rewritten by its next item
     }
-    const KProj& P = K.p[p];
-    const int js = rem / Up;
-    const int u = rem - js * Up;
-    if (u >= Ue) {
-      expand_copy<E>(K, P, js, u - Ue, t_valid);
-    } else {
-      const int s = find_segment(K.exp_ptr, S, u);
-      const int local = u - K.exp_ptr[s];
-      const int n = K.seg_indptr[s + 1] - K.seg_indptr[s];
-      if (is_mfma_segment(n)) expand_mfma<E>(K, P, js, s, local, smem);
-      else expand_valu<E>(K, P, js, s, smem);
-    }
-    __syncthreads();
   }
 }
 
@@ -655,8 +820,8 @@ __device__ int block_exclusive_scan(int x, int* wsum, int* total) {
 // One work-group: column prefix of the chunk histograms, segment arrays,
 // ragged v offsets, work plan, counters.
 __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N, int nchunk,
-                                                                   const int32_t* rank, int32_t* hist,
-                                                                   SegOut out) {
+                                                                   const int32_t* rank, const float* alpha,
+                                                                   int32_t* hist, SegOut out) {
   __shared__ int wsum[kSegScanThreads / 64 + 1];
   __shared__ int carry[6];
   if (threadIdx.x < 6) carry[threadIdx.x] = 0;
@@ -687,6 +852,11 @@ __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N,
       out.v_indptr[si] = pre[2];
       out.shr_ptr[si] = pre[3];
       out.exp_ptr[si] = pre[4];
+      for (int i = 0; i < vals[3]; ++i) out.shr_item[pre[3] + i] = si;
+      for (int i = 0; i < vals[4]; ++i) out.exp_item[pre[4] + i] = si;
+      int4* desc = reinterpret_cast<int4*>(out.seg_desc) + 2 * si;
+      desc[0] = make_int4(a, r, pre[0], cnt);
+      desc[1] = make_int4(pre[2], pre[3], pre[4], __float_as_int(alpha[a]));
       for (int c = 0; c < nchunk; ++c) hist[(int64_t)c * W + a] += pre[0];
     }
     __syncthreads();
@@ -732,7 +902,9 @@ __global__ __launch_bounds__(kSegChunk) void seg_scatter_kernel(const int32_t* i
   const int c = blockIdx.x;
   const int i = threadIdx.x;
   const int t = c * kSegChunk + i;
-  constexpr uint32_t kExcluded = 0x3FFFFFu;
+  // class of tokens without an adapter; kept below 0x3FFFFF so that no real
+  // key (class << 10 | position) can equal the 0xFFFFFFFF padding key
+  constexpr uint32_t kExcluded = 0x3FFFFEu;
   uint32_t key = 0xFFFFFFFFu;
   if (t < T) {
     const int id = ids[t];
@@ -774,14 +946,14 @@ __global__ __launch_bounds__(kSegChunk) void seg_scatter_kernel(const int32_t* i
 // ================================================================ launchers
 static hipError_t launch_err() { return hipGetLastError(); }
 
-hipError_t launch_build_segments(const int32_t* ids, int T, int N, const int32_t* rank, int32_t* hist,
-                                 const SegOut& out, hipStream_t stream) {
+hipError_t launch_build_segments(const int32_t* ids, int T, int N, const int32_t* rank, const float* alpha,
+                                 int32_t* hist, const SegOut& out, hipStream_t stream) {
   const int nchunk = ceil_div_i(T, kSegChunk);
   if (nchunk > 0) {
     seg_hist_kernel<<<nchunk, kThreads, 0, stream>>>(ids, T, N, rank, hist);
     if (hipError_t e = launch_err()) return e;
   }
-  seg_scan_kernel<<<1, kSegScanThreads, 0, stream>>>(T, N, nchunk, rank, hist, out);
+  seg_scan_kernel<<<1, kSegScanThreads, 0, stream>>>(T, N, nchunk, rank, alpha, hist, out);
   if (hipError_t e = launch_err()) return e;
   if (nchunk > 0) {
     seg_scatter_kernel<<<nchunk, kSegChunk, 0, stream>>>(ids, T, N, rank, hist, out.perm);

@@ -19,7 +19,7 @@ from .build import LIB_PATH
 
 LORA_DTYPE_F32, LORA_DTYPE_BF16 = 0, 1
 LORA_MAX_RANK = 128
-LORA_KSLICE = 1024
+LORA_KSLICE = 512
 COUNT_S, COUNT_INVALID, COUNT_T_VALID, COUNT_V_TOTAL, COUNT_FLAGS = 0, 1, 2, 3, 6
 
 _vp = ctypes.c_void_p
@@ -44,7 +44,7 @@ class lora_proj_t(ctypes.Structure):
 class lora_segments_t(ctypes.Structure):
     _fields_ = [("T", _i32), ("num_adapters", _i32), ("perm", _vp), ("seg_indptr", _vp),
                 ("seg_adapter", _vp), ("v_indptr", _vp), ("shr_ptr", _vp), ("exp_ptr", _vp),
-                ("counts", _vp)]
+                ("shr_item", _vp), ("exp_item", _vp), ("seg_desc", _vp), ("counts", _vp)]
 
 
 _lib = None

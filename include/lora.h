@@ -66,7 +66,7 @@ typedef int32_t lora_status_t;
 
 #define LORA_PAGE_ROWS 16    /* ranks per page ("16-row pages") */
 #define LORA_MAX_RANK 128
-#define LORA_KSLICE 1024     /* input columns per shrink partial sum */
+#define LORA_KSLICE 512      /* input columns per shrink partial sum */
 #define LORA_MAX_ADAPTERS (1 << 20)
 
 /* Adapter set: one rank and one alpha per adapter, shared by every layer and
@@ -137,6 +137,8 @@ typedef struct {
  *   v_indptr[S_max+1]     offset of segment s in the ragged rank-r
  *                         intermediate v: v[v_indptr[s] + i*r + k]
  *   shr_ptr[S_max+1], exp_ptr[S_max+1]   work-plan prefix sums (internal)
+ *   shr_item[10T+1], exp_item[2T+1]      work item -> segment tables (internal)
+ *   seg_desc[8*S_max]     per-segment descriptors (internal)
  *   counts[8]             {S, n_invalid, T_valid, V_total, shrink items,
  *                         expand items, device error flags, reserved}
  * A token is valid when 0 <= ids[t] < num_adapters and its adapter's rank is
@@ -152,6 +154,9 @@ typedef struct {
   int32_t* v_indptr;
   int32_t* shr_ptr;
   int32_t* exp_ptr;
+  int32_t* shr_item;
+  int32_t* exp_item;
+  int32_t* seg_desc;
   int32_t* counts;
 } lora_segments_t;
 
@@ -175,7 +180,7 @@ lora_status_t lora_segments_init(void* buf, size_t bytes, int32_t T, int32_t num
  * projections whose largest input width is max_d_in. */
 size_t lora_workspace_size(int32_t T, int32_t num_adapters, int32_t n_projs, int32_t max_d_in);
 
-/* Number of shrink partial slices for an input width: ceil(d_in / 1024). */
+/* Number of shrink partial slices for an input width: ceil(d_in / 512). */
 int32_t lora_v_slices(int32_t d_in);
 
 /* Group the batch's tokens by adapter and build the work plan (a
@@ -189,7 +194,7 @@ lora_status_t lora_build_segments(const int32_t* ids, int32_t T, const lora_adap
 
 /* Shrink ([MLSP] SGMV: v_i = x_i A_i, the rank-r intermediate) for one
  * projection.  v: device fp32 [lora_v_slices(d_in)][v_stride]; slice q holds
- * the partial sum over inputs q*1024 .. min((q+1)*1024, d_in)-1 in the ragged
+ * the partial sum over inputs q*512 .. min((q+1)*512, d_in)-1 in the ragged
  * layout of v_indptr; v = sum of the slices in ascending q.  v_stride >=
  * T*128.  Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED, HIP. */
 lora_status_t lora_shrink(const lora_proj_t* proj, const lora_adapters_t* adapters,

@@ -38,8 +38,9 @@ def test_status_strings():
     for code in range(-7, 1):
         assert lora.lora_status_string(code) not in ("", "unknown status")
     assert lora.lora_status_string(-99) == "unknown status"
-    assert L.lora_v_slices(1) == 1 and L.lora_v_slices(1024) == 1 and L.lora_v_slices(1025) == 2
-    assert L.lora_v_slices(11008) == 11 and L.lora_v_slices(0) == 0
+    ks = lora.LORA_KSLICE
+    assert L.lora_v_slices(1) == 1 and L.lora_v_slices(ks) == 1 and L.lora_v_slices(ks + 1) == 2
+    assert L.lora_v_slices(11008) == -(-11008 // ks) and L.lora_v_slices(0) == 0
 
 
 def test_sizes():
@@ -48,7 +49,7 @@ def test_sizes():
     s = L.lora_segments_size(1024, 1000)
     assert s >= 4 * (1024 + 4 * 1001 + 1000 + 8)
     w = L.lora_workspace_size(1024, 1000, 3, 4096)
-    assert w >= s + 3 * 4 * 1024 * 128 * 4
+    assert w >= s + 3 * lora.lora_v_slices(4096) * 1024 * 128 * 4
     # projections beyond one launch reuse the same v area
     assert L.lora_workspace_size(8, 4, 16, 256) == L.lora_workspace_size(8, 4, 40, 256)
 
