@@ -30,7 +30,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int smax_of(int32_t T, int32_t N) { return std::max(0, std::min(T, N)); }
 
 struct SegSizes {
-  size_t perm, seg_indptr, seg_adapter, v_indptr, shr_ptr, exp_ptr, shr_item, exp_item, seg_desc, counts, total;
+  size_t perm, seg_indptr, seg_adapter, v_indptr, plan, counts, total;
 };
 
 SegSizes seg_sizes(int32_t T, int32_t N) {
@@ -40,15 +40,20 @@ SegSizes seg_sizes(int32_t T, int32_t N) {
   z.seg_indptr = align_up(sizeof(int32_t) * (sm + 1));
   z.seg_adapter = align_up(sizeof(int32_t) * std::max<size_t>(sm, 1));
   z.v_indptr = z.seg_indptr;
-  z.shr_ptr = z.seg_indptr;
-  z.exp_ptr = z.seg_indptr;
-  z.shr_item = align_up(sizeof(int32_t) * (size_t)shrink_item_capacity(T));
-  z.exp_item = align_up(sizeof(int32_t) * (size_t)expand_item_capacity(T));
-  z.seg_desc = align_up(sizeof(int32_t) * 8 * std::max<size_t>(sm, 1));
-  z.counts = align_up(sizeof(int32_t) * 8);
-  z.total = z.perm + z.seg_indptr + z.seg_adapter + z.v_indptr + z.shr_ptr + z.exp_ptr + z.shr_item +
-            z.exp_item + z.seg_desc + z.counts;
+  z.plan = align_up(sizeof(int32_t) * (size_t)plan_layout(T, N).total);
+  z.counts = align_up(sizeof(int32_t) * kNumCounts);
+  z.total = z.perm + z.seg_indptr + z.seg_adapter + z.v_indptr + z.plan + z.counts;
   return z;
+}
+
+// Pointers of the plan area of a segment buffer laid out for (T, N).
+struct PlanPtrs {
+  int32_t *seg_desc, *shr_m, *shr_v, *exp_m, *exp_v;
+};
+PlanPtrs plan_ptrs(const lora_segments_t* s) {
+  const PlanLayout L = plan_layout(s->T, s->num_adapters);
+  return PlanPtrs{s->plan + L.seg_desc, s->plan + L.shrink_mfma, s->plan + L.shrink_valu, s->plan + L.expand_mfma,
+                  s->plan + L.expand_valu};
 }
 
 size_t hist_bytes(int32_t T, int32_t N) {
@@ -67,8 +72,7 @@ lora_status_t check_adapters(const lora_adapters_t* ad) {
 }
 
 lora_status_t check_segs(const lora_segments_t* s) {
-  if (!s || !s->perm || !s->seg_indptr || !s->seg_adapter || !s->v_indptr || !s->shr_ptr ||
-      !s->exp_ptr || !s->shr_item || !s->exp_item || !s->seg_desc || !s->counts)
+  if (!s || !s->perm || !s->seg_indptr || !s->seg_adapter || !s->v_indptr || !s->plan || !s->counts)
     return LORA_ERR_INVALID_ARG;
   if (s->T < 0 || s->num_adapters < 1) return LORA_ERR_INVALID_ARG;
   return LORA_OK;
@@ -142,6 +146,7 @@ int grid_for(int resident, int64_t bound) {
 KProj make_kproj(const lora_proj_t& p, float* v, int nv, int dtype) {
   KProj k;
   memset(&k, 0, sizeof k);
+  const bool bf16 = dtype == LORA_DTYPE_BF16;
   k.X = p.X;
   k.Yb = p.Y_base;
   k.Y = p.Y;
@@ -156,25 +161,20 @@ KProj make_kproj(const lora_proj_t& p, float* v, int nv, int dtype) {
   k.d_in = p.d_in;
   k.d_out = p.d_out;
   k.nq = lora_v_slices(p.d_in);
-  k.njs = ceil_div_i(p.d_out, expand_cols(dtype == LORA_DTYPE_BF16));
+  k.njs = ceil_div_i(p.d_out, expand_cols(bf16));
   k.nv = nv;
   return k;
 }
 
-void fill_common(KArgs& K, const lora_segments_t* s, const lora_adapters_t* ad, const lora_pool_t* pool,
-                 int64_t v_stride) {
+void fill_common(KArgs& K, const lora_segments_t* s, const lora_pool_t* pool, int64_t v_stride) {
+  const PlanPtrs pp = plan_ptrs(s);
   K.perm = s->perm;
-  K.seg_indptr = s->seg_indptr;
-  K.seg_adapter = s->seg_adapter;
-  K.v_indptr = s->v_indptr;
-  K.shr_ptr = s->shr_ptr;
-  K.exp_ptr = s->exp_ptr;
-  K.shr_item = s->shr_item;
-  K.exp_item = s->exp_item;
-  K.seg_desc = reinterpret_cast<const int4*>(s->seg_desc);
+  K.seg_desc = reinterpret_cast<const int4*>(pp.seg_desc);
+  K.shr_item_m = pp.shr_m;
+  K.shr_item_v = pp.shr_v;
+  K.exp_item_m = pp.exp_m;
+  K.exp_item_v = pp.exp_v;
   K.counts = s->counts;
-  K.rank = ad->rank;
-  K.alpha = ad->alpha;
   K.pool = pool->base;
   K.v_stride = v_stride;
   K.num_pages = pool->num_pages;
@@ -188,8 +188,8 @@ lora_status_t run(const KArgs& K, int dtype, bool do_shrink, bool do_expand, hip
   const int di = dtype == LORA_DTYPE_BF16 ? 1 : 0;
   int64_t bs = 0, be = 0;
   for (int p = 0; p < K.np; ++p) {
-    bs += (int64_t)K.p[p].nq * shrink_item_capacity(K.T);
-    be += (int64_t)K.p[p].njs * (expand_item_capacity(K.T) + K.T);
+    bs += (int64_t)K.p[p].nq * (21LL * K.T + 2);
+    be += (int64_t)K.p[p].njs * (3LL * K.T + 2);
   }
   // items are per wave: kWaves items per work-group
   if (do_shrink && launch_shrink(K, dtype, grid_for(d->cus * d->occ_shrink[di], ceil_div64(bs, kWaves)), stream) !=
@@ -203,9 +203,9 @@ lora_status_t run(const KArgs& K, int dtype, bool do_shrink, bool do_expand, hip
 
 lora_status_t build_into(const int32_t* ids, int32_t T, const lora_adapters_t* ad, const lora_segments_t* segs,
                          int32_t* hist, hipStream_t stream) {
-  SegOut o{segs->perm,     segs->seg_indptr, segs->seg_adapter, segs->v_indptr,
-           segs->shr_ptr,  segs->exp_ptr,    segs->shr_item,    segs->exp_item,
-           segs->seg_desc, segs->counts};
+  const PlanPtrs pp = plan_ptrs(segs);
+  SegOut o{segs->perm, segs->seg_indptr, segs->seg_adapter, segs->v_indptr, pp.seg_desc,
+           pp.shr_m,   pp.shr_v,         pp.exp_m,          pp.exp_v,       segs->counts};
   return launch_build_segments(ids, T, ad->num_adapters, ad->rank, ad->alpha, hist, o, stream) == hipSuccess
              ? LORA_OK
              : LORA_ERR_HIP;
@@ -248,11 +248,7 @@ lora_status_t lora_segments_init(void* buf, size_t bytes, int32_t T, int32_t num
   out->seg_indptr = reinterpret_cast<int32_t*>(p); p += z.seg_indptr;
   out->seg_adapter = reinterpret_cast<int32_t*>(p); p += z.seg_adapter;
   out->v_indptr = reinterpret_cast<int32_t*>(p); p += z.v_indptr;
-  out->shr_ptr = reinterpret_cast<int32_t*>(p); p += z.shr_ptr;
-  out->exp_ptr = reinterpret_cast<int32_t*>(p); p += z.exp_ptr;
-  out->shr_item = reinterpret_cast<int32_t*>(p); p += z.shr_item;
-  out->exp_item = reinterpret_cast<int32_t*>(p); p += z.exp_item;
-  out->seg_desc = reinterpret_cast<int32_t*>(p); p += z.seg_desc;
+  out->plan = reinterpret_cast<int32_t*>(p); p += z.plan;
   out->counts = reinterpret_cast<int32_t*>(p);
   return LORA_OK;
 }
@@ -285,7 +281,7 @@ lora_status_t lora_shrink(const lora_proj_t* proj, const lora_adapters_t* adapte
   if (!v || v_stride < (int64_t)segs->T * LORA_MAX_RANK) return LORA_ERR_INVALID_ARG;
   KArgs K;
   memset(&K, 0, sizeof K);
-  fill_common(K, segs, adapters, pool, v_stride);
+  fill_common(K, segs, pool, v_stride);
   K.p[0] = make_kproj(*proj, v, lora_v_slices(proj->d_in), pool->dtype);
   K.np = 1;
   return run(K, pool->dtype, true, false, static_cast<hipStream_t>(stream));
@@ -301,7 +297,7 @@ lora_status_t lora_expand(const lora_proj_t* proj, const lora_adapters_t* adapte
   if (!v || v_slices < 1 || v_stride < (int64_t)segs->T * LORA_MAX_RANK) return LORA_ERR_INVALID_ARG;
   KArgs K;
   memset(&K, 0, sizeof K);
-  fill_common(K, segs, adapters, pool, v_stride);
+  fill_common(K, segs, pool, v_stride);
   K.p[0] = make_kproj(*proj, const_cast<float*>(v), v_slices, pool->dtype);
   K.np = 1;
   return run(K, pool->dtype, false, true, static_cast<hipStream_t>(stream));
@@ -348,7 +344,7 @@ lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_
   for (int base = 0; base < n_projs; base += kProjsPerLaunch) {
     KArgs K;
     memset(&K, 0, sizeof K);
-    fill_common(K, S, adapters, pool, v_stride);
+    fill_common(K, S, pool, v_stride);
     K.np = std::min(kProjsPerLaunch, n_projs - base);
     for (int i = 0; i < K.np; ++i) {
       float* v = reinterpret_cast<float*>(vbase + (size_t)i * vpp);

@@ -21,26 +21,20 @@ struct KProj {
   const int32_t* b_pages;
   int64_t ldx, ldyb, ldy;
   int32_t d_in, d_out;
-  int32_t nq;   // shrink slices written: ceil(d_in / 512)
-  int32_t njs;  // expand column blocks: ceil(d_out / expand_cols)
-  int32_t nv;   // v slices the expand sums
-  int32_t pad;
+  int32_t nq;     // shrink slices written: ceil(d_in / 512)
+  int32_t njs;    // MBGMV expand column blocks: ceil(d_out / expand_cols)
+  int32_t nv;     // v slices the expand sums
 };
 
 struct KArgs {
   KProj p[kProjsPerLaunch];
   const int32_t* perm;
-  const int32_t* seg_indptr;
-  const int32_t* seg_adapter;
-  const int32_t* v_indptr;
-  const int32_t* shr_ptr;
-  const int32_t* exp_ptr;
-  const int32_t* shr_item;
-  const int32_t* exp_item;
-  const int4* seg_desc;  // per segment: {a, r, t0, n}, {v_offset, shr_ptr, exp_ptr, alpha bits}
+  const int4* seg_desc;  // per segment: {a, r, t0, n}, {v_offset, shrink item0, expand item0, alpha bits}
+  const int32_t* shr_item_m;
+  const int32_t* shr_item_v;
+  const int32_t* exp_item_m;
+  const int32_t* exp_item_v;
   int32_t* counts;
-  const int32_t* rank;
-  const float* alpha;
   const void* pool;
   int64_t v_stride;
   int32_t num_pages;
@@ -54,11 +48,11 @@ struct SegOut {
   int32_t* seg_indptr;
   int32_t* seg_adapter;
   int32_t* v_indptr;
-  int32_t* shr_ptr;
-  int32_t* exp_ptr;
-  int32_t* shr_item;
-  int32_t* exp_item;
   int32_t* seg_desc;
+  int32_t* shr_item_m;
+  int32_t* shr_item_v;
+  int32_t* exp_item_m;
+  int32_t* exp_item_v;
   int32_t* counts;
 };
 

@@ -43,13 +43,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 struct Bf16 {
   typedef uint16_t T;
   static constexpr int kEpv = 8;  // elements per 16-byte vector
-  static constexpr int kShrinkBlocks = 3;  // occupancy targets (work-groups per CU)
+  static constexpr int kShrinkBlocks = 5;  // occupancy targets (work-groups per CU)
   static constexpr int kExpandBlocks = 3;
 };
 struct F32 {
   typedef float T;
   static constexpr int kEpv = 4;
-  static constexpr int kShrinkBlocks = 2;
+  static constexpr int kShrinkBlocks = 3;
   static constexpr int kExpandBlocks = 2;
 };
 
@@ -149,7 +149,7 @@ __device__ __forceinline__ void from_f(float* p, float f) { *p = f; }
 template <class E>
 __device__ __forceinline__ const typename E::T* page_ptr(const KArgs& K, int page) {
   if ((unsigned)page >= (unsigned)K.num_pages) {
-    atomicOr(&K.counts[LORA_COUNT_FLAGS], LORA_FLAG_PAGE_RANGE);
+    atomicOr(&K.counts[kCountFlags], LORA_FLAG_PAGE_RANGE);
     return nullptr;
   }
   return reinterpret_cast<const typename E::T*>(K.pool) + ((int64_t)page << (K.pw_log2 + 4));
@@ -220,13 +220,15 @@ __device__ __forceinline__ float wave_reduce_scatter32(float (&v)[32], int lane)
 // items: no work-group barrier couples the waves.
 struct WaveWalk {
   int i, end, stride;
-  __device__ WaveWalk(int total, int wave) {
+  // `walkers` items are taken per block at a time (kWaves: one per wave; 1:
+  // whole-block items), `w` is this walker's index in the block.
+  __device__ WaveWalk(int total, int w, int walkers = kWaves) {
     const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
     const int x = blockIdx.x % nx;
     const int lo = (int)(((int64_t)total * x) / nx);
     end = (int)(((int64_t)total * (x + 1)) / nx);
-    i = lo + (int)(blockIdx.x / nx) * kWaves + wave;
-    stride = (gridDim.x / nx) * kWaves;
+    i = lo + (int)(blockIdx.x / nx) * walkers + w;
+    stride = (gridDim.x / nx) * walkers;
   }
 };
 
@@ -309,207 +311,183 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int 
     P.v[(int64_t)q * K.v_stride + d1.x + (int64_t)(tb + tt) * r + g * 16 + rr] = sum;
 }
 
-// MBGMM item (one wave): (segment, token chunk, slice q), every rank group at
-// once so each activation byte is read once.  C[rank][token] +=
-// A^T[rank][col] * X^T[col][token] over the slice's 512 columns, with the
-// operands of SIF K steps requested before the first of their MFMAs.
-template <class E, int GM, int NTT, int SIF>
-__device__ __forceinline__ void shrink_mfma_body(const KArgs& K, const KProj& P, int q, int a, int r, int t0, int voff,
-                                 int tb, int nt, int lane) {
+// MBGMM item (one wave): (segment, 16-token tile, rank group g, slice q):
+// C[rank][token] += A^T[rank][col] * X^T[col][token] over the slice's 512
+// columns, one 16x16 tile, with the operands of 8 K steps requested before
+// the first of their MFMAs (two memory round trips per item).  The rank
+// groups of a token tile are consecutive items, so the tile's activations
+// are re-read from the L2 that holds them.
+template <class E>
+__device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int q, int4 d0, int4 d1, int local,
+                                            int lane) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
   constexpr int STEP = 4 * EPV;
   constexpr int NSTEP = kKSlice / STEP;
+  constexpr int SIF = 8;
   static_assert(NSTEP % SIF == 0, "steps in flight divide the slice");
-  const int li = lane & 15, qq = lane >> 4;
+  const int a = d0.x, r = d0.y, t0 = d0.z, n = d0.w;
   const int G = rank_groups(r);
+  const int tt = local / G;
+  const int g = local - tt * G;
+  const int tb = tt * 16;
+  const int nt = min(16, n - tb);
+  const int li = lane & 15, qq = lane >> 4;
   const int col0 = q * kKSlice;
   const int ncols = min(kKSlice, P.d_in - col0);
   const int pw = 1 << K.pw_log2;
-  const int ncolA = (P.d_in + pw - 1) >> K.pw_log2;
+  const int slot = cld(P.a_indptr + a) + g * ((P.d_in + pw - 1) >> K.pw_log2);
+  const bool one_page = pw >= kKSlice;
+  const T* pg1 = one_page ? page_ptr<E>(K, cld(P.a_pages + slot + (col0 >> K.pw_log2))) : nullptr;
+  const bool rok = g * 16 + li < r;
   const T* X = reinterpret_cast<const T*>(P.X);
-
-  const bool one_page = pw >= kKSlice;  // the slice lies in one page of each group
-  const int abase = cld(P.a_indptr + a);
-  int slot[GM];
-  bool rok[GM];
-  const T* pg1[GM];
-#pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    slot[g] = abase + g * ncolA;
-    rok[g] = g < G && g * 16 + li < r;
-    pg1[g] = (one_page && g < G) ? page_ptr<E>(K, cld(P.a_pages + slot[g] + (col0 >> K.pw_log2))) : nullptr;
-  }
-  int64_t xrow[NTT];
-#pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) {
-    const int tok = tt * 16 + li;
-    xrow[tt] = tok < nt ? (int64_t)K.perm[t0 + tb + tok] * P.ldx : -1;
-  }
-  f4 acc[GM][NTT];
-#pragma unroll
-  for (int g = 0; g < GM; ++g)
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) acc[g][tt] = f4{0.f, 0.f, 0.f, 0.f};
-
+  const int64_t xrow = li < nt ? (int64_t)K.perm[t0 + tb + li] * P.ldx : -1;
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
   for (int st0 = 0; st0 < NSTEP; st0 += SIF) {
-    uint4 av[SIF][GM], xv[SIF][NTT];
+    uint4 av[SIF], xv[SIF];
 #pragma unroll
     for (int j = 0; j < SIF; ++j) {
       const int c = (st0 + j) * STEP + qq * EPV;
       const bool ok = c < ncols;
       const int col = col0 + c;
-#pragma unroll
-      for (int g = 0; g < GM; ++g) {
-        av[j][g] = zero4();
-        if (ok && rok[g]) {
-          const T* pg = one_page ? pg1[g] : page_ptr<E>(K, P.a_pages[slot[g] + (col >> K.pw_log2)]);
-          if (pg != nullptr) av[j][g] = ldg16(pg + li * pw + (col & (pw - 1)));
-        }
+      av[j] = zero4();
+      if (ok && rok) {
+        const T* pg = one_page ? pg1 : page_ptr<E>(K, P.a_pages[slot + (col >> K.pw_log2)]);
+        if (pg != nullptr) av[j] = ldg16(pg + li * pw + (col & (pw - 1)));
       }
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) xv[j][tt] = (ok && xrow[tt] >= 0) ? ldg16(X + xrow[tt] + col) : zero4();
+      xv[j] = (ok && xrow >= 0) ? ldg16(X + xrow + col) : zero4();
     }
 #pragma unroll
-    for (int j = 0; j < SIF; ++j)
-#pragma unroll
-      for (int g = 0; g < GM; ++g)
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) mma(acc[g][tt], av[j][g], xv[j][tt], E());
+    for (int j = 0; j < SIF; ++j) mma(acc, av[j], xv[j], E());
   }
-  float* vout = P.v + (int64_t)q * K.v_stride + voff;
+  const int k0 = g * 16 + qq * 4;
+  if (li < nt) {
+    float* dst = P.v + (int64_t)q * K.v_stride + d1.x + (int64_t)(tb + li) * r + k0;
 #pragma unroll
-  for (int g = 0; g < GM; ++g) {
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
-      const int tok = tt * 16 + li;
-      const int k0 = g * 16 + qq * 4;
-      if (g < G && tok < nt) {
-        float* dst = vout + (int64_t)(tb + tok) * r + k0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (k0 + i < r) dst[i] = acc[g][tt][i];
-      }
-    }
+    for (int i = 0; i < 4; ++i)
+      if (k0 + i < r) dst[i] = acc[i];
   }
-}
-
-template <class E>
-__device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int q, int4 d0, int4 d1, int local, int lane) {
-  const int a = d0.x, r = d0.y, t0 = d0.z, n = d0.w;
-  const int G = rank_groups(r);
-  const int tch = 16 * mfma_token_tiles(G);
-  const int tb = local * tch;
-  const int nt = min(tch, n - tb);
-  if (G <= 1) shrink_mfma_body<E, 1, 4, 4>(K, P, q, a, r, t0, d1.x, tb, nt, lane);
-  else if (G == 2) shrink_mfma_body<E, 2, 2, 4>(K, P, q, a, r, t0, d1.x, tb, nt, lane);
-  else if (G <= 4) shrink_mfma_body<E, 4, 1, 4>(K, P, q, a, r, t0, d1.x, tb, nt, lane);
-  else shrink_mfma_body<E, 8, 1, 1>(K, P, q, a, r, t0, d1.x, tb, nt, lane);
 }
 
 template <class E>
 __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArgs K) {
-  const int S = K.counts[LORA_COUNT_S];
-  const int U = K.counts[4];
+  const int S = cld(K.counts + kCountS);
   if (S <= 0) return;
+  const int Um = cld(K.counts + kCountShrinkMfma), Uv = cld(K.counts + kCountShrinkValu);
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // MBGMM items first, then MBGMV items; each path walks its own item list,
+  // so the two register footprints never share a loop body.
   int total = 0;
-  for (int p = 0; p < K.np; ++p) total += K.p[p].nq * U;
-  // Two walks over the same items, MBGMM items in the first and MBGMV items
-  // in the second, so the register footprints of the two paths never share
-  // a loop body.
-#pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    for (WaveWalk it(total, wave); it.i < it.end; it.i += it.stride) {
-      int rem = it.i, p = 0;
-      while (rem >= K.p[p].nq * U) { rem -= K.p[p].nq * U; ++p; }
-      const int q = rem / U;
-      const int u = rem - q * U;
-      const int s = cld(K.shr_item + u);
-      const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
-      if (is_mfma_segment(d0.w) != (pass == 0)) continue;
-      const int local = u - d1.y;
-      if (pass == 0) shrink_mfma<E>(K, K.p[p], q, d0, d1, local, lane);
-      else shrink_valu<E>(K, K.p[p], q, d0, d1, local, lane);
-    }
+  for (int p = 0; p < K.np; ++p) total += K.p[p].nq * Um;
+  for (WaveWalk it(total, wave); it.i < it.end; it.i += it.stride) {
+    int rem = it.i, p = 0;
+    while (rem >= K.p[p].nq * Um) { rem -= K.p[p].nq * Um; ++p; }
+    const int q = rem / Um;
+    const int u = rem - q * Um;
+    const int s = cld(K.shr_item_m + u);
+    const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
+    shrink_mfma<E>(K, K.p[p], q, d0, d1, u - d1.y, lane);
+  }
+  total = 0;
+  for (int p = 0; p < K.np; ++p) total += K.p[p].nq * Uv;
+  for (WaveWalk it(total, wave); it.i < it.end; it.i += it.stride) {
+    int rem = it.i, p = 0;
+    while (rem >= K.p[p].nq * Uv) { rem -= K.p[p].nq * Uv; ++p; }
+    const int q = rem / Uv;
+    const int u = rem - q * Uv;
+    const int s = cld(K.shr_item_v + u);
+    const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
+    shrink_valu<E>(K, K.p[p], q, d0, d1, u - d1.y, lane);
   }
 }
 
 // ================================================================ expand
-// v of tokens [tb, tb+nt) of a segment into the wave's LDS rows of G*16
-// floats, ranks >= r zero-filled.  The chunk's v is nt*r contiguous floats in
-// every partial slice; in passes of 1024 elements each lane sums 16 of them
-// over the slices (ascending slice order), two slices' loads in flight.
-__device__ __forceinline__ void stage_v(const KArgs& K, const KProj& P, int voff, int r, int tb, int nt,
-                                        float* vs, int lane) {
-  constexpr int M = 16;
+// v of tokens [tb, tb+nt) of a segment into LDS rows of G*16 floats, ranks
+// >= r zero-filled, by NT threads (one wave, or a whole block).  The chunk's
+// v is nt*r contiguous floats in every partial slice.  Each thread sums M of
+// them over the slices, SF slices' loads in flight at a time (M*SF = 16);
+// every element is summed in ascending slice order whatever M and SF are.
+template <int NT, int M, int SF>
+__device__ __forceinline__ void stage_v_pass(const KArgs& K, const KProj& P, const float* src, int e0, int ne,
+                                             int r, int rs, float* vs, int tid) {
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+  for (int q = 0; q < P.nv; q += SF) {
+    float x[SF][M];
+#pragma unroll
+    for (int j = 0; j < SF; ++j)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int e = e0 + tid + NT * m;
+        x[j][m] = (q + j < P.nv && e < ne) ? src[(int64_t)(q + j) * K.v_stride + e] : 0.0f;
+      }
+#pragma unroll
+    for (int j = 0; j < SF; ++j)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[m] += x[j][m];
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int e = e0 + tid + NT * m;
+    if (e < ne) {
+      const int t = e / r;
+      vs[t * rs + (e - t * r)] = acc[m];
+    }
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void stage_v_rows(const KArgs& K, const KProj& P, int voff, int r, int tb, int nt,
+                                             float* vs, int tid) {
   const int rs = rank_groups(r) * 16;
   const int ne = nt * r;
   const float* src = P.v + voff + (int64_t)tb * r;
-  for (int e0 = 0; e0 < ne; e0 += 64 * M) {
-    float acc[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-    int q = 0;
-    for (; q + 2 <= P.nv; q += 2) {
-      float x[2][M];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const int e = e0 + lane + 64 * m;
-          x[j][m] = e < ne ? src[(int64_t)(q + j) * K.v_stride + e] : 0.0f;
-        }
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] = (acc[m] + x[0][m]) + x[1][m];
-    }
-    if (q < P.nv) {
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const int e = e0 + lane + 64 * m;
-        if (e < ne) acc[m] += src[(int64_t)q * K.v_stride + e];
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const int e = e0 + lane + 64 * m;
-      if (e < ne) {
-        const int t = e / r;
-        vs[t * rs + (e - t * r)] = acc[m];
-      }
-    }
-  }
-  for (int idx = lane; idx < nt * (rs - r); idx += 64) {  // zero the rank padding of every row
+  const int mm = ceil_div_i(ne, NT);
+  if (mm <= 1) stage_v_pass<NT, 1, 16>(K, P, src, 0, ne, r, rs, vs, tid);
+  else if (mm <= 2) stage_v_pass<NT, 2, 8>(K, P, src, 0, ne, r, rs, vs, tid);
+  else if (mm <= 4) stage_v_pass<NT, 4, 4>(K, P, src, 0, ne, r, rs, vs, tid);
+  else if (mm <= 8) stage_v_pass<NT, 8, 2>(K, P, src, 0, ne, r, rs, vs, tid);
+  else
+    for (int e0 = 0; e0 < ne; e0 += NT * 16) stage_v_pass<NT, 16, 1>(K, P, src, e0, ne, r, rs, vs, tid);
+  for (int idx = tid; idx < nt * (rs - r); idx += NT) {  // zero the rank padding of every row
     const int t = idx / (rs - r);
     vs[t * rs + r + (idx - t * (rs - r))] = 0.0f;
   }
+}
+
+// one wave stages its own rows
+__device__ __forceinline__ void stage_v(const KArgs& K, const KProj& P, int voff, int r, int tb, int nt,
+                                        float* vs, int lane) {
+  stage_v_rows<64>(K, P, voff, r, tb, nt, vs, lane);
   wave_sync();
 }
 
-// B element k (rank within the group) of lane-local column c, from the 8
-// vectors a lane holds per rank group.
-__device__ __forceinline__ float b_elem(const uint4 (&b)[8], int c, int k, Bf16) {
+// B element k (rank within the group) of lane-local column c, from the 4
+// vectors (64 bytes) a lane holds per rank group.
+__device__ __forceinline__ float b_elem(const uint4 (&b)[4], int c, int k, Bf16) {
   const uint32_t u = (&b[0].x)[(c * 16 + k) >> 1];
   return (k & 1) ? bf_hi(u) : bf_lo(u);
 }
-__device__ __forceinline__ float b_elem(const uint4 (&b)[8], int c, int k, F32) {
+__device__ __forceinline__ float b_elem(const uint4 (&b)[4], int c, int k, F32) {
   return __uint_as_float((&b[0].x)[c * 16 + k]);
 }
 
 // MBGMV expand item (one wave): (segment, <= 8 tokens, column block).  Each
-// lane owns CPL adjacent output columns (4 in bf16, 2 in fp32) whose 16-rank
-// rows are adjacent in the B page: 128 contiguous bytes per lane and rank
-// group, 8 KiB per wave.  The next group's B is fetched while the current
-// one is consumed; Y_base of the tokens is fetched before v is staged.
+// lane owns CPL adjacent output columns (2 in bf16, 1 in fp32) whose 16-rank
+// rows are adjacent in the B page: 64 contiguous bytes per lane and rank
+// group, 4 KiB per wave.  The B loads of up to four rank groups and the
+// Y_base loads are issued before v is staged.
 template <class E>
-__device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, int jb, int4 d0, int4 d1, int local, float* vs,
-                            int lane) {
+__device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, int jb, int4 d0, int4 d1, int local,
+                                            float* vs, int lane) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
-  constexpr int CPL = 8 / (int)sizeof(T);
+  constexpr int CPL = 4 / (int)sizeof(T);
   constexpr int CB = 64 * CPL;
   constexpr int MT = kValuExpandTokens;
+  constexpr int GB = 4;  // rank groups per batch of loads
   const int a = d0.x, r = d0.y;
   const int tb = local * MT;
   const int t0 = d0.z + tb;
@@ -522,26 +500,30 @@ __device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, int 
   const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
   const bool one_page = pw >= CB;  // the block lies in one page of each group
   const int bbase = cld(P.b_indptr + a);
-  const int slot0 = bbase + (j0 >> K.pw_log2);
-  const int uslot0 = bbase + ((jb * CB) >> K.pw_log2);
-  auto load_group = [&](int g, uint4 (&b)[8]) {
-    const int kmax = min(16, r - g * 16);
-    const T* pg = !live ? nullptr
-                 : one_page ? page_ptr<E>(K, cld(P.b_pages + uslot0 + g * ncolB))
-                            : page_ptr<E>(K, P.b_pages[slot0 + g * ncolB]);
-    const T* row = pg == nullptr ? nullptr : pg + (j0 & (pw - 1)) * 16;
+  const int ublk = (jb * CB) >> K.pw_log2;
+  const int off = (j0 & (pw - 1)) * 16;
+  auto load_batch = [&](int g0, uint4 (&b)[GB][4]) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
+    for (int gi = 0; gi < GB; ++gi) {
+      const int g = g0 + gi;
+      const int kmax = min(16, r - g * 16);
+      const T* pg = nullptr;
+      if (g < G && live)
+        pg = one_page ? page_ptr<E>(K, cld(P.b_pages + bbase + g * ncolB + ublk))
+                      : page_ptr<E>(K, P.b_pages[bbase + g * ncolB + (j0 >> K.pw_log2)]);
 #pragma unroll
-      for (int v = 0; v < 16 / EPV; ++v) {
-        const int kv = v * EPV;
-        const T* src = row + c * 16 + kv;
-        b[c * (16 / EPV) + v] = (row == nullptr || kv >= kmax) ? zero4()
-                               : (kv + EPV <= kmax ? ldg16(src) : load_partial<E>(src, kmax - kv));
-      }
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int v = 0; v < 16 / EPV; ++v) {
+          const int kv = v * EPV;
+          const T* src = pg + off + c * 16 + kv;
+          b[gi][c * (16 / EPV) + v] = (pg == nullptr || kv >= kmax) ? zero4()
+                                      : (kv + EPV <= kmax ? ldg16(src) : load_partial<E>(src, kmax - kv));
+        }
+    }
   };
-  uint4 bcur[8], bnext[8];
-  load_group(0, bcur);
+  uint4 b[GB][4];
+  load_batch(0, b);
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
   T* Y = reinterpret_cast<T*>(P.Y);
   float yb[MT][CPL];
@@ -562,28 +544,30 @@ __device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, int 
   for (int tt = 0; tt < MT; ++tt)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[tt][c] = 0.0f;
-  for (int g = 0; g < G; ++g) {
-    if (g + 1 < G) load_group(g + 1, bnext);
+  for (int g0 = 0; g0 < G; g0 += GB) {
+    if (g0 > 0) load_batch(g0, b);
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      float b[CPL][4];
+    for (int gi = 0; gi < GB; ++gi) {
+      if (g0 + gi >= G) break;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c)
+      for (int k4 = 0; k4 < 4; ++k4) {
+        float bv[CPL][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b[c][i] = b_elem(bcur, c, k4 * 4 + i, E());
+        for (int c = 0; c < CPL; ++c)
 #pragma unroll
-      for (int tt = 0; tt < MT; ++tt) {
-        if (tt < n) {
-          const f4 vv = *reinterpret_cast<const f4*>(vs + tt * rs + g * 16 + k4 * 4);
+          for (int i = 0; i < 4; ++i) bv[c][i] = b_elem(b[gi], c, k4 * 4 + i, E());
 #pragma unroll
-          for (int c = 0; c < CPL; ++c)
+        for (int tt = 0; tt < MT; ++tt) {
+          if (tt < n) {
+            const f4 vv = *reinterpret_cast<const f4*>(vs + tt * rs + (g0 + gi) * 16 + k4 * 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[tt][c] = fmaf(vv[i], b[c][i], acc[tt][c]);
+            for (int c = 0; c < CPL; ++c)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[tt][c] = fmaf(vv[i], bv[c][i], acc[tt][c]);
+          }
         }
       }
     }
-#pragma unroll
-    for (int v = 0; v < 8; ++v) bcur[v] = bnext[v];
   }
   if (!live) return;
 #pragma unroll
@@ -596,110 +580,154 @@ __device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, int 
   }
 }
 
-// MBGMM expand item (one wave): (segment, one 16-token tile, column block).
-// C[col][token] += B^T[col][rank] * v^T[rank][token]; B pages hold the 16
+// Y_base / Y access of 4 consecutive output columns (the 4 C values a lane
+// holds for one token).
+__device__ __forceinline__ void load4(const uint16_t* p, float (&y)[4]) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  y[0] = bf_lo(u.x); y[1] = bf_hi(u.x); y[2] = bf_lo(u.y); y[3] = bf_hi(u.y);
+}
+__device__ __forceinline__ void load4(const float* p, float (&y)[4]) {
+  const float4 u = *reinterpret_cast<const float4*>(p);
+  y[0] = u.x; y[1] = u.y; y[2] = u.z; y[3] = u.w;
+}
+__device__ __forceinline__ void store4(uint16_t* p, const float (&y)[4]) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
+}
+__device__ __forceinline__ void store4(float* p, const float (&y)[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(y[0], y[1], y[2], y[3]);
+}
+
+// MBGMM expand item (one wave): (segment, one 16-token tile, column block of
+// 1024 columns in bf16 / 512 in fp32).  v of the tile is staged once; the
+// block is walked in parts of four 16-column tiles, the B operands and
+// Y_base values of part p+1 requested while part p is multiplied.
+// C[col][token] += B^T[col][rank] * v^T[rank][token]: B pages hold the 16
 // ranks of an output column contiguously, so each lane's operand is one
-// 16-byte load.  The block is done in quarters of four 16-column tiles, each
-// with all its B operands and Y_base values requested before the MFMAs.
-template <class E>
-__device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int jb, int4 d0, int4 d1, int local, float* vs,
-                            int lane) {
+// 16-byte load, and a lane's four C values are four adjacent columns of one
+// token (one 8- or 16-byte Y access).
+template <class E, int NKS>
+__device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P, int j0, int jend, int wc, int a,
+                                                 int r, int t0, int nt, float scale, const float* vs, int lane) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
   constexpr int KSTEP = 4 * EPV;
-  constexpr int CB = 64 * (8 / (int)sizeof(T));
-  constexpr int NQ = CB / 64;      // quarters of 64 columns
-  constexpr int MAXKS = LORA_MAX_RANK / KSTEP;
-  const int a = d0.x, r = d0.y;
-  const int tb = local * kMfmaExpandTokens;
-  const int t0 = d0.z + tb;
-  const int nt = min(kMfmaExpandTokens, d0.w - tb);
-  const float scale = __int_as_float(d1.w) / (float)r;
-  const int rs = rank_groups(r) * 16;
-  stage_v(K, P, d1.x, r, tb, nt, vs, lane);
+  // 16-column tiles per part: the operands of two parts (current and next)
+  // stay within 64 VGPRs.
+  constexpr int CT = NKS >= 8 ? 1 : 8 / NKS > 4 ? 4 : 8 / NKS;
+  constexpr int PART = 16 * CT;
   const int li = lane & 15, qq = lane >> 4;
+  const int rs = rank_groups(r) * 16;
   const int pw = 1 << K.pw_log2;
   const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
-  const int nks = ceil_div_i(r, KSTEP);
-  const bool one_page = pw >= CB;  // the block lies in one page of each group
+  const bool one_page = pw >= wc;  // [j0, j0+wc) is wc-aligned: one page of each group
   const int bbase = cld(P.b_indptr + a);
-  const int ublk = (jb * CB) >> K.pw_log2;
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
   T* Y = reinterpret_cast<T*>(P.Y);
   const int64_t row = li < nt ? K.perm[t0 + li] : -1;
-  // v operands of this lane's token (li) for every K step
-  uint4 vv[MAXKS];
+  const T* pgk[NKS];
 #pragma unroll
-  for (int ks = 0; ks < MAXKS; ++ks) {
+  for (int ks = 0; ks < NKS; ++ks) {
     const int k0 = ks * KSTEP + qq * EPV;
-    vv[ks] = (ks < nks && li < nt && k0 < r) ? pack_operand(vs + li * rs + k0, EPV, E()) : zero4();
+    pgk[ks] = (one_page && k0 < r) ? page_ptr<E>(K, P.b_pages[bbase + (k0 >> 4) * ncolB + (j0 >> K.pw_log2)])
+                                   : nullptr;
   }
-#pragma unroll 1
-  for (int quarter = 0; quarter < NQ; ++quarter) {
-    const int jq = jb * CB + quarter * 64;
-    if (jq >= P.d_out) break;
-    f4 acc[4];
-    uint4 bv[4][MAXKS];
-    float ybv[4][4];
+  uint4 vv[NKS];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
-      const int j = jq + ct * 16 + li;
-      const bool jok = j < P.d_out;
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int k0 = ks * KSTEP + qq * EPV;
+    vv[ks] = (li < nt && k0 < r) ? pack_operand(vs + li * rs + k0, EPV, E()) : zero4();
+  }
+  auto load_part = [&](int part, uint4 (&bv)[CT][NKS], float (&ybv)[CT][4]) {
 #pragma unroll
-      for (int ks = 0; ks < MAXKS; ++ks) {
+    for (int ct = 0; ct < CT; ++ct) {
+      const int jl = part * PART + ct * 16 + li;
+      const int j = j0 + jl;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
         const int k0 = ks * KSTEP + qq * EPV;
         const int kn = min(EPV, r - k0);
         bv[ct][ks] = zero4();
-        if (ks < nks && jok && kn > 0) {
-          const int g = k0 >> 4;
-          const T* pg;
-          if (one_page) {
-            // the lanes of one K step span at most two rank groups (uniform lookups)
-            const int g0 = (ks * KSTEP) >> 4;
-            const int gl = min(g0 + 1, rank_groups(r) - 1);
-            const T* p0 = page_ptr<E>(K, cld(P.b_pages + bbase + g0 * ncolB + ublk));
-            const T* p1 = page_ptr<E>(K, cld(P.b_pages + bbase + gl * ncolB + ublk));
-            pg = g == g0 ? p0 : p1;
-          } else {
-            pg = page_ptr<E>(K, P.b_pages[bbase + g * ncolB + (j >> K.pw_log2)]);
-          }
+        if (jl < jend && kn > 0) {
+          const T* pg = one_page ? pgk[ks] : page_ptr<E>(K, P.b_pages[bbase + (k0 >> 4) * ncolB + (j >> K.pw_log2)]);
           if (pg != nullptr) {
             const T* src = pg + (j & (pw - 1)) * 16 + (k0 & 15);
             bv[ct][ks] = kn >= EPV ? ldg16(src) : load_partial<E>(src, kn);
           }
         }
       }
-      const int col = jq + ct * 16 + qq * 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ybv[ct][i] = (row >= 0 && col < P.d_out) ? to_f(Yb[row * P.ldyb + col + i]) : 0.0f;
+      const int c4 = part * PART + ct * 16 + qq * 4;
+      if (row >= 0 && c4 < jend) load4(Yb + row * P.ldyb + j0 + c4, ybv[ct]);
+      else ybv[ct][0] = ybv[ct][1] = ybv[ct][2] = ybv[ct][3] = 0.0f;
     }
+  };
+  uint4 bcur[CT][NKS], bnext[CT][NKS];
+  float ycur[CT][4], ynext[CT][4];
+  const int np = ceil_div_i(jend, PART);
+  load_part(0, bcur, ycur);
+  for (int part = 0; part < np; ++part) {
+    if (part + 1 < np) load_part(part + 1, bnext, ynext);
+    f4 acc[CT];
 #pragma unroll
-    for (int ks = 0; ks < MAXKS; ++ks) {
-      if (ks < nks) {
+    for (int ct = 0; ct < CT; ++ct) {
+      acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) mma(acc[ct], bv[ct][ks], vv[ks], E());
-      }
+      for (int ks = 0; ks < NKS; ++ks) mma(acc[ct], bcur[ct][ks], vv[ks], E());
     }
     if (row >= 0) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int col = jq + ct * 16 + qq * 4;
-        if (col < P.d_out) {
-          T* y = Y + row * P.ldy + col;
+      for (int ct = 0; ct < CT; ++ct) {
+        const int c4 = part * PART + ct * 16 + qq * 4;
+        if (c4 < jend) {
+          float y[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) from_f(y + i, ybv[ct][i] + scale * acc[ct][i]);
+          for (int i = 0; i < 4; ++i) y[i] = ycur[ct][i] + scale * acc[ct][i];
+          store4(Y + row * P.ldy + j0 + c4, y);
         }
       }
     }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) bcur[ct][ks] = bnext[ct][ks];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ycur[ct][i] = ynext[ct][i];
+    }
   }
+}
+
+// MBGMM expand item (one block): (segment, 16-token tile, 4*wc columns).  The
+// block stages v of the tile once into shared LDS rows; wave w then produces
+// columns [w*wc, (w+1)*wc) of the item.
+template <class E>
+__device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int jb, int wc, int4 d0, int4 d1,
+                                            int local, float* vs, int wave, int lane) {
+  constexpr int KSTEP = 4 * E::kEpv;
+  constexpr int MAXKS = LORA_MAX_RANK / KSTEP;
+  const int a = d0.x, r = d0.y;
+  const int tb = local * kMfmaExpandTokens;
+  const int t0 = d0.z + tb;
+  const int nt = min(kMfmaExpandTokens, d0.w - tb);
+  const float scale = __int_as_float(d1.w) / (float)r;
+  stage_v_rows<kThreads>(K, P, d1.x, r, tb, nt, vs, threadIdx.x);
+  __syncthreads();
+  const int j0 = (jb * kWaves + wave) * wc;
+  const int jend = min(wc, P.d_out - j0);
+  if (jend > 0) {
+    const int nks = ceil_div_i(r, KSTEP);
+    if (nks <= 1) expand_mfma_body<E, 1>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
+    else if (nks <= 2) expand_mfma_body<E, 2>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
+    else if (MAXKS <= 4 || nks <= 4)
+      expand_mfma_body<E, MAXKS <= 4 ? MAXKS : 4>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
+    else expand_mfma_body<E, MAXKS>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
+  }
+  __syncthreads();  // the rows are restaged by the block's next item
 }
 
 // Rows of tokens without an adapter: Y = Y_base (only when Y is not Y_base).
 template <class E>
 __device__ __forceinline__ void expand_copy(const KArgs& K, const KProj& P, int jb, int chunk, int t_valid, int lane) {
   typedef typename E::T T;
-  constexpr int CPL = 8 / (int)sizeof(T);
+  constexpr int CPL = 4 / (int)sizeof(T);
   const int j0 = jb * 64 * CPL + lane * CPL;
   if (j0 >= P.d_out) return;
   const int t_beg = t_valid + chunk * kValuExpandTokens;
@@ -716,40 +744,60 @@ __device__ __forceinline__ void expand_copy(const KArgs& K, const KProj& P, int 
 template <class E>
 __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArgs K) {
   __shared__ __attribute__((aligned(16))) float vs_all[kWaves][kMfmaExpandTokens * LORA_MAX_RANK];
-  const int S = K.counts[LORA_COUNT_S];
-  const int t_valid = K.counts[LORA_COUNT_T_VALID];
-  const int Ue = S > 0 ? K.counts[5] : 0;
+  const int S = cld(K.counts + kCountS);
+  const int t_valid = cld(K.counts + kCountTValid);
+  const int Um = S > 0 ? cld(K.counts + kCountExpandMfma) : 0;
+  const int Uv = S > 0 ? cld(K.counts + kCountExpandValu) : 0;
   const int ncopy = ceil_div_i(K.T - t_valid, kValuExpandTokens);
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   float* vs = vs_all[wave];
-  int total = 0;
-  for (int p = 0; p < K.np; ++p) total += K.p[p].njs * (Ue + (K.p[p].Y != K.p[p].Yb ? ncopy : 0));
-  // Two walks over the same items: MBGMM items in the first, MBGMV and copy
-  // items in the second (separate register footprints, as in the shrink).
-#pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    for (WaveWalk it(total, wave); it.i < it.end; it.i += it.stride) {
-      int rem = it.i, p = 0;
-      int Up = Ue + (K.p[0].Y != K.p[0].Yb ? ncopy : 0);
-      while (rem >= K.p[p].njs * Up) {
-        rem -= K.p[p].njs * Up;
-        ++p;
-        Up = Ue + (K.p[p].Y != K.p[p].Yb ? ncopy : 0);
-      }
-      const int jb = rem / Up;
-      const int u = rem - jb * Up;
-      if (u >= Ue) {
-        if (pass == 1) expand_copy<E>(K, K.p[p], jb, u - Ue, t_valid, lane);
-        continue;
-      }
-      const int s = cld(K.exp_item + u);
-      const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
-      if (is_mfma_segment(d0.w) != (pass == 0)) continue;
-      const int local = u - d1.z;
-      if (pass == 0) expand_mfma<E>(K, K.p[p], jb, d0, d1, local, vs, lane);
-      else expand_valu<E>(K, K.p[p], jb, d0, d1, local, vs, lane);
-      wave_sync();  // the wave's LDS rows are rewritten by its next item
+  // MBGMM items first (whole-block items), then MBGMV items and the copies of
+  // rows without an adapter (one wave each); each path walks its own item
+  // list.  The columns per wave of an MBGMM item (64..256) shrink until the
+  // items cover about twice the grid, so a few hot segments still spread
+  // over every compute unit.
+  if (Um > 0) {
+    int wc = 256, total = 0;
+    for (;; wc >>= 1) {
+      total = 0;
+      for (int p = 0; p < K.np; ++p) total += ceil_div_i(K.p[p].d_out, kWaves * wc) * Um;
+      if (wc == 64 || total >= 2 * (int)gridDim.x) break;
     }
+    for (WaveWalk it(total, 0, 1); it.i < it.end; it.i += it.stride) {
+      int rem = it.i, p = 0;
+      int nb = ceil_div_i(K.p[0].d_out, kWaves * wc);
+      while (rem >= nb * Um) {
+        rem -= nb * Um;
+        ++p;
+        nb = ceil_div_i(K.p[p].d_out, kWaves * wc);
+      }
+      const int jb = rem / Um;
+      const int u = rem - jb * Um;
+      const int s = cld(K.exp_item_m + u);
+      const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
+      expand_mfma<E>(K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[0], wave, lane);
+    }
+  }
+  int total = 0;
+  for (int p = 0; p < K.np; ++p) total += K.p[p].njs * (Uv + (K.p[p].Y != K.p[p].Yb ? ncopy : 0));
+  for (WaveWalk it(total, wave); it.i < it.end; it.i += it.stride) {
+    int rem = it.i, p = 0;
+    int Up = Uv + (K.p[0].Y != K.p[0].Yb ? ncopy : 0);
+    while (rem >= K.p[p].njs * Up) {
+      rem -= K.p[p].njs * Up;
+      ++p;
+      Up = Uv + (K.p[p].Y != K.p[p].Yb ? ncopy : 0);
+    }
+    const int jb = rem / Up;
+    const int u = rem - jb * Up;
+    if (u >= Uv) {
+      expand_copy<E>(K, K.p[p], jb, u - Uv, t_valid, lane);
+      continue;
+    }
+    const int s = cld(K.exp_item_v + u);
+    const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
+    expand_valu<E>(K, K.p[p], jb, d0, d1, u - d1.z, vs, lane);
+    wave_sync();
   }
 }
 
@@ -823,8 +871,8 @@ __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N,
                                                                    const int32_t* rank, const float* alpha,
                                                                    int32_t* hist, SegOut out) {
   __shared__ int wsum[kSegScanThreads / 64 + 1];
-  __shared__ int carry[6];
-  if (threadIdx.x < 6) carry[threadIdx.x] = 0;
+  __shared__ int carry[8];
+  if (threadIdx.x < 8) carry[threadIdx.x] = 0;
   __syncthreads();
   const int W = N + 2;
   for (int base = 0; base < N; base += kSegScanThreads) {
@@ -838,31 +886,35 @@ __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N,
       }
     }
     const int r = (a < N && cnt > 0) ? rank[a] : 0;
-    const int vals[5] = {cnt, cnt > 0 ? 1 : 0, cnt * r, cnt > 0 ? shrink_items(cnt, r) : 0,
-                         cnt > 0 ? expand_items(cnt) : 0};
-    int pre[5], tots[5];
+    const bool has = cnt > 0;
+    // {tokens, segments, v entries, MBGMM shrink, MBGMV shrink, MBGMM expand, MBGMV expand}
+    const int vals[7] = {cnt, has ? 1 : 0, cnt * r, has ? shrink_items_mfma(cnt, r) : 0,
+                         has ? shrink_items_valu(cnt, r) : 0, has ? expand_items_mfma(cnt) : 0,
+                         has ? expand_items_valu(cnt) : 0};
+    int pre[7], tots[7];
 #pragma unroll
-    for (int f = 0; f < 5; ++f) {
+    for (int f = 0; f < 7; ++f) {
       pre[f] = block_exclusive_scan(vals[f], wsum, &tots[f]) + carry[f];
     }
-    if (a < N && cnt > 0) {
+    if (a < N && has) {
       const int si = pre[1];
+      const bool mf = is_mfma_segment(cnt);
       out.seg_adapter[si] = a;
       out.seg_indptr[si] = pre[0];
       out.v_indptr[si] = pre[2];
-      out.shr_ptr[si] = pre[3];
-      out.exp_ptr[si] = pre[4];
-      for (int i = 0; i < vals[3]; ++i) out.shr_item[pre[3] + i] = si;
-      for (int i = 0; i < vals[4]; ++i) out.exp_item[pre[4] + i] = si;
+      int32_t* shr = mf ? out.shr_item_m + pre[3] : out.shr_item_v + pre[4];
+      for (int i = 0; i < (mf ? vals[3] : vals[4]); ++i) shr[i] = si;
+      int32_t* exq = mf ? out.exp_item_m + pre[5] : out.exp_item_v + pre[6];
+      for (int i = 0; i < (mf ? vals[5] : vals[6]); ++i) exq[i] = si;
       int4* desc = reinterpret_cast<int4*>(out.seg_desc) + 2 * si;
       desc[0] = make_int4(a, r, pre[0], cnt);
-      desc[1] = make_int4(pre[2], pre[3], pre[4], __float_as_int(alpha[a]));
+      desc[1] = make_int4(pre[2], mf ? pre[3] : pre[4], mf ? pre[5] : pre[6], __float_as_int(alpha[a]));
       for (int c = 0; c < nchunk; ++c) hist[(int64_t)c * W + a] += pre[0];
     }
     __syncthreads();
     if (threadIdx.x == 0) {
 #pragma unroll
-      for (int f = 0; f < 5; ++f) carry[f] += tots[f];
+      for (int f = 0; f < 7; ++f) carry[f] += tots[f];
     }
     __syncthreads();
   }
@@ -871,8 +923,6 @@ __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N,
     const int S = carry[1], t_valid = carry[0];
     out.seg_indptr[S] = t_valid;
     out.v_indptr[S] = carry[2];
-    out.shr_ptr[S] = carry[3];
-    out.exp_ptr[S] = carry[4];
     int run = t_valid, n_invalid = 0;
     for (int c = 0; c < nchunk; ++c) {
       const int base_only = hist[(int64_t)c * W + N];
@@ -881,14 +931,15 @@ __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N,
       run += base_only + bad;
       n_invalid += bad;
     }
-    out.counts[LORA_COUNT_S] = S;
-    out.counts[LORA_COUNT_INVALID] = n_invalid;
-    out.counts[LORA_COUNT_T_VALID] = t_valid;
-    out.counts[LORA_COUNT_V_TOTAL] = carry[2];
-    out.counts[4] = carry[3];
-    out.counts[5] = carry[4];
-    out.counts[LORA_COUNT_FLAGS] = 0;
-    out.counts[7] = 0;
+    out.counts[kCountS] = S;
+    out.counts[kCountInvalid] = n_invalid;
+    out.counts[kCountTValid] = t_valid;
+    out.counts[kCountVTotal] = carry[2];
+    out.counts[kCountShrinkMfma] = carry[3];
+    out.counts[kCountShrinkValu] = carry[4];
+    out.counts[kCountExpandMfma] = carry[5];
+    out.counts[kCountExpandValu] = carry[6];
+    for (int i = kCountFlags; i < kNumCounts; ++i) out.counts[i] = 0;
   }
 }
 

@@ -39,36 +39,54 @@ constexpr int kSegChunk = 1024;           // tokens per segment-builder block
 #endif
 constexpr int kMfmaMinTokens = LORA_MFMA_MIN_TOKENS;  // segment length that switches to MFMA
 
-// Output columns per expand item: 4 per lane in bf16, 2 per lane in fp32.
-LORA_HD inline int expand_cols(bool bf16) { return bf16 ? 256 : 128; }
+// Output columns per MBGMV expand item: 2 per lane in bf16, 1 per lane in
+// fp32 (64 bytes of B per lane and rank group either way).
+LORA_HD inline int expand_cols(bool bf16) { return bf16 ? 128 : 64; }
 
 LORA_HD inline int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 LORA_HD inline int rank_groups(int r) { return (r + 15) >> 4; }
 
-// MBGMM shrink: accumulators are rank_groups x token_tiles 16x16 tiles; the
-// product is kept at 4 tiles (8 for rank > 64), so the operands of several K
-// steps fit in registers at once.
-LORA_HD inline int mfma_token_tiles(int groups) {
-  return groups <= 1 ? 4 : groups == 2 ? 2 : 1;
-}
-
 LORA_HD inline bool is_mfma_segment(int n) { return n >= kMfmaMinTokens; }
 
-// Shrink work items of one segment (per 512-column slice).
-LORA_HD inline int shrink_items(int n, int r) {
-  const int G = rank_groups(r);
-  if (is_mfma_segment(n)) return ceil_div_i(n, 16 * mfma_token_tiles(G));
-  return G * ceil_div_i(n, kValuTokens);
+// Work items of one segment, per 512-column shrink slice or per expand
+// column block.  MBGMV shrink: (rank group, <= kValuTokens tokens); MBGMM
+// shrink: (16-token tile, rank group); MBGMV expand: <= 8 tokens; MBGMM
+// expand: one 16-token tile.
+LORA_HD inline int shrink_items_valu(int n, int r) {
+  return is_mfma_segment(n) ? 0 : rank_groups(r) * ceil_div_i(n, kValuTokens);
 }
-
-// Expand work items of one segment (per expand column block).
-LORA_HD inline int expand_items(int n) {
-  return ceil_div_i(n, is_mfma_segment(n) ? kMfmaExpandTokens : kValuExpandTokens);
+LORA_HD inline int shrink_items_mfma(int n, int r) {
+  return is_mfma_segment(n) ? rank_groups(r) * ceil_div_i(n, 16) : 0;
 }
+LORA_HD inline int expand_items_valu(int n) { return is_mfma_segment(n) ? 0 : ceil_div_i(n, kValuExpandTokens); }
+LORA_HD inline int expand_items_mfma(int n) { return is_mfma_segment(n) ? ceil_div_i(n, kMfmaExpandTokens) : 0; }
 
-// Capacity of the per-batch item tables (entries), from T alone:
-// shrink items <= sum G*(n/2 + 1) <= 4T + 8S <= 12T, expand items <= T/8 + S <= 2T.
-LORA_HD inline long long shrink_item_capacity(int T) { return 12LL * (T > 0 ? T : 0) + 1; }
-LORA_HD inline long long expand_item_capacity(int T) { return 2LL * (T > 0 ? T : 0) + 1; }
+// counters (int32) written by the segment builder
+constexpr int kCountS = 0, kCountInvalid = 1, kCountTValid = 2, kCountVTotal = 3;
+constexpr int kCountShrinkMfma = 4, kCountShrinkValu = 5, kCountExpandMfma = 6, kCountExpandValu = 7;
+constexpr int kCountFlags = 8;
+constexpr int kNumCounts = 16;
+
+// The internal plan area: per-segment descriptors (2 x int4: {adapter,
+// rank, first token, tokens}, {v offset, first shrink item, first expand
+// item, alpha bits}) and the item -> segment tables of the two paths.
+// Offsets in int32 units, each a multiple of 64.
+struct PlanLayout {
+  long long seg_desc, shrink_mfma, shrink_valu, expand_mfma, expand_valu, total;
+};
+LORA_HD inline long long align64(long long x) { return (x + 63) / 64 * 64; }
+LORA_HD inline PlanLayout plan_layout(int T, int N) {
+  const long long t = T > 0 ? T : 0;
+  const long long smax = (T < N ? t : (N > 0 ? N : 0));
+  PlanLayout L;
+  L.seg_desc = 0;
+  L.shrink_mfma = align64(8 * (smax > 0 ? smax : 1));
+  // MBGMM shrink items <= 8*(T/16 + S) <= 9T; MBGMV <= 8*(T/2 + S) <= 12T
+  L.shrink_valu = L.shrink_mfma + align64(9 * t + 1);
+  L.expand_mfma = L.shrink_valu + align64(12 * t + 1);
+  L.expand_valu = L.expand_mfma + align64(2 * t + 1);
+  L.total = L.expand_valu + align64(2 * t + 1);
+  return L;
+}
 
 }  // namespace lora

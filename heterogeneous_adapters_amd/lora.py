@@ -20,7 +20,8 @@ from .build import LIB_PATH
 LORA_DTYPE_F32, LORA_DTYPE_BF16 = 0, 1
 LORA_MAX_RANK = 128
 LORA_KSLICE = 512
-COUNT_S, COUNT_INVALID, COUNT_T_VALID, COUNT_V_TOTAL, COUNT_FLAGS = 0, 1, 2, 3, 6
+COUNT_S, COUNT_INVALID, COUNT_T_VALID, COUNT_V_TOTAL, COUNT_FLAGS = 0, 1, 2, 3, 8
+N_COUNTS = 16
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -43,8 +44,7 @@ class lora_proj_t(ctypes.Structure):
 
 class lora_segments_t(ctypes.Structure):
     _fields_ = [("T", _i32), ("num_adapters", _i32), ("perm", _vp), ("seg_indptr", _vp),
-                ("seg_adapter", _vp), ("v_indptr", _vp), ("shr_ptr", _vp), ("exp_ptr", _vp),
-                ("shr_item", _vp), ("exp_item", _vp), ("seg_desc", _vp), ("counts", _vp)]
+                ("seg_adapter", _vp), ("v_indptr", _vp), ("plan", _vp), ("counts", _vp)]
 
 
 _lib = None
@@ -176,7 +176,7 @@ class Segments:
         return self.buf[off:off + 4 * n].view(torch.int32)
 
     def counts(self) -> torch.Tensor:
-        return self._view("counts", 8)
+        return self._view("counts", N_COUNTS)
 
     def arrays(self) -> dict:
         """Host copies of the segment arrays (synchronises)."""

@@ -136,11 +136,9 @@ typedef struct {
  *   seg_adapter[S_max]    adapter of segment s
  *   v_indptr[S_max+1]     offset of segment s in the ragged rank-r
  *                         intermediate v: v[v_indptr[s] + i*r + k]
- *   shr_ptr[S_max+1], exp_ptr[S_max+1]   work-plan prefix sums (internal)
- *   shr_item[10T+1], exp_item[2T+1]      work item -> segment tables (internal)
- *   seg_desc[8*S_max]     per-segment descriptors (internal)
- *   counts[8]             {S, n_invalid, T_valid, V_total, shrink items,
- *                         expand items, device error flags, reserved}
+ *   plan                  the work plan the kernels walk (internal layout)
+ *   counts[16]            {S, n_invalid, T_valid, V_total, then internal
+ *                         work-plan totals and device error flags}
  * A token is valid when 0 <= ids[t] < num_adapters and its adapter's rank is
  * in [1, 128].  ids[t] == -1 marks a base-model token ([MLSA] "What vLLM
  * actually gives you": base-model requests share the server); other invalid
@@ -152,11 +150,7 @@ typedef struct {
   int32_t* seg_indptr;
   int32_t* seg_adapter;
   int32_t* v_indptr;
-  int32_t* shr_ptr;
-  int32_t* exp_ptr;
-  int32_t* shr_item;
-  int32_t* exp_item;
-  int32_t* seg_desc;
+  int32_t* plan;
   int32_t* counts;
 } lora_segments_t;
 
@@ -164,7 +158,7 @@ typedef struct {
 #define LORA_COUNT_INVALID 1
 #define LORA_COUNT_T_VALID 2
 #define LORA_COUNT_V_TOTAL 3
-#define LORA_COUNT_FLAGS 6
+#define LORA_COUNT_FLAGS 8
 #define LORA_FLAG_PAGE_RANGE 1 /* a page id outside the pool was skipped (read as 0) */
 
 /* Bytes of the device buffer that holds segments for T tokens and
