@@ -13,9 +13,17 @@ gate/up, down: four calls per layer, the grouping a real forward pass allows).
 Prints ONE JSON line.  ``value`` is whole-step algorithmic HBM GB/s (bytes the
 method must move: activations once, each distinct adapter's unpadded A and B
 once) with every input already resident in HBM.  ``roofline`` covers the
-dominant launch unit (one call = shrink kernel + expand kernel over a group
-of projections), timed with HIP events on the stream the library launches
-on.  ``cpu_baseline`` is the CPU oracle on a bounded sample of the same step.
+dominant kernel (the expand kernel; both kernels are reported under
+``kernels``): after the timed steps the same groups are run through
+lora_shrink / lora_expand -- the two launches of lora_apply, same grid --
+with HIP events around each launch on the stream the library launches on.
+``traffic`` is the HBM bytes per launch from the committed rocprofv3 counter
+summary, or null when the kernel sources changed since it was taken.
+``cpu_baseline`` is the CPU oracle on a bounded sample of the same step.
+
+``--summarize-profile DIR`` (no GPU) turns rocprofv3 CSV output (kernel
+stats, or FETCH_SIZE / WRITE_SIZE counter runs that include
+``--calibration-copy``) into the text summaries kept under profiles/.
 ``prefill`` reports the MBGMM prefill workload (32 sequences of 128..2048
 tokens, 16 adapters) in TFLOP/s against the bf16 MFMA peak.
 """
@@ -31,6 +39,39 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+KERNEL_SOURCES = ("heterogeneous_adapters_amd/csrc/lora_kernels.hip", "heterogeneous_adapters_amd/csrc/lora_kernels.h",
+                  "heterogeneous_adapters_amd/csrc/lora_plan.h", "include/lora.h")
+TRAFFIC_SUMMARY = "profiles/expand_kernel_bf16.llama7b_decode_T1024.hbm_traffic.txt"
+CALIB_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_hash: str):
+    """HBM bytes per launch of the expand kernel from the committed counter
+    summary; None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_hash:
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -47,6 +88,11 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--pool-layout", choices=["scattered", "contiguous"], default="scattered",
                     help="physical page placement: seeded random permutation, or consecutive per adapter")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="end with a plain elementwise copy of 1 GiB (counter calibration)")
+    ap.add_argument("--summarize-profile", metavar="DIR", nargs="+",
+                    help="summarize rocprofv3 CSV output under the DIRs and exit (no GPU)")
+    ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
     return ap.parse_args()
 
 
@@ -63,8 +109,71 @@ def groups_for(n_layers, names, mode):
     return out
 
 
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profile(dirs, command):
+    """Text summary of rocprofv3 CSV output under the directories in dirs
+    (kernel stats, and/or FETCH_SIZE / WRITE_SIZE counter runs that end with
+    the calibration copy)."""
+    import glob
+    import numpy as np
+    lines = [f"command: {command}" if command else "command: (not recorded)",
+             f"kernel_source_hash: {kernel_source_hash()}"]
+    found = lambda pat: sorted(p for d in dirs for p in glob.glob(os.path.join(d, "**", pat), recursive=True))
+    for path in found("*kernel_stats.csv"):
+        lines.append("kernel stats (rocprofv3 --kernel-trace --stats), lora kernels and their share of all GPU time:")
+        rows = _read_csv(path)
+        tot = sum(float(r["TotalDurationNs"]) for r in rows)
+        lines.append(f"  {'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10} {'pct':>6}  name")
+        for r in rows:
+            if "lora::" not in r["Name"]:
+                continue
+            lines.append(f"  {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                         f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['TotalDurationNs']) / 1e6:10.3f} "
+                         f"{100 * float(r['TotalDurationNs']) / tot:6.2f}  {r['Name']}")
+    per = {}
+    for path in found("*counter_collection.csv"):
+        for r in _read_csv(path):
+            d = per.setdefault((r["Kernel_Name"], r["Counter_Name"]), {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if per:
+        calib = {}
+        for (name, ctr), disp in per.items():
+            if "neg_kernel" in name:
+                calib[ctr] = (CALIB_BYTES / 1024) / float(np.median(list(disp.values())))
+        lines.append(f"counters (rocprofv3 --pmc), KiB per dispatch as read; calibration: a plain elementwise "
+                     f"copy (torch.neg) of {CALIB_BYTES >> 20} MiB fp32 reads and writes exactly that many bytes")
+        for (name, ctr), disp in sorted(per.items()):
+            if "lora::" in name or "neg_kernel" in name:
+                vals = np.array(list(disp.values()))
+                lines.append(f"  {ctr:10s} dispatches {len(vals):5d} mean {vals.mean():12.1f} min {vals.min():12.1f} "
+                             f"max {vals.max():12.1f}  {name[:90]}")
+        for ctr, f in sorted(calib.items()):
+            lines.append(f"{ctr.lower()}_scale: {f:.4f}")
+        for kname, key in (("shrink_kernel<lora::Bf16>", "shrink"), ("expand_kernel<lora::Bf16>", "expand")):
+            tot, have = 0.0, 0
+            for (name, ctr), disp in per.items():
+                if kname in name and ctr in calib:
+                    b = float(np.mean(list(disp.values()))) * 1024 * calib[ctr]
+                    lines.append(f"{key}_{ctr.lower()}_bytes_per_launch: {b:.0f}")
+                    tot += b
+                    have += 1
+            if have == 2:
+                lines.append(f"{key}_hbm_bytes_per_launch: {tot:.0f}")
+                if key == "expand":
+                    lines.append(f"hbm_bytes_per_launch: {tot:.0f}")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.profile_command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(tokens shard across GPUs with no exchange; see the sharding design)", file=sys.stderr)
@@ -150,6 +259,32 @@ def main():
     if seg["flags"] != 0:
         raise RuntimeError(f"device flags {seg['flags']}")
 
+    # per-kernel leg: the same groups through lora_shrink / lora_expand (the
+    # two launches lora_apply makes, same grid), HIP events around each
+    # launch on the library's stream; Y must come out bit-identical
+    y_apply = [y.clone() for y in Y[:7]]
+    v_stride = T * lora.LORA_MAX_RANK
+    max_g = max(len(g) for g in groups)
+    vbuf = [torch.empty(lora.lora_v_slices(max(t.d_in for t in dw.tables)) * v_stride, dtype=torch.float32,
+                        device=dev) for _ in range(max_g)]
+    vptrs = [(ctypes.c_void_p * len(g))(*[vbuf[j].data_ptr() for j in range(len(g))]) for g in groups]
+    kev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in groups] for _ in range(args.steps)]
+    for k in range(args.steps):
+        for gi, arr in enumerate(arrays):
+            ev = kev[k][gi]
+            ev[0].record(stream)
+            st = L.lora_shrink(arr, len(groups[gi]), ad_c, seg_c, pool_c, vptrs[gi], v_stride, sptr)
+            ev[1].record(stream)
+            st = st or L.lora_expand(arr, len(groups[gi]), ad_c, seg_c, pool_c, vptrs[gi], 0, v_stride, sptr)
+            ev[2].record(stream)
+            if st != 0:
+                raise lora.LoraError("lora_shrink/lora_expand", st)
+    torch.cuda.synchronize()
+    split_same = all(torch.equal(a, b) for a, b in zip(y_apply, Y[:7]))
+    shr_ms = np.array([[ev[0].elapsed_time(ev[1]) for ev in row] for row in kev]).mean(axis=0)  # per group
+    exp_ms = np.array([[ev[1].elapsed_time(ev[2]) for ev in row] for row in kev]).mean(axis=0)
+    del vbuf
+
     # the same step captured once in a HIP graph and replayed (removes host
     # launch cost; results checked bit for bit against the eager step)
     graph = None
@@ -190,12 +325,20 @@ def main():
 
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     mean_call_ms = call_ms.mean(axis=0)
-    achieved = float(np.sum(call_bytes) / (mean_call_ms.sum() * 1e-3) / 1e9)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "lora_apply call = shrink_kernel<Bf16> + expand_kernel<Bf16>",
-                "launches_per_step": len(groups), "mean_call_us": round(float(mean_call_ms.mean()) * 1e3, 2),
-                "algorithmic_bytes_per_call": int(np.mean(call_bytes))}
+    kernels = {}
+    for kname, ms_g, part in (("shrink_kernel<Bf16>", shr_ms, 0), ("expand_kernel<Bf16>", exp_ms, 1)):
+        kb = [sum(traffic.split_bytes(dw.ids, dw.ranks, dw.tables[i].d_in, dw.tables[i].d_out, e)[part]
+                  for i in g) for g in groups]
+        gb = float(np.sum(kb) / (ms_g.sum() * 1e-3) / 1e9)
+        kernels[kname] = {"launches_per_step": len(groups), "mean_launch_us": round(float(ms_g.mean()) * 1e3, 2),
+                          "algorithmic_bytes_per_launch": int(np.mean(kb)), "gbs": round(gb, 1),
+                          "frac_hbm_peak": round(gb / HBM_PEAK_GBS, 4)}
+    dom = kernels["expand_kernel<Bf16>"]
+    roofline = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dom["frac_hbm_peak"], "traffic": load_traffic(kernel_source_hash()),
+                "kernel": "expand_kernel<Bf16>", "mean_launch_us": dom["mean_launch_us"],
+                "algorithmic_bytes_per_launch": dom["algorithmic_bytes_per_launch"],
+                "launches_per_step": len(groups)}
 
     # ---------------------------------------------------------- CPU oracle
     cpu = None
@@ -277,12 +420,23 @@ def main():
         "tflops": round(step_flops / (ms_step * 1e-3) / 1e12, 2),
         "ms_per_step_events": round(ms_step_ev, 4),
         "roofline": roofline,
+        "kernels": dict(kernels, **{"lora_apply_call": {
+            "mean_call_us": round(float(mean_call_ms.mean()) * 1e3, 2),
+            "algorithmic_bytes_per_call": int(np.mean(call_bytes)),
+            "gbs": round(float(np.sum(call_bytes) / (mean_call_ms.sum() * 1e-3) / 1e9), 1)},
+            "split_matches_apply": bool(split_same)}),
         "cpu_baseline": cpu,
         "prefill": prefill,
         "graph_replay": graph,
         "setup_s": round(gen_s, 1),
     }
     print(json.dumps(out), flush=True)
+    if args.calibration_copy:
+        a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -272,35 +272,46 @@ lora_status_t lora_build_segments(const int32_t* ids, int32_t T, const lora_adap
   return build_into(ids, T, adapters, &s, static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream));
 }
 
-lora_status_t lora_shrink(const lora_proj_t* proj, const lora_adapters_t* adapters, const lora_segments_t* segs,
-                          const lora_pool_t* pool, float* v, int64_t v_stride, void* stream) {
-  if (lora_status_t st = check_proj(proj)) return st;
+// Shared body of lora_shrink / lora_expand: groups of up to kProjsPerLaunch
+// projections per launch, the launch geometry of lora_apply.
+static lora_status_t run_split(const lora_proj_t* projs, int32_t n_projs, const lora_adapters_t* adapters,
+                               const lora_segments_t* segs, const lora_pool_t* pool, float* const* v,
+                               int32_t v_slices, int64_t v_stride, bool shrink, void* stream) {
+  if (n_projs < 0 || (n_projs > 0 && (!projs || !v))) return LORA_ERR_INVALID_ARG;
   if (lora_status_t st = check_adapters(adapters)) return st;
   if (lora_status_t st = check_segs(segs)) return st;
   if (lora_status_t st = check_pool(pool)) return st;
-  if (!v || v_stride < (int64_t)segs->T * LORA_MAX_RANK) return LORA_ERR_INVALID_ARG;
-  KArgs K;
-  memset(&K, 0, sizeof K);
-  fill_common(K, segs, pool, v_stride);
-  K.p[0] = make_kproj(*proj, v, lora_v_slices(proj->d_in), pool->dtype);
-  K.np = 1;
-  return run(K, pool->dtype, true, false, static_cast<hipStream_t>(stream));
+  if (v_slices < 0 || v_stride < (int64_t)segs->T * LORA_MAX_RANK) return LORA_ERR_INVALID_ARG;
+  for (int i = 0; i < n_projs; ++i) {
+    if (lora_status_t st = check_proj(&projs[i])) return st;
+    if (!v[i]) return LORA_ERR_INVALID_ARG;
+  }
+  for (int base = 0; base < n_projs; base += kProjsPerLaunch) {
+    KArgs K;
+    memset(&K, 0, sizeof K);
+    fill_common(K, segs, pool, v_stride);
+    K.np = std::min(kProjsPerLaunch, n_projs - base);
+    for (int i = 0; i < K.np; ++i) {
+      const lora_proj_t& p = projs[base + i];
+      const int nv = (shrink || v_slices == 0) ? lora_v_slices(p.d_in) : v_slices;
+      K.p[i] = make_kproj(p, v[base + i], nv, pool->dtype);
+    }
+    if (lora_status_t e = run(K, pool->dtype, shrink, !shrink, static_cast<hipStream_t>(stream))) return e;
+  }
+  return LORA_OK;
 }
 
-lora_status_t lora_expand(const lora_proj_t* proj, const lora_adapters_t* adapters, const lora_segments_t* segs,
-                          const lora_pool_t* pool, const float* v, int32_t v_slices, int64_t v_stride,
+lora_status_t lora_shrink(const lora_proj_t* projs, int32_t n_projs, const lora_adapters_t* adapters,
+                          const lora_segments_t* segs, const lora_pool_t* pool, float* const* v, int64_t v_stride,
                           void* stream) {
-  if (lora_status_t st = check_proj(proj)) return st;
-  if (lora_status_t st = check_adapters(adapters)) return st;
-  if (lora_status_t st = check_segs(segs)) return st;
-  if (lora_status_t st = check_pool(pool)) return st;
-  if (!v || v_slices < 1 || v_stride < (int64_t)segs->T * LORA_MAX_RANK) return LORA_ERR_INVALID_ARG;
-  KArgs K;
-  memset(&K, 0, sizeof K);
-  fill_common(K, segs, pool, v_stride);
-  K.p[0] = make_kproj(*proj, const_cast<float*>(v), v_slices, pool->dtype);
-  K.np = 1;
-  return run(K, pool->dtype, false, true, static_cast<hipStream_t>(stream));
+  return run_split(projs, n_projs, adapters, segs, pool, v, 0, v_stride, true, stream);
+}
+
+lora_status_t lora_expand(const lora_proj_t* projs, int32_t n_projs, const lora_adapters_t* adapters,
+                          const lora_segments_t* segs, const lora_pool_t* pool, const float* const* v,
+                          int32_t v_slices, int64_t v_stride, void* stream) {
+  return run_split(projs, n_projs, adapters, segs, pool, const_cast<float* const*>(v), v_slices, v_stride, false,
+                   stream);
 }
 
 lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_t T, const lora_proj_t* projs,

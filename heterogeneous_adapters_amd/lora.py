@@ -78,10 +78,10 @@ def lib():
         L.lora_workspace_size.restype = ctypes.c_size_t
         L.lora_build_segments.argtypes = [_vp, _i32, P(lora_adapters_t), P(lora_segments_t), _vp,
                                           ctypes.c_size_t, _vp]
-        L.lora_shrink.argtypes = [P(lora_proj_t), P(lora_adapters_t), P(lora_segments_t), P(lora_pool_t),
-                                  _vp, _i64, _vp]
-        L.lora_expand.argtypes = [P(lora_proj_t), P(lora_adapters_t), P(lora_segments_t), P(lora_pool_t),
-                                  _vp, _i32, _i64, _vp]
+        L.lora_shrink.argtypes = [P(lora_proj_t), _i32, P(lora_adapters_t), P(lora_segments_t),
+                                  P(lora_pool_t), P(_vp), _i64, _vp]
+        L.lora_expand.argtypes = [P(lora_proj_t), _i32, P(lora_adapters_t), P(lora_segments_t),
+                                  P(lora_pool_t), P(_vp), _i32, _i64, _vp]
         L.lora_apply.argtypes = [_vp, P(lora_segments_t), _i32, P(lora_proj_t), _i32, P(lora_adapters_t),
                                  P(lora_pool_t), _vp, ctypes.c_size_t, _vp]
         L.lora_validate_tables.argtypes = [_i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
@@ -216,20 +216,35 @@ def lora_build_segments(ids: torch.Tensor, adapters: Adapters, segs: Segments, w
         _stream(stream)))
 
 
-def lora_shrink(proj: Proj, adapters: Adapters, segs: Segments, pool: Pool, v: torch.Tensor,
-                v_stride: int, stream=None) -> None:
-    assert v.dtype == torch.float32
-    _check("lora_shrink", lib().lora_shrink(ctypes.byref(proj.c), ctypes.byref(adapters.c),
-                                            ctypes.byref(segs.c), ctypes.byref(pool.c), _ptr(v),
-                                            v_stride, _stream(stream)))
+def _proj_group(projs, v):
+    if isinstance(projs, Proj):
+        projs = [projs]
+    if isinstance(v, torch.Tensor):
+        v = [v]
+    projs, v = list(projs), list(v)
+    if len(projs) != len(v):
+        raise ValueError("one v buffer per projection")
+    for t in v:
+        if t.dtype != torch.float32:
+            raise TypeError("v must be float32")
+    arr = (lora_proj_t * max(len(projs), 1))(*[p.c for p in projs])
+    vp = (_vp * max(len(v), 1))(*[_ptr(t) for t in v])
+    return arr, len(projs), vp
 
 
-def lora_expand(proj: Proj, adapters: Adapters, segs: Segments, pool: Pool, v: torch.Tensor,
-                v_slices: int, v_stride: int, stream=None) -> None:
-    assert v.dtype == torch.float32
-    _check("lora_expand", lib().lora_expand(ctypes.byref(proj.c), ctypes.byref(adapters.c),
-                                            ctypes.byref(segs.c), ctypes.byref(pool.c), _ptr(v),
-                                            v_slices, v_stride, _stream(stream)))
+def lora_shrink(projs, adapters: Adapters, segs: Segments, pool: Pool, v, v_stride: int, stream=None) -> None:
+    """projs: a Proj or a sequence of them; v: one fp32 tensor per projection."""
+    arr, n, vp = _proj_group(projs, v)
+    _check("lora_shrink", lib().lora_shrink(arr, n, ctypes.byref(adapters.c), ctypes.byref(segs.c),
+                                            ctypes.byref(pool.c), vp, v_stride, _stream(stream)))
+
+
+def lora_expand(projs, adapters: Adapters, segs: Segments, pool: Pool, v, v_slices: int, v_stride: int,
+                stream=None) -> None:
+    """v_slices: 0 = each projection's lora_v_slices(d_in), k >= 1 = k slices for all."""
+    arr, n, vp = _proj_group(projs, v)
+    _check("lora_expand", lib().lora_expand(arr, n, ctypes.byref(adapters.c), ctypes.byref(segs.c),
+                                            ctypes.byref(pool.c), vp, v_slices, v_stride, _stream(stream)))
 
 
 def lora_apply(ids: Optional[torch.Tensor], segs: Optional[Segments], T: int, projs: Sequence[Proj],

@@ -186,21 +186,26 @@ lora_status_t lora_build_segments(const int32_t* ids, int32_t T, const lora_adap
                                   const lora_segments_t* segs, void* ws, size_t ws_bytes,
                                   void* stream);
 
-/* Shrink ([MLSP] SGMV: v_i = x_i A_i, the rank-r intermediate) for one
- * projection.  v: device fp32 [lora_v_slices(d_in)][v_stride]; slice q holds
- * the partial sum over inputs q*512 .. min((q+1)*512, d_in)-1 in the ragged
- * layout of v_indptr; v = sum of the slices in ascending q.  v_stride >=
- * T*128.  Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED, HIP. */
-lora_status_t lora_shrink(const lora_proj_t* proj, const lora_adapters_t* adapters,
-                          const lora_segments_t* segs, const lora_pool_t* pool, float* v,
+/* Shrink ([MLSP] SGMV: v_i = x_i A_i, the rank-r intermediate) for n_projs
+ * projections of one batch (projs: host array), one kernel launch per group
+ * of up to 16 projections -- the first launch of lora_apply.  v: host array
+ * of n_projs device pointers; v[i] is fp32 [lora_v_slices(d_in_i)][v_stride]
+ * and its slice q holds the partial sum over inputs q*512 ..
+ * min((q+1)*512, d_in)-1 in the ragged layout of v_indptr; v = the sum of
+ * the slices in ascending q.  v_stride >= T*128.
+ * Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED, HIP. */
+lora_status_t lora_shrink(const lora_proj_t* projs, int32_t n_projs, const lora_adapters_t* adapters,
+                          const lora_segments_t* segs, const lora_pool_t* pool, float* const* v,
                           int64_t v_stride, void* stream);
 
 /* Expand ([MLSP] SGMV: y_i = v_i B_i scaled by alpha_i/r_i and added to the
- * base output) for one projection.  v as written by lora_shrink (v_slices
- * slices, summed in ascending order) or any v with v_slices = 1.  Rows of
- * tokens without an adapter receive Y_base.  Errors as lora_shrink. */
-lora_status_t lora_expand(const lora_proj_t* proj, const lora_adapters_t* adapters,
-                          const lora_segments_t* segs, const lora_pool_t* pool, const float* v,
+ * base output) for n_projs projections -- the second launch of lora_apply.
+ * v as written by lora_shrink.  v_slices: 0 -> lora_v_slices(d_in_i) slices
+ * for projection i (what lora_shrink wrote); k >= 1 -> k slices for every
+ * projection (k = 1: v given whole).  Rows of tokens without an adapter
+ * receive Y_base.  Errors as lora_shrink. */
+lora_status_t lora_expand(const lora_proj_t* projs, int32_t n_projs, const lora_adapters_t* adapters,
+                          const lora_segments_t* segs, const lora_pool_t* pool, const float* const* v,
                           int32_t v_slices, int64_t v_stride, void* stream);
 
 /* The fused adapter branch for n_projs projections of one batch: shrink then

@@ -96,8 +96,9 @@ def test_shrink_expand_apply_reject_bad_arguments(case, code):
     L = lora.lib()
     r = ctypes.byref
     v = ctypes.c_void_p(b.p())
-    assert L.lora_shrink(r(proj), r(ad), r(seg), r(pool), v, 8 * 128, None) == code
-    assert L.lora_expand(r(proj), r(ad), r(seg), r(pool), v, 1, 8 * 128, None) == code
+    vs = (ctypes.c_void_p * 1)(b.p())
+    assert L.lora_shrink(r(proj), 1, r(ad), r(seg), r(pool), vs, 8 * 128, None) == code
+    assert L.lora_expand(r(proj), 1, r(ad), r(seg), r(pool), vs, 1, 8 * 128, None) == code
     arr = (lora.lora_proj_t * 1)(proj)
     assert L.lora_apply(None, r(seg), 8, arr, 1, r(ad), r(pool), v, 1 << 30, None) == code
 
@@ -108,10 +109,14 @@ def test_other_rejections():
     L = lora.lib()
     r = ctypes.byref
     v = ctypes.c_void_p(b.p())
+    vs = (ctypes.c_void_p * 1)(b.p())
     # v_stride below T * 128
-    assert L.lora_shrink(r(proj), r(ad), r(seg), r(pool), v, 8 * 127, None) == -1
-    # v_slices < 1
-    assert L.lora_expand(r(proj), r(ad), r(seg), r(pool), v, 0, 8 * 128, None) == -1
+    assert L.lora_shrink(r(proj), 1, r(ad), r(seg), r(pool), vs, 8 * 127, None) == -1
+    # v_slices < 0; no v array; a null v pointer; negative projection count
+    assert L.lora_expand(r(proj), 1, r(ad), r(seg), r(pool), vs, -1, 8 * 128, None) == -1
+    assert L.lora_expand(r(proj), 1, r(ad), r(seg), r(pool), None, 0, 8 * 128, None) == -1
+    assert L.lora_shrink(r(proj), 1, r(ad), r(seg), r(pool), (ctypes.c_void_p * 1)(None), 8 * 128, None) == -1
+    assert L.lora_shrink(r(proj), -1, r(ad), r(seg), r(pool), vs, 8 * 128, None) == -1
     arr = (lora.lora_proj_t * 1)(proj)
     # neither ids nor segments; T mismatch; workspace too small
     assert L.lora_apply(None, None, 8, arr, 1, r(ad), r(pool), v, 1 << 30, None) == -1
@@ -127,7 +132,7 @@ def test_other_rejections():
     assert L.lora_build_segments(v, 8, r(ad), r(seg), v, 4, None) == -4
     # Y aliasing Y_base with another leading dimension
     p2 = lora.lora_proj_t(b.p(), 64, b.p(512), 64, b.p(512), 72, 64, 64, b.p(), b.p(), b.p(), b.p())
-    assert L.lora_shrink(r(p2), r(ad), r(seg), r(pool), v, 8 * 128, None) == -1
+    assert L.lora_shrink(r(p2), 1, r(ad), r(seg), r(pool), vs, 8 * 128, None) == -1
     # segment buffer: misaligned / too small
     s2 = lora.lora_segments_t()
     assert L.lora_segments_init(ctypes.c_void_p(b.p(4)), 1 << 14, 8, 4, r(s2)) == -7

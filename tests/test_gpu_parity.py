@@ -38,6 +38,14 @@ def gpu_apply(w, in_place=False, pool=None, ids=None, via="apply"):
     ws = lora.workspace(w.T, w.N, w.n_projs, max_din)
     if via == "apply":
         lora.lora_apply(b.ids, segs, w.T, projs, b.adapters, b.pool, ws)
+    elif via == "split_group":
+        # the whole group through lora_shrink then lora_expand: the launches of lora_apply
+        lora.lora_build_segments(b.ids, b.adapters, segs, ws)
+        stride = max(w.T, 1) * lora.LORA_MAX_RANK
+        vs = [torch.empty(lora.lora_v_slices(t.d_in) * stride, dtype=torch.float32, device="cuda")
+              for t in w.tables]
+        lora.lora_shrink(projs, b.adapters, segs, b.pool, vs, stride)
+        lora.lora_expand(projs, b.adapters, segs, b.pool, vs, 0, stride)
     else:
         lora.lora_build_segments(b.ids, b.adapters, segs, ws)
         for p, pr in enumerate(projs):
@@ -160,6 +168,9 @@ def test_shrink_expand_entry_points(dtype):
     Y1, seg = gpu_apply(w, via="apply")
     Y2, _ = gpu_apply(w, via="split")
     assert np.array_equal(Y1[0], Y2[0])
+    Y3, _ = gpu_apply(w, via="split_group")
+    for p in range(w.n_projs):
+        assert np.array_equal(Y1[p], Y3[p])
     # shrink alone: sum of the partial slices against the oracle's v
     b = batch.to_device(w)
     segs = lora.Segments(w.T, w.N)
@@ -276,6 +287,10 @@ def test_many_projections_in_one_call():
     Ys, _ = gpu_apply(w)
     for p in range(w.n_projs):
         assert rowwise_rel(W.as_f64(Ys[p], w.dtype), W.as_f64(oracle_Y(w, p), w.dtype)) < TOL[w.dtype]
+    # the same groups through lora_shrink / lora_expand: bit-identical
+    Yg, _ = gpu_apply(w, via="split_group")
+    for p in range(w.n_projs):
+        assert np.array_equal(Ys[p], Yg[p])
 
 
 def test_excluded_token_at_last_chunk_position():
