@@ -189,7 +189,7 @@ lora_status_t run(const KArgs& K, int dtype, bool do_shrink, bool do_expand, hip
   int64_t bs = 0, be = 0;
   for (int p = 0; p < K.np; ++p) {
     bs += (int64_t)K.p[p].nq * (21LL * K.T + 2);
-    be += (int64_t)K.p[p].njs * (3LL * K.T + 2);
+    be += (int64_t)K.p[p].njs * (6LL * K.T + 2);
   }
   // items are per wave: kWaves items per work-group
   if (do_shrink && launch_shrink(K, dtype, grid_for(d->cus * d->occ_shrink[di], ceil_div64(bs, kWaves)), stream) !=

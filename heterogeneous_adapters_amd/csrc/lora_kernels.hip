@@ -130,16 +130,6 @@ __device__ __forceinline__ uint4 pack_operand(const float* v, int n, F32) {
   return make_uint4(__float_as_uint(e[0]), __float_as_uint(e[1]), __float_as_uint(e[2]), __float_as_uint(e[3]));
 }
 
-// Load n (< kEpv) leading elements of a vector, zero the rest; never touches
-// the elements beyond n (page padding is not read).
-template <class E>
-__device__ __forceinline__ uint4 load_partial(const typename E::T* p, int n) {
-  typename E::T e[E::kEpv];
-#pragma unroll
-  for (int i = 0; i < E::kEpv; ++i) e[i] = i < n ? p[i] : (typename E::T)0;
-  return __builtin_bit_cast(uint4, e);
-}
-
 __device__ __forceinline__ float to_f(uint16_t h) { return bf_to_f(h); }
 __device__ __forceinline__ float to_f(float f) { return f; }
 __device__ __forceinline__ void from_f(uint16_t* p, float f) { *p = f_to_bf(f); }
@@ -153,6 +143,36 @@ __device__ __forceinline__ const typename E::T* page_ptr(const KArgs& K, int pag
     return nullptr;
   }
   return reinterpret_cast<const typename E::T*>(K.pool) + ((int64_t)page << (K.pw_log2 + 4));
+}
+
+// Page base with the range check folded in: an id outside the pool sets the
+// device flag, the load is redirected to page 0 and `ok` zeroes its value.
+template <class E>
+__device__ __forceinline__ const typename E::T* page_base(const KArgs& K, int page, bool& ok) {
+  ok = (unsigned)page < (unsigned)K.num_pages;
+  if (!ok) atomicOr(&K.counts[kCountFlags], LORA_FLAG_PAGE_RANGE);
+  return reinterpret_cast<const typename E::T*>(K.pool) + ((int64_t)(ok ? page : 0) << (K.pw_log2 + 4));
+}
+
+// Keep the first kn (1..kEpv) elements of a vector, zero the rest.
+__device__ __forceinline__ uint4 keep_first(uint4 w, int kn, Bf16) {
+  auto m = [kn](int d) { return kn > 2 * d + 1 ? 0xffffffffu : (kn > 2 * d ? 0x0000ffffu : 0u); };
+  return make_uint4(w.x & m(0), w.y & m(1), w.z & m(2), w.w & m(3));
+}
+__device__ __forceinline__ uint4 keep_first(uint4 w, int kn, F32) {
+  return make_uint4(kn > 0 ? w.x : 0u, kn > 1 ? w.y : 0u, kn > 2 ? w.z : 0u, kn > 3 ? w.w : 0u);
+}
+
+// One 16-byte vector of a B column (kEpv consecutive ranks of one output
+// column; the 16 rank slots of a column are one 32- or 64-byte row of its
+// page).  kn = ranks of the vector below r: none, or a page outside the pool
+// -> zeros without a load.  A vector with some ranks past r is read whole
+// (the column row is fetched whole anyway) and masked where it is used, so
+// that no instruction waits on the load here.
+__device__ __forceinline__ uint4 load_b(const void* p, int kn, bool ok) {
+  uint4 w = zero4();
+  if (kn > 0 && ok) w = ldg16(p);
+  return w;
 }
 
 // Largest s with ptr[s] <= u (ptr strictly increasing, ptr[0] = 0).
@@ -239,6 +259,18 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// The kernels take one by-value KArgs argument, which sits at offset 0 of the
+// kernel-argument segment.  They read it through the segment pointer, so a
+// descriptor picked by a run-time projection index is a scalar load from
+// that segment, never a private copy of the whole struct.
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ const KArgs& kernel_args() {
+  return *reinterpret_cast<const KArgs*>(__builtin_amdgcn_kernarg_segment_ptr());
+}
+#else
+__device__ const KArgs& kernel_args();
+#endif
 
 // ================================================================ shrink
 // MBGMV item (one wave): (segment, rank group g, <= 2 tokens, 512-column
@@ -371,7 +403,8 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
 }
 
 template <class E>
-__global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArgs K) {
+__global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArgs) {
+  const KArgs& K = kernel_args();
   const int S = cld(K.counts + kCountS);
   if (S <= 0) return;
   const int Um = cld(K.counts + kCountShrinkMfma), Uv = cld(K.counts + kCountShrinkValu);
@@ -444,13 +477,9 @@ __device__ __forceinline__ void stage_v_rows(const KArgs& K, const KProj& P, int
   const int rs = rank_groups(r) * 16;
   const int ne = nt * r;
   const float* src = P.v + voff + (int64_t)tb * r;
-  const int mm = ceil_div_i(ne, NT);
-  if (mm <= 1) stage_v_pass<NT, 1, 16>(K, P, src, 0, ne, r, rs, vs, tid);
-  else if (mm <= 2) stage_v_pass<NT, 2, 8>(K, P, src, 0, ne, r, rs, vs, tid);
-  else if (mm <= 4) stage_v_pass<NT, 4, 4>(K, P, src, 0, ne, r, rs, vs, tid);
-  else if (mm <= 8) stage_v_pass<NT, 8, 2>(K, P, src, 0, ne, r, rs, vs, tid);
+  if (ne <= 2 * NT) stage_v_pass<NT, 2, 8>(K, P, src, 0, ne, r, rs, vs, tid);
   else
-    for (int e0 = 0; e0 < ne; e0 += NT * 16) stage_v_pass<NT, 16, 1>(K, P, src, e0, ne, r, rs, vs, tid);
+    for (int e0 = 0; e0 < ne; e0 += NT * 8) stage_v_pass<NT, 8, 2>(K, P, src, e0, ne, r, rs, vs, tid);
   for (int idx = tid; idx < nt * (rs - r); idx += NT) {  // zero the rank padding of every row
     const int t = idx / (rs - r);
     vs[t * rs + r + (idx - t * (rs - r))] = 0.0f;
@@ -462,6 +491,86 @@ __device__ __forceinline__ void stage_v(const KArgs& K, const KProj& P, int voff
                                         float* vs, int lane) {
   stage_v_rows<64>(K, P, voff, r, tb, nt, vs, lane);
   wave_sync();
+}
+
+// v of all n tokens of a segment as bf16 (hi, lo) pairs in the wave's LDS
+// rows, for products with packed bf16 B on the dot2 instructions: every fp32
+// value x (the ascending-slice sum) becomes hi = bf16(x), lo = bf16(x - hi),
+// so x = hi + lo to a relative 2^-17 and each product with a bf16 weight is
+// exact in fp32.  Layout per token and rank group g (16 dwords): for each
+// half h of the group's 16 ranks, 4 dwords of hi pairs (ranks 8h+2j,
+// 8h+2j+1) then 4 dwords of lo pairs.  Ranks >= r are zero.
+template <int M>
+__device__ __forceinline__ void stage_v_split_pass(const KArgs& K, const KProj& P, const float* src, int p0,
+                                                   int np, int r, int G, uint32_t* vs, int lane) {
+  const int hp = G * 8;  // rank pairs per token
+  float acc[M][2];
+  int e[M], kk[M], dst[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int p = p0 + lane + 64 * m;
+    const int t = p / hp, kp = p - t * hp;  // pair kp = ranks 2kp, 2kp+1
+    kk[m] = p < np ? 2 * kp : LORA_MAX_RANK;  // past the end: nothing loaded or stored
+    e[m] = t * r + 2 * kp;
+    dst[m] = t * (G * 16) + (kp >> 3) * 16 + ((kp >> 2) & 1) * 8 + (kp & 3);
+    acc[m][0] = acc[m][1] = 0.0f;
+  }
+  constexpr int SF = M >= 8 ? 1 : 8 / M;
+  for (int q = 0; q < P.nv; q += SF) {
+    float x[SF][M][2];
+#pragma unroll
+    for (int j = 0; j < SF; ++j)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float* a = src + (int64_t)(q + j) * K.v_stride + e[m];
+        const bool ok = q + j < P.nv;
+        x[j][m][0] = ok && kk[m] < r ? a[0] : 0.0f;
+        x[j][m][1] = ok && kk[m] + 1 < r ? a[1] : 0.0f;
+      }
+#pragma unroll
+    for (int j = 0; j < SF; ++j)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        acc[m][0] += x[j][m][0];
+        acc[m][1] += x[j][m][1];
+      }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    if (kk[m] < LORA_MAX_RANK) {
+      const uint32_t hi = pack_bf2(acc[m][0], acc[m][1]);
+      const uint32_t lo = pack_bf2(acc[m][0] - bf_lo(hi), acc[m][1] - bf_hi(hi));
+      vs[dst[m]] = hi;
+      vs[dst[m] + 4] = lo;
+    }
+  }
+}
+
+__device__ __forceinline__ void stage_v_split(const KArgs& K, const KProj& P, int voff, int r, int n, uint32_t* vs,
+                                              int lane) {
+  const int G = rank_groups(r);
+  const int np = n * G * 8;
+  const float* src = P.v + voff;
+  const int mm = ceil_div_i(np, 64);
+  if (mm <= 1) stage_v_split_pass<1>(K, P, src, 0, np, r, G, vs, lane);
+  else if (mm <= 2) stage_v_split_pass<2>(K, P, src, 0, np, r, G, vs, lane);
+  else
+    for (int p0 = 0; p0 < np; p0 += 64 * 4) stage_v_split_pass<4>(K, P, src, p0, np, r, G, vs, lane);
+  wave_sync();
+}
+
+// dot products of one 16-byte B vector (8 ranks of one column, packed bf16
+// pairs) with the split v of one token: 4 pairs x (hi, lo).
+__device__ __forceinline__ float dot_split(uint4 w, uint4 vh, uint4 vl, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, vh.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, vh.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, vh.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, vh.w), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, vl.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, vl.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, vl.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, vl.w), acc, false);
+  return acc;
 }
 
 // B element k (rank within the group) of lane-local column c, from the 4
@@ -479,104 +588,234 @@ __device__ __forceinline__ float b_elem(const uint4 (&b)[4], int c, int k, F32) 
 // rows are adjacent in the B page: 64 contiguous bytes per lane and rank
 // group, 4 KiB per wave.  The B loads of up to four rank groups and the
 // Y_base loads are issued before v is staged.
+// Metadata of one MBGMV expand item, loaded one item ahead (scalar loads
+// issued while the previous item's weight loads are in flight): the
+// segment descriptor, the adapter's B-table offset and the page ids of its
+// first kValuGroupBatch rank groups (when the item's columns lie in one page).
+constexpr int kValuGroupBatch = 4;
+struct ValuItem {
+  int p, jb, local;  // projection, column block, item index inside the segment
+  int copy;          // != 0: a copy of rows without an adapter (chunk = local)
+  int4 d0, d1;       // segment descriptor
+  int pg[kValuGroupBatch];
+};
+
 template <class E>
-__device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, int jb, int4 d0, int4 d1, int local,
-                                            float* vs, int lane) {
+__device__ __forceinline__ ValuItem fetch_valu_item(const KArgs& K, int i, int Uv, int ncopy) {
+  ValuItem it;
+  int rem = i, p = 0;
+  int Up = Uv + (K.p[0].Y != K.p[0].Yb ? ncopy : 0);
+  while (rem >= K.p[p].njs * Up) {
+    rem -= K.p[p].njs * Up;
+    ++p;
+    Up = Uv + (K.p[p].Y != K.p[p].Yb ? ncopy : 0);
+  }
+  const KProj& P = K.p[p];
+  it.p = p;
+  it.jb = rem / Up;
+  const int u = rem - it.jb * Up;
+  it.copy = u >= Uv;
+  if (it.copy) {
+    it.local = u - Uv;
+    return it;
+  }
+  const int s = cld(K.exp_item_v + u);
+  it.d0 = cld4(K.seg_desc + 2 * s);
+  it.d1 = cld4(K.seg_desc + 2 * s + 1);
+  it.local = u - it.d1.z;
+  constexpr int CB = kValuSubBlocks * 64 * (4 / (int)sizeof(typename E::T));
+  const int pw = 1 << K.pw_log2;
+  if (pw >= CB) {
+    const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
+    const int base = cld(P.b_indptr + it.d0.x) + ((it.jb * CB) >> K.pw_log2);
+    const int G = rank_groups(it.d0.y);
+#pragma unroll
+    for (int g = 0; g < kValuGroupBatch; ++g) it.pg[g] = g < G ? cld(P.b_pages + base + g * ncolB) : 0;
+  }
+  return it;
+}
+
+// Y_base / Y access of the CPL adjacent columns a lane owns: one dword (two
+// bf16 or one fp32), kept packed until used.
+template <class T>
+__device__ __forceinline__ uint32_t load_dword(const T* p) { return *reinterpret_cast<const uint32_t*>(p); }
+template <class T>
+__device__ __forceinline__ void store_dword(T* p, uint32_t u) { *reinterpret_cast<uint32_t*>(p) = u; }
+__device__ __forceinline__ float unpack_col(uint32_t u, int c, Bf16) { return c == 0 ? bf_lo(u) : bf_hi(u); }
+__device__ __forceinline__ float unpack_col(uint32_t u, int, F32) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t pack_cols(const float (&y)[2]) { return pack_bf2(y[0], y[1]); }
+__device__ __forceinline__ uint32_t pack_cols(const float (&y)[1]) { return __float_as_uint(y[0]); }
+
+// MBGMV expand item (one wave): (segment, part of a column block, chunk of
+// <= kValuExpandTokens of the segment's tokens).  A column block is kValuSubBlocks = 4 sub-blocks
+// of 64 lanes x CPL adjacent columns (2 in bf16, 1 in fp32); the 16 ranks of
+// a column are adjacent in the B page, so a lane reads 64 contiguous bytes
+// per sub-block and rank group.  A segment with 1, 2 or more rank groups
+// covers the block in 1, 2 or 4 parts of nsub = 4, 2 or 1 sub-blocks, so
+// every item holds four (sub-block, rank group) pairs -- 16 KiB of B per wave
+// in bf16 -- all requested at once with the first token's Y_base.  Pair i
+// is (sub-block i % nsub, group g0 + i / nsub).  v of the chunk's tokens is
+// staged once; the tokens are then produced one at a time from the B
+// registers, the next token's Y_base requested before the current token's
+// products.
+template <class E, class Prefetch>
+__device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, const ValuItem& item, float* vs,
+                                            int lane, Prefetch&& prefetch) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
   constexpr int CPL = 4 / (int)sizeof(T);
-  constexpr int CB = 64 * CPL;
-  constexpr int MT = kValuExpandTokens;
-  constexpr int GB = 4;  // rank groups per batch of loads
+  constexpr int SUBW = 64 * CPL;  // columns per sub-block
+  constexpr int NP = kValuSubBlocks;  // (sub-block, group) pairs per item
+  const int4 d0 = item.d0, d1 = item.d1;
   const int a = d0.x, r = d0.y;
-  const int tb = local * MT;
-  const int t0 = d0.z + tb;
-  const int n = min(MT, d0.w - tb);
+  // item = (part, chunk): chunks of one part are consecutive items, so they
+  // run side by side on one XCD and re-read the part's B from its L2
+  const int nch = valu_expand_chunks(d0.w);
+  const int part = item.local / nch, chunk = item.local - part * nch;
+  const int tb = chunk * kValuExpandTokens;
+  const int t0 = d0.z + tb, n = min(kValuExpandTokens, d0.w - tb);
   const float scale = __int_as_float(d1.w) / (float)r;
   const int G = rank_groups(r);
+  const int rs = G * 16;
+  const int nsub = kValuSubBlocks / valu_expand_parts(r);
+  const int ngb = NP / nsub;  // rank groups per batch of loads
   const int pw = 1 << K.pw_log2;
-  const int j0 = jb * CB + lane * CPL;
-  const bool live = j0 < P.d_out;
   const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
-  const bool one_page = pw >= CB;  // the block lies in one page of each group
-  const int bbase = cld(P.b_indptr + a);
-  const int ublk = (jb * CB) >> K.pw_log2;
-  const int off = (j0 & (pw - 1)) * 16;
-  auto load_batch = [&](int g0, uint4 (&b)[GB][4]) {
+  const int jblk = item.jb * (kValuSubBlocks * SUBW);
+  const bool one_page = pw >= kValuSubBlocks * SUBW;  // the column block lies in one page of each group
+  // first column this lane owns in each of the item's sub-blocks; a lane past
+  // d_out works on the last column (never stored)
+  int jc[NP];
+  bool live[NP];
 #pragma unroll
-    for (int gi = 0; gi < GB; ++gi) {
+  for (int sb = 0; sb < NP; ++sb) {
+    const int j = jblk + (part * nsub + sb) * SUBW + lane * CPL;
+    live[sb] = sb < nsub && j < P.d_out;  // d_out is a multiple of 8: a lane's columns are all in or all out
+    jc[sb] = j < P.d_out ? j : P.d_out - CPL;
+  }
+  // page ids of the batch's rank groups (one-page case), as four scalars: an
+  // array indexed by the run-time group of a pair would live in scratch
+  int pid0 = item.pg[0], pid1 = item.pg[1], pid2 = item.pg[2], pid3 = item.pg[3];
+  uint4 b[NP][4];
+  auto load_batch = [&](int g0) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int sb = i % nsub, gi = i / nsub;
       const int g = g0 + gi;
-      const int kmax = min(16, r - g * 16);
+      const int jcol = nsub == 4 ? jc[i] : (nsub == 2 ? jc[i & 1] : jc[0]);
+      bool ok = true;
       const T* pg = nullptr;
-      if (g < G && live)
-        pg = one_page ? page_ptr<E>(K, cld(P.b_pages + bbase + g * ncolB + ublk))
-                      : page_ptr<E>(K, P.b_pages[bbase + g * ncolB + (j0 >> K.pw_log2)]);
+      if (g < G)
+        pg = page_base<E>(K, one_page ? (gi == 0 ? pid0 : gi == 1 ? pid1 : gi == 2 ? pid2 : pid3)
+                                      : P.b_pages[cld(P.b_indptr + a) + g * ncolB + (jcol >> K.pw_log2)],
+                          ok);
+      (void)sb;
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
 #pragma unroll
         for (int v = 0; v < 16 / EPV; ++v) {
-          const int kv = v * EPV;
-          const T* src = pg + off + c * 16 + kv;
-          b[gi][c * (16 / EPV) + v] = (pg == nullptr || kv >= kmax) ? zero4()
-                                      : (kv + EPV <= kmax ? ldg16(src) : load_partial<E>(src, kmax - kv));
+          const int kn = g < G ? min(EPV, r - g * 16 - v * EPV) : 0;
+          b[i][c * (16 / EPV) + v] = load_b(pg + (jcol & (pw - 1)) * 16 + c * 16 + v * EPV, kn, ok);
         }
     }
   };
-  uint4 b[GB][4];
-  load_batch(0, b);
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
   T* Y = reinterpret_cast<T*>(P.Y);
-  float yb[MT][CPL];
+  // Y_base of one token (one dword per sub-block), requested one token ahead
+  uint32_t yb[NP], ybn[NP];
+  auto load_yb = [&](int t, uint32_t (&dst)[NP]) {
+    const int64_t row = cld(K.perm + t0 + t);
 #pragma unroll
-  for (int tt = 0; tt < MT; ++tt) {
+    for (int sb = 0; sb < NP; ++sb) dst[sb] = sb < nsub ? load_dword(Yb + row * P.ldyb + jc[sb]) : 0u;
+  };
+  load_batch(0);
+  load_yb(0, yb);
+  // the next item's metadata, while this item's loads are in flight
+  __builtin_amdgcn_sched_barrier(0);
+  prefetch();
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (EPV == 8) stage_v_split(K, P, d1.x + tb * r, r, n, reinterpret_cast<uint32_t*>(vs), lane);
+  else stage_v(K, P, d1.x, r, tb, n, vs, lane);
+  for (int t = 0; t < n; ++t) {
+    if (t + 1 < n) load_yb(t + 1, ybn);
+    float acc[NP][CPL];  // per pair
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) yb[tt][c] = 0.0f;
-    if (tt < n && live) {
-      const T* src = Yb + (int64_t)cld(K.perm + t0 + tt) * P.ldyb + j0;
+    for (int i = 0; i < NP; ++i)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) yb[tt][c] = to_f(src[c]);
-    }
-  }
-  stage_v(K, P, d1.x, r, tb, n, vs, lane);
-  const int rs = G * 16;
-  float acc[MT][CPL];
+      for (int c = 0; c < CPL; ++c) acc[i][c] = 0.0f;
+    for (int g0 = 0; g0 < G; g0 += ngb) {
+      // more than one batch of rank groups (only with nsub == 1): the batches
+      // are loaded in turn, for every token
+      if (g0 > 0 || (t > 0 && G > ngb)) {
+        if (one_page) {
+          const int base = cld(P.b_indptr + a) + (jblk >> K.pw_log2);
+          pid0 = cld(P.b_pages + base + g0 * ncolB);
+          pid1 = g0 + 1 < G ? cld(P.b_pages + base + (g0 + 1) * ncolB) : 0;
+          pid2 = g0 + 2 < G ? cld(P.b_pages + base + (g0 + 2) * ncolB) : 0;
+          pid3 = g0 + 3 < G ? cld(P.b_pages + base + (g0 + 3) * ncolB) : 0;
+        }
+        load_batch(g0);
+      }
+      uint4 vv[4];  // v of the current group: bf16 {hi 0-7, lo 0-7, hi 8-15, lo 8-15}; fp32 ranks 0-15
 #pragma unroll
-  for (int tt = 0; tt < MT; ++tt)
+      for (int i = 0; i < NP; ++i) {
+        const int g = g0 + i / nsub;
+        if (g >= G) continue;
+        if (i % nsub == 0) {  // first pair of a group: its v, once
+          const uint4* vt = reinterpret_cast<const uint4*>(vs + t * rs + g * 16);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[tt][c] = 0.0f;
-  for (int g0 = 0; g0 < G; g0 += GB) {
-    if (g0 > 0) load_batch(g0, b);
+          for (int q = 0; q < 4; ++q) vv[q] = vt[q];
+        }
+        uint4 w[4];
 #pragma unroll
-    for (int gi = 0; gi < GB; ++gi) {
-      if (g0 + gi >= G) break;
+        for (int q = 0; q < 4; ++q) w[q] = b[i][q];
+        if (r - g * 16 < 16) {  // the last group of a rank below a multiple of 16: mask ranks >= r
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        float bv[CPL][4];
+          for (int c = 0; c < CPL; ++c)
 #pragma unroll
-        for (int c = 0; c < CPL; ++c)
+            for (int v = 0; v < 16 / EPV; ++v) {
+              const int kn = r - g * 16 - v * EPV;
+              w[c * (16 / EPV) + v] = kn >= EPV ? w[c * (16 / EPV) + v] : keep_first(w[c * (16 / EPV) + v], kn, E());
+            }
+        }
+        if constexpr (EPV == 8) {  // bf16: packed B against split v (see stage_v_split)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) bv[c][i] = b_elem(b[gi], c, k4 * 4 + i, E());
+          for (int c = 0; c < CPL; ++c)
+            acc[i][c] = dot_split(w[c * 2 + 1], vv[2], vv[3], dot_split(w[c * 2], vv[0], vv[1], acc[i][c]));
+        } else {
 #pragma unroll
-        for (int tt = 0; tt < MT; ++tt) {
-          if (tt < n) {
-            const f4 vv = *reinterpret_cast<const f4*>(vs + tt * rs + (g0 + gi) * 16 + k4 * 4);
+          for (int k4 = 0; k4 < 4; ++k4)
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[tt][c] = fmaf(vv[i], bv[c][i], acc[tt][c]);
-          }
+              for (int e = 0; e < 4; ++e)
+                acc[i][c] = fmaf(__uint_as_float((&vv[k4].x)[e]), b_elem(w, c, k4 * 4 + e, E()), acc[i][c]);
         }
       }
     }
-  }
-  if (!live) return;
+    // pairs of one sub-block summed in ascending group order
+    if (nsub == 2) {
 #pragma unroll
-  for (int tt = 0; tt < MT; ++tt) {
-    if (tt < n) {
-      T* dst = Y + (int64_t)cld(K.perm + t0 + tt) * P.ldy + j0;
+      for (int c = 0; c < CPL; ++c) {
+        acc[0][c] += acc[2][c];
+        acc[1][c] += acc[3][c];
+      }
+    } else if (nsub == 1) {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) from_f(dst + c, yb[tt][c] + scale * acc[tt][c]);
+      for (int c = 0; c < CPL; ++c) acc[0][c] = ((acc[0][c] + acc[1][c]) + acc[2][c]) + acc[3][c];
     }
+    const int64_t row = cld(K.perm + t0 + t);
+#pragma unroll
+    for (int sb = 0; sb < NP; ++sb) {
+      if (live[sb]) {
+        float y[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) y[c] = unpack_col(yb[sb], c, E()) + scale * acc[sb][c];
+        store_dword(Y + row * P.ldy + jc[sb], pack_cols(y));
+      }
+    }
+#pragma unroll
+    for (int sb = 0; sb < NP; ++sb) yb[sb] = ybn[sb];
   }
 }
 
@@ -623,13 +862,17 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
   const int bbase = cld(P.b_indptr + a);
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
   T* Y = reinterpret_cast<T*>(P.Y);
-  const int64_t row = li < nt ? K.perm[t0 + li] : -1;
+  // lanes of tokens past the tile read the tile's first row (never stored)
+  const int64_t row = K.perm[t0 + (li < nt ? li : 0)];
+  const int G = rank_groups(r);
+  // page of each of this lane's K steps; a step past the last rank group
+  // reads the last group and is zeroed by the rank mask
   const T* pgk[NKS];
+  bool okk[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    const int k0 = ks * KSTEP + qq * EPV;
-    pgk[ks] = (one_page && k0 < r) ? page_ptr<E>(K, P.b_pages[bbase + (k0 >> 4) * ncolB + (j0 >> K.pw_log2)])
-                                   : nullptr;
+    const int g = min((ks * KSTEP + qq * EPV) >> 4, G - 1);
+    pgk[ks] = page_base<E>(K, one_page ? P.b_pages[bbase + g * ncolB + (j0 >> K.pw_log2)] : 0, okk[ks]);
   }
   uint4 vv[NKS];
 #pragma unroll
@@ -640,24 +883,21 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
   auto load_part = [&](int part, uint4 (&bv)[CT][NKS], float (&ybv)[CT][4]) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      const int jl = part * PART + ct * 16 + li;
-      const int j = j0 + jl;
+      // columns past the block are clamped to its last column (never stored)
+      const int j = j0 + min(part * PART + ct * 16 + li, jend - 1);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int k0 = ks * KSTEP + qq * EPV;
-        const int kn = min(EPV, r - k0);
+        const int g = min(k0 >> 4, G - 1);
         bv[ct][ks] = zero4();
-        if (jl < jend && kn > 0) {
-          const T* pg = one_page ? pgk[ks] : page_ptr<E>(K, P.b_pages[bbase + (k0 >> 4) * ncolB + (j >> K.pw_log2)]);
-          if (pg != nullptr) {
-            const T* src = pg + (j & (pw - 1)) * 16 + (k0 & 15);
-            bv[ct][ks] = kn >= EPV ? ldg16(src) : load_partial<E>(src, kn);
-          }
+        if (ks * KSTEP < r) {  // uniform: a K step wholly past the rank is skipped
+          bool ok = okk[ks];
+          const T* pg = one_page ? pgk[ks] : page_base<E>(K, P.b_pages[bbase + g * ncolB + (j >> K.pw_log2)], ok);
+          if (ok) bv[ct][ks] = ldg16(pg + (j & (pw - 1)) * 16 + (k0 & 15));
         }
       }
-      const int c4 = part * PART + ct * 16 + qq * 4;
-      if (row >= 0 && c4 < jend) load4(Yb + row * P.ldyb + j0 + c4, ybv[ct]);
-      else ybv[ct][0] = ybv[ct][1] = ybv[ct][2] = ybv[ct][3] = 0.0f;
+      const int c4 = min(part * PART + ct * 16 + qq * 4, jend - 4);
+      load4(Yb + row * P.ldyb + j0 + c4, ybv[ct]);
     }
   };
   uint4 bcur[CT][NKS], bnext[CT][NKS];
@@ -671,9 +911,14 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
     for (int ct = 0; ct < CT; ++ct) {
       acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) mma(acc[ct], bcur[ct][ks], vv[ks], E());
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks * KSTEP >= r) continue;  // uniform
+        // ranks past r in this lane's vector are masked here, at the use
+        const uint4 w = (ks + 1) * KSTEP > r ? keep_first(bcur[ct][ks], r - (ks * KSTEP + qq * EPV), E()) : bcur[ct][ks];
+        mma(acc[ct], w, vv[ks], E());
+      }
     }
-    if (row >= 0) {
+    if (li < nt) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const int c4 = part * PART + ct * 16 + qq * 4;
@@ -713,42 +958,45 @@ __device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int 
   const int j0 = (jb * kWaves + wave) * wc;
   const int jend = min(wc, P.d_out - j0);
   if (jend > 0) {
+    // K steps past the rank are skipped inside the body, so two variants
+    // cover every rank
     const int nks = ceil_div_i(r, KSTEP);
-    if (nks <= 1) expand_mfma_body<E, 1>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
-    else if (nks <= 2) expand_mfma_body<E, 2>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
-    else if (MAXKS <= 4 || nks <= 4)
-      expand_mfma_body<E, MAXKS <= 4 ? MAXKS : 4>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
+    if (nks <= MAXKS / 2) expand_mfma_body<E, MAXKS / 2>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
     else expand_mfma_body<E, MAXKS>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
   }
   __syncthreads();  // the rows are restaged by the block's next item
 }
 
-// Rows of tokens without an adapter: Y = Y_base (only when Y is not Y_base).
+// Rows of tokens without an adapter: Y = Y_base (only when Y is not Y_base),
+// kCopyTokens rows x one column block per item.
 template <class E>
 __device__ __forceinline__ void expand_copy(const KArgs& K, const KProj& P, int jb, int chunk, int t_valid, int lane) {
   typedef typename E::T T;
   constexpr int CPL = 4 / (int)sizeof(T);
-  const int j0 = jb * 64 * CPL + lane * CPL;
-  if (j0 >= P.d_out) return;
-  const int t_beg = t_valid + chunk * kValuExpandTokens;
-  const int t_end = min(K.T, t_beg + kValuExpandTokens);
+  constexpr int SUBW = 64 * CPL;
+  const int t_beg = t_valid + chunk * kCopyTokens;
+  const int t_end = min(K.T, t_beg + kCopyTokens);
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
   T* Y = reinterpret_cast<T*>(P.Y);
   for (int i = t_beg; i < t_end; ++i) {
-    const int64_t row = K.perm[i];
+    const int64_t row = cld(K.perm + i);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) Y[row * P.ldy + j0 + c] = Yb[row * P.ldyb + j0 + c];
+    for (int sb = 0; sb < kValuSubBlocks; ++sb) {
+      const int j = (jb * kValuSubBlocks + sb) * SUBW + lane * CPL;
+      if (j < P.d_out) store_dword(Y + row * P.ldy + j, load_dword(Yb + row * P.ldyb + j));
+    }
   }
 }
 
 template <class E>
-__global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArgs K) {
+__global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArgs) {
+  const KArgs& K = kernel_args();
   __shared__ __attribute__((aligned(16))) float vs_all[kWaves][kMfmaExpandTokens * LORA_MAX_RANK];
   const int S = cld(K.counts + kCountS);
   const int t_valid = cld(K.counts + kCountTValid);
   const int Um = S > 0 ? cld(K.counts + kCountExpandMfma) : 0;
   const int Uv = S > 0 ? cld(K.counts + kCountExpandValu) : 0;
-  const int ncopy = ceil_div_i(K.T - t_valid, kValuExpandTokens);
+  const int ncopy = ceil_div_i(K.T - t_valid, kCopyTokens);
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   float* vs = vs_all[wave];
   // MBGMM items first (whole-block items), then MBGMV items and the copies of
@@ -780,24 +1028,25 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
   }
   int total = 0;
   for (int p = 0; p < K.np; ++p) total += K.p[p].njs * (Uv + (K.p[p].Y != K.p[p].Yb ? ncopy : 0));
-  for (WaveWalk it(total, wave); it.i < it.end; it.i += it.stride) {
-    int rem = it.i, p = 0;
-    int Up = Uv + (K.p[0].Y != K.p[0].Yb ? ncopy : 0);
-    while (rem >= K.p[p].njs * Up) {
-      rem -= K.p[p].njs * Up;
-      ++p;
-      Up = Uv + (K.p[p].Y != K.p[p].Yb ? ncopy : 0);
+  WaveWalk it(total, wave);
+  if (it.i >= it.end) return;
+  ValuItem cur = fetch_valu_item<E>(K, it.i, Uv, ncopy);
+  for (;;) {
+    const int ni = it.i + it.stride;
+    const bool more = ni < it.end;
+    ValuItem nxt;
+    if (cur.copy) {
+      expand_copy<E>(K, K.p[cur.p], cur.jb, cur.local, t_valid, lane);
+      if (more) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy);
+    } else {
+      expand_valu<E>(K, K.p[cur.p], cur, vs, lane, [&]() {
+        if (more) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy);
+      });
+      wave_sync();
     }
-    const int jb = rem / Up;
-    const int u = rem - jb * Up;
-    if (u >= Uv) {
-      expand_copy<E>(K, K.p[p], jb, u - Uv, t_valid, lane);
-      continue;
-    }
-    const int s = cld(K.exp_item_v + u);
-    const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
-    expand_valu<E>(K, K.p[p], jb, d0, d1, u - d1.z, vs, lane);
-    wave_sync();
+    if (!more) break;
+    cur = nxt;
+    it.i = ni;
   }
 }
 
@@ -890,7 +1139,7 @@ __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N,
     // {tokens, segments, v entries, MBGMM shrink, MBGMV shrink, MBGMM expand, MBGMV expand}
     const int vals[7] = {cnt, has ? 1 : 0, cnt * r, has ? shrink_items_mfma(cnt, r) : 0,
                          has ? shrink_items_valu(cnt, r) : 0, has ? expand_items_mfma(cnt) : 0,
-                         has ? expand_items_valu(cnt) : 0};
+                         has ? expand_items_valu(cnt, r) : 0};
     int pre[7], tots[7];
 #pragma unroll
     for (int f = 0; f < 7; ++f) {

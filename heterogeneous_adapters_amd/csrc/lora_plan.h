@@ -30,7 +30,8 @@ constexpr int kThreads = 256;             // work-group size (4 wave64)
 constexpr int kWaves = kThreads / 64;
 constexpr int kKSlice = 512;              // input columns per shrink item (one partial slice)
 constexpr int kValuTokens = 2;            // tokens per MBGMV shrink item
-constexpr int kValuExpandTokens = 8;      // tokens per MBGMV expand item
+constexpr int kValuExpandTokens = 4;      // tokens per MBGMV expand item (a chunk of the segment)
+constexpr int kCopyTokens = 8;            // rows per copy item (tokens without an adapter)
 constexpr int kMfmaExpandTokens = 16;     // tokens per MBGMM expand item (one tile)
 constexpr int kProjsPerLaunch = 16;       // projection descriptors per launch
 constexpr int kSegChunk = 1024;           // tokens per segment-builder block
@@ -39,9 +40,11 @@ constexpr int kSegChunk = 1024;           // tokens per segment-builder block
 #endif
 constexpr int kMfmaMinTokens = LORA_MFMA_MIN_TOKENS;  // segment length that switches to MFMA
 
-// Output columns per MBGMV expand item: 2 per lane in bf16, 1 per lane in
-// fp32 (64 bytes of B per lane and rank group either way).
-LORA_HD inline int expand_cols(bool bf16) { return bf16 ? 128 : 64; }
+// Output columns of an MBGMV expand column block: 4 sub-blocks of 64 lanes x
+// (2 bf16 | 1 fp32) columns, i.e. 64 bytes of B per lane, sub-block and rank
+// group.
+constexpr int kValuSubBlocks = 4;
+LORA_HD inline int expand_cols(bool bf16) { return kValuSubBlocks * 64 * (bf16 ? 2 : 1); }
 
 LORA_HD inline int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 LORA_HD inline int rank_groups(int r) { return (r + 15) >> 4; }
@@ -50,15 +53,21 @@ LORA_HD inline bool is_mfma_segment(int n) { return n >= kMfmaMinTokens; }
 
 // Work items of one segment, per 512-column shrink slice or per expand
 // column block.  MBGMV shrink: (rank group, <= kValuTokens tokens); MBGMM
-// shrink: (16-token tile, rank group); MBGMV expand: <= 8 tokens; MBGMM
-// expand: one 16-token tile.
+// shrink: (16-token tile, rank group); MBGMV expand: (part, chunk of <= 4
+// tokens), the column block split in 1, 2 or 4 parts for 1, 2 or more rank
+// groups (every part holds at most 4 (sub-block, rank group) pairs of B);
+// MBGMM expand: one 16-token tile.
 LORA_HD inline int shrink_items_valu(int n, int r) {
   return is_mfma_segment(n) ? 0 : rank_groups(r) * ceil_div_i(n, kValuTokens);
 }
 LORA_HD inline int shrink_items_mfma(int n, int r) {
   return is_mfma_segment(n) ? rank_groups(r) * ceil_div_i(n, 16) : 0;
 }
-LORA_HD inline int expand_items_valu(int n) { return is_mfma_segment(n) ? 0 : ceil_div_i(n, kValuExpandTokens); }
+LORA_HD inline int valu_expand_parts(int r) { return rank_groups(r) == 1 ? 1 : rank_groups(r) == 2 ? 2 : 4; }
+LORA_HD inline int valu_expand_chunks(int n) { return ceil_div_i(n, kValuExpandTokens); }
+LORA_HD inline int expand_items_valu(int n, int r) {
+  return is_mfma_segment(n) ? 0 : valu_expand_parts(r) * valu_expand_chunks(n);
+}
 LORA_HD inline int expand_items_mfma(int n) { return is_mfma_segment(n) ? ceil_div_i(n, kMfmaExpandTokens) : 0; }
 
 // counters (int32) written by the segment builder
@@ -84,8 +93,9 @@ LORA_HD inline PlanLayout plan_layout(int T, int N) {
   // MBGMM shrink items <= 8*(T/16 + S) <= 9T; MBGMV <= 8*(T/2 + S) <= 12T
   L.shrink_valu = L.shrink_mfma + align64(9 * t + 1);
   L.expand_mfma = L.shrink_valu + align64(12 * t + 1);
+  // MBGMM expand items <= T/16 + S <= 2T; MBGMV <= 4*(T/4 + S) <= 5T
   L.expand_valu = L.expand_mfma + align64(2 * t + 1);
-  L.total = L.expand_valu + align64(2 * t + 1);
+  L.total = L.expand_valu + align64(5 * t + 1);
   return L;
 }
 
