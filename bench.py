@@ -13,7 +13,7 @@ gate/up, down: four calls per layer, the grouping a real forward pass allows).
 Prints ONE JSON line.  ``value`` is whole-step algorithmic HBM GB/s (bytes the
 method must move: activations once, each distinct adapter's unpadded A and B
 once) with every input already resident in HBM.  ``roofline`` covers the
-dominant kernel (the expand kernel; both kernels are reported under
+dominant kernel (the expand kernel, its wide-page instantiation; both kernels are reported under
 ``kernels``): after the timed steps the same groups are run through
 lora_shrink / lora_expand -- the two launches of lora_apply, same grid --
 with HIP events around each launch on the stream the library launches on.
@@ -154,7 +154,7 @@ def summarize_profile(dirs, command):
                              f"max {vals.max():12.1f}  {name[:90]}")
         for ctr, f in sorted(calib.items()):
             lines.append(f"{ctr.lower()}_scale: {f:.4f}")
-        for kname, key in (("shrink_kernel<lora::Bf16>", "shrink"), ("expand_kernel<lora::Bf16>", "expand")):
+        for kname, key in (("shrink_kernel<lora::Bf16>", "shrink"), ("expand_kernel<lora::Bf16, true>", "expand")):
             tot, have = 0.0, 0
             for (name, ctr), disp in per.items():
                 if kname in name and ctr in calib:
@@ -326,17 +326,17 @@ def main():
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     mean_call_ms = call_ms.mean(axis=0)
     kernels = {}
-    for kname, ms_g, part in (("shrink_kernel<Bf16>", shr_ms, 0), ("expand_kernel<Bf16>", exp_ms, 1)):
+    for kname, ms_g, part in (("shrink_kernel<Bf16>", shr_ms, 0), ("expand_kernel<Bf16, true>", exp_ms, 1)):
         kb = [sum(traffic.split_bytes(dw.ids, dw.ranks, dw.tables[i].d_in, dw.tables[i].d_out, e)[part]
                   for i in g) for g in groups]
         gb = float(np.sum(kb) / (ms_g.sum() * 1e-3) / 1e9)
         kernels[kname] = {"launches_per_step": len(groups), "mean_launch_us": round(float(ms_g.mean()) * 1e3, 2),
                           "algorithmic_bytes_per_launch": int(np.mean(kb)), "gbs": round(gb, 1),
                           "frac_hbm_peak": round(gb / HBM_PEAK_GBS, 4)}
-    dom = kernels["expand_kernel<Bf16>"]
+    dom = kernels["expand_kernel<Bf16, true>"]
     roofline = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": dom["frac_hbm_peak"], "traffic": load_traffic(kernel_source_hash()),
-                "kernel": "expand_kernel<Bf16>", "mean_launch_us": dom["mean_launch_us"],
+                "kernel": "expand_kernel<Bf16, true>", "mean_launch_us": dom["mean_launch_us"],
                 "algorithmic_bytes_per_launch": dom["algorithmic_bytes_per_launch"],
                 "launches_per_step": len(groups)}
 

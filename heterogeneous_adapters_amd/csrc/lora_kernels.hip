@@ -163,17 +163,13 @@ __device__ __forceinline__ uint4 keep_first(uint4 w, int kn, F32) {
   return make_uint4(kn > 0 ? w.x : 0u, kn > 1 ? w.y : 0u, kn > 2 ? w.z : 0u, kn > 3 ? w.w : 0u);
 }
 
-// One 16-byte vector of a B column (kEpv consecutive ranks of one output
-// column; the 16 rank slots of a column are one 32- or 64-byte row of its
-// page).  kn = ranks of the vector below r: none, or a page outside the pool
-// -> zeros without a load.  A vector with some ranks past r is read whole
-// (the column row is fetched whole anyway) and masked where it is used, so
-// that no instruction waits on the load here.
-__device__ __forceinline__ uint4 load_b(const void* p, int kn, bool ok) {
-  uint4 w = zero4();
-  if (kn > 0 && ok) w = ldg16(p);
-  return w;
-}
+// B vectors (kEpv consecutive ranks of one output column; the 16 rank slots
+// of a column are one 32- or 64-byte row of its page) are loaded
+// unconditionally from valid addresses -- ranks past r from the same column
+// row, a rank group past the adapter's from its last group, a page outside
+// the pool from page 0 -- and zeroed where they are used.  A skipped load
+// would write zeros into registers that an older load may still target, and
+// the compiler then waits for that older load.
 
 // Largest s with ptr[s] <= u (ptr strictly increasing, ptr[0] = 0).
 __device__ __forceinline__ int find_segment(const int32_t* ptr, int S, int u) {
@@ -658,9 +654,9 @@ __device__ __forceinline__ uint32_t pack_cols(const float (&y)[1]) { return __fl
 // staged once; the tokens are then produced one at a time from the B
 // registers, the next token's Y_base requested before the current token's
 // products.
-template <class E, class Prefetch>
-__device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, const ValuItem& item, float* vs,
-                                            int lane, Prefetch&& prefetch) {
+template <class E, bool ONE_PAGE, class Prefetch>
+__device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P, const ValuItem& item, float* vs,
+                                                 int lane, Prefetch&& prefetch) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
   constexpr int CPL = 4 / (int)sizeof(T);
@@ -682,7 +678,7 @@ __device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, cons
   const int pw = 1 << K.pw_log2;
   const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
   const int jblk = item.jb * (kValuSubBlocks * SUBW);
-  const bool one_page = pw >= kValuSubBlocks * SUBW;  // the column block lies in one page of each group
+  constexpr bool one_page = ONE_PAGE;  // the column block lies in one page of each group
   // first column this lane owns in each of the item's sub-blocks; a lane past
   // d_out works on the last column (never stored)
   int jc[NP];
@@ -697,26 +693,37 @@ __device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, cons
   // array indexed by the run-time group of a pair would live in scratch
   int pid0 = item.pg[0], pid1 = item.pg[1], pid2 = item.pg[2], pid3 = item.pg[3];
   uint4 b[NP][4];
+  bool okp[NP];  // page of the pair inside the pool
+  // The two page-lookup cases are separate instantiations: a page id read
+  // per lane (block spanning pages) must be waited for before its data load,
+  // and a shared path puts that wait in front of every pair's loads.
   auto load_batch = [&](int g0) {
+    if constexpr (ONE_PAGE) {  // page ids are wave-uniform scalars: all 16 loads go out back to back
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int sb = i % nsub, gi = i / nsub;
-      const int g = g0 + gi;
-      const int jcol = nsub == 4 ? jc[i] : (nsub == 2 ? jc[i & 1] : jc[0]);
-      bool ok = true;
-      const T* pg = nullptr;
-      if (g < G)
-        pg = page_base<E>(K, one_page ? (gi == 0 ? pid0 : gi == 1 ? pid1 : gi == 2 ? pid2 : pid3)
-                                      : P.b_pages[cld(P.b_indptr + a) + g * ncolB + (jcol >> K.pw_log2)],
-                          ok);
-      (void)sb;
+      for (int i = 0; i < NP; ++i) {
+        const int gi = i / nsub;
+        const int jcol = nsub == 4 ? jc[i] : (nsub == 2 ? jc[i & 1] : jc[0]);
+        // a group past the adapter's has page id 0 here (never used)
+        const T* pg = page_base<E>(K, gi == 0 ? pid0 : gi == 1 ? pid1 : gi == 2 ? pid2 : pid3, okp[i]);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c)
+        for (int q = 0; q < 4; ++q) b[i][q] = ldg16(pg + (jcol & (pw - 1)) * 16 + (q / (16 / EPV)) * 16 + (q % (16 / EPV)) * EPV);
+      }
+    } else {  // per-lane page ids, all requested before the first data load
+      int pl[NP];
+      const int base = cld(P.b_indptr + a);
 #pragma unroll
-        for (int v = 0; v < 16 / EPV; ++v) {
-          const int kn = g < G ? min(EPV, r - g * 16 - v * EPV) : 0;
-          b[i][c * (16 / EPV) + v] = load_b(pg + (jcol & (pw - 1)) * 16 + c * 16 + v * EPV, kn, ok);
-        }
+      for (int i = 0; i < NP; ++i) {
+        const int g = min(g0 + i / nsub, G - 1);
+        const int jcol = nsub == 4 ? jc[i] : (nsub == 2 ? jc[i & 1] : jc[0]);
+        pl[i] = P.b_pages[base + g * ncolB + (jcol >> K.pw_log2)];
+      }
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int jcol = nsub == 4 ? jc[i] : (nsub == 2 ? jc[i & 1] : jc[0]);
+        const T* pg = page_base<E>(K, pl[i], okp[i]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) b[i][q] = ldg16(pg + (jcol & (pw - 1)) * 16 + (q / (16 / EPV)) * 16 + (q % (16 / EPV)) * EPV);
+      }
     }
   };
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
@@ -747,7 +754,7 @@ __device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, cons
       // more than one batch of rank groups (only with nsub == 1): the batches
       // are loaded in turn, for every token
       if (g0 > 0 || (t > 0 && G > ngb)) {
-        if (one_page) {
+        if constexpr (ONE_PAGE) {
           const int base = cld(P.b_indptr + a) + (jblk >> K.pw_log2);
           pid0 = cld(P.b_pages + base + g0 * ncolB);
           pid1 = g0 + 1 < G ? cld(P.b_pages + base + (g0 + 1) * ncolB) : 0;
@@ -768,7 +775,7 @@ __device__ __forceinline__ void expand_valu(const KArgs& K, const KProj& P, cons
         }
         uint4 w[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = b[i][q];
+        for (int q = 0; q < 4; ++q) w[q] = okp[i] ? b[i][q] : zero4();
         if (r - g * 16 < 16) {  // the last group of a rank below a multiple of 16: mask ranks >= r
 #pragma unroll
           for (int c = 0; c < CPL; ++c)
@@ -844,7 +851,7 @@ __device__ __forceinline__ void store4(float* p, const float (&y)[4]) {
 // ranks of an output column contiguously, so each lane's operand is one
 // 16-byte load, and a lane's four C values are four adjacent columns of one
 // token (one 8- or 16-byte Y access).
-template <class E, int NKS>
+template <class E, int NKS, bool WIDE>
 __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P, int j0, int jend, int wc, int a,
                                                  int r, int t0, int nt, float scale, const float* vs, int lane) {
   typedef typename E::T T;
@@ -858,7 +865,9 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
   const int rs = rank_groups(r) * 16;
   const int pw = 1 << K.pw_log2;
   const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
-  const bool one_page = pw >= wc;  // [j0, j0+wc) is wc-aligned: one page of each group
+  // [j0, j0+wc) is wc-aligned, so it lies in one page of each group when
+  // pw >= wc; always in a WIDE kernel (pw >= 512 >= wc)
+  const bool one_page = WIDE || pw >= wc;
   const int bbase = cld(P.b_indptr + a);
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
   T* Y = reinterpret_cast<T*>(P.Y);
@@ -872,7 +881,7 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const int g = min((ks * KSTEP + qq * EPV) >> 4, G - 1);
-    pgk[ks] = page_base<E>(K, one_page ? P.b_pages[bbase + g * ncolB + (j0 >> K.pw_log2)] : 0, okk[ks]);
+    pgk[ks] = page_base<E>(K, one_page ? cld(P.b_pages + bbase + g * ncolB + (j0 >> K.pw_log2)) : 0, okk[ks]);
   }
   uint4 vv[NKS];
 #pragma unroll
@@ -880,7 +889,7 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
     const int k0 = ks * KSTEP + qq * EPV;
     vv[ks] = (li < nt && k0 < r) ? pack_operand(vs + li * rs + k0, EPV, E()) : zero4();
   }
-  auto load_part = [&](int part, uint4 (&bv)[CT][NKS], float (&ybv)[CT][4]) {
+  auto load_part = [&](int part, uint4 (&bv)[CT][NKS], float (&ybv)[CT][4], bool (&okc)[CT][NKS]) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       // columns past the block are clamped to its last column (never stored)
@@ -889,12 +898,12 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
       for (int ks = 0; ks < NKS; ++ks) {
         const int k0 = ks * KSTEP + qq * EPV;
         const int g = min(k0 >> 4, G - 1);
-        bv[ct][ks] = zero4();
-        if (ks * KSTEP < r) {  // uniform: a K step wholly past the rank is skipped
-          bool ok = okk[ks];
-          const T* pg = one_page ? pgk[ks] : page_base<E>(K, P.b_pages[bbase + g * ncolB + (j >> K.pw_log2)], ok);
-          if (ok) bv[ct][ks] = ldg16(pg + (j & (pw - 1)) * 16 + (k0 & 15));
-        }
+        // unconditional (see load_b's note); a K step wholly past the rank
+        // reads the last group and is skipped at the product
+        bool ok = okk[ks];
+        const T* pg = one_page ? pgk[ks] : page_base<E>(K, P.b_pages[bbase + g * ncolB + (j >> K.pw_log2)], ok);
+        bv[ct][ks] = ldg16(pg + (j & (pw - 1)) * 16 + (k0 & 15));
+        okc[ct][ks] = ok;
       }
       const int c4 = min(part * PART + ct * 16 + qq * 4, jend - 4);
       load4(Yb + row * P.ldyb + j0 + c4, ybv[ct]);
@@ -902,10 +911,11 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
   };
   uint4 bcur[CT][NKS], bnext[CT][NKS];
   float ycur[CT][4], ynext[CT][4];
+  bool okcur[CT][NKS], oknext[CT][NKS];
   const int np = ceil_div_i(jend, PART);
-  load_part(0, bcur, ycur);
+  load_part(0, bcur, ycur, okcur);
   for (int part = 0; part < np; ++part) {
-    if (part + 1 < np) load_part(part + 1, bnext, ynext);
+    if (part + 1 < np) load_part(part + 1, bnext, ynext, oknext);
     f4 acc[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -913,8 +923,10 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         if (ks * KSTEP >= r) continue;  // uniform
-        // ranks past r in this lane's vector are masked here, at the use
-        const uint4 w = (ks + 1) * KSTEP > r ? keep_first(bcur[ct][ks], r - (ks * KSTEP + qq * EPV), E()) : bcur[ct][ks];
+        // ranks past r in this lane's vector, and pages outside the pool, are
+        // masked here, at the use
+        uint4 w = (ks + 1) * KSTEP > r ? keep_first(bcur[ct][ks], r - (ks * KSTEP + qq * EPV), E()) : bcur[ct][ks];
+        if (!okcur[ct][ks]) w = zero4();
         mma(acc[ct], w, vv[ks], E());
       }
     }
@@ -933,7 +945,10 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) bcur[ct][ks] = bnext[ct][ks];
+      for (int ks = 0; ks < NKS; ++ks) {
+        bcur[ct][ks] = bnext[ct][ks];
+        okcur[ct][ks] = oknext[ct][ks];
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) ycur[ct][i] = ynext[ct][i];
     }
@@ -943,7 +958,7 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
 // MBGMM expand item (one block): (segment, 16-token tile, 4*wc columns).  The
 // block stages v of the tile once into shared LDS rows; wave w then produces
 // columns [w*wc, (w+1)*wc) of the item.
-template <class E>
+template <class E, bool WIDE>
 __device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int jb, int wc, int4 d0, int4 d1,
                                             int local, float* vs, int wave, int lane) {
   constexpr int KSTEP = 4 * E::kEpv;
@@ -961,8 +976,8 @@ __device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int 
     // K steps past the rank are skipped inside the body, so two variants
     // cover every rank
     const int nks = ceil_div_i(r, KSTEP);
-    if (nks <= MAXKS / 2) expand_mfma_body<E, MAXKS / 2>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
-    else expand_mfma_body<E, MAXKS>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
+    if (nks <= MAXKS / 2) expand_mfma_body<E, MAXKS / 2, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
+    else expand_mfma_body<E, MAXKS, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
   }
   __syncthreads();  // the rows are restaged by the block's next item
 }
@@ -988,7 +1003,10 @@ __device__ __forceinline__ void expand_copy(const KArgs& K, const KProj& P, int 
   }
 }
 
-template <class E>
+// WIDE: pages hold at least one whole MBGMV column block (expand_cols), so
+// every page lookup of an item is wave-uniform; chosen by the host from the
+// page width (the other instantiation looks pages up per lane).
+template <class E, bool WIDE>
 __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArgs) {
   const KArgs& K = kernel_args();
   __shared__ __attribute__((aligned(16))) float vs_all[kWaves][kMfmaExpandTokens * LORA_MAX_RANK];
@@ -1023,7 +1041,7 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
       const int u = rem - jb * Um;
       const int s = cld(K.exp_item_m + u);
       const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
-      expand_mfma<E>(K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[0], wave, lane);
+      expand_mfma<E, WIDE>(K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[0], wave, lane);
     }
   }
   int total = 0;
@@ -1039,7 +1057,7 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
       expand_copy<E>(K, K.p[cur.p], cur.jb, cur.local, t_valid, lane);
       if (more) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy);
     } else {
-      expand_valu<E>(K, K.p[cur.p], cur, vs, lane, [&]() {
+      expand_valu_body<E, WIDE>(K, K.p[cur.p], cur, vs, lane, [&]() {
         if (more) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy);
       });
       wave_sync();
@@ -1269,8 +1287,15 @@ hipError_t launch_shrink(const KArgs& K, int dtype, int grid, hipStream_t stream
 }
 
 hipError_t launch_expand(const KArgs& K, int dtype, int grid, hipStream_t stream) {
-  if (dtype == LORA_DTYPE_BF16) expand_kernel<Bf16><<<grid, kThreads, 0, stream>>>(K);
-  else expand_kernel<F32><<<grid, kThreads, 0, stream>>>(K);
+  const bool bf16 = dtype == LORA_DTYPE_BF16;
+  const bool wide = (1 << K.pw_log2) >= expand_cols(bf16);
+  if (bf16) {
+    if (wide) expand_kernel<Bf16, true><<<grid, kThreads, 0, stream>>>(K);
+    else expand_kernel<Bf16, false><<<grid, kThreads, 0, stream>>>(K);
+  } else {
+    if (wide) expand_kernel<F32, true><<<grid, kThreads, 0, stream>>>(K);
+    else expand_kernel<F32, false><<<grid, kThreads, 0, stream>>>(K);
+  }
   return launch_err();
 }
 
@@ -1278,10 +1303,10 @@ hipError_t occupancy(int dtype, int* shrink_blocks, int* expand_blocks) {
   hipError_t e;
   if (dtype == LORA_DTYPE_BF16) {
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(shrink_blocks, shrink_kernel<Bf16>, kThreads, 0);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(expand_blocks, expand_kernel<Bf16>, kThreads, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(expand_blocks, expand_kernel<Bf16, true>, kThreads, 0);
   } else {
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(shrink_blocks, shrink_kernel<F32>, kThreads, 0);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(expand_blocks, expand_kernel<F32>, kThreads, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(expand_blocks, expand_kernel<F32, true>, kThreads, 0);
   }
   return e;
 }
