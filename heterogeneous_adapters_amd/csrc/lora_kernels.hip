@@ -277,7 +277,7 @@ __device__ const KArgs& kernel_args();
 // 64 lanes are reduced across the wave.  All loads are issued before the
 // first product, so an item costs one memory round trip after its page
 // lookup.
-template <class E>
+template <class E, bool WIDE>
 __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int q, int4 d0, int4 d1, int local, int lane) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
@@ -289,37 +289,50 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int 
   const int tb = (local - g * nch) * NV;
   const int nt = min(NV, n - tb);
   const int col0 = q * kKSlice;
-  const int ncols = min(kKSlice, P.d_in - col0);
+  const int ncols = min(kKSlice, P.d_in - col0);  // a multiple of 8
   const int pw = 1 << K.pw_log2;
   const int rows = min(16, r - g * 16);
-  const int slot0 = P.a_indptr[a] + g * ((P.d_in + pw - 1) >> K.pw_log2);
+  const int slot0 = cld(P.a_indptr + a) + g * ((P.d_in + pw - 1) >> K.pw_log2);
   const T* X = reinterpret_cast<const T*>(P.X);
-
-  // per-lane page pointers (the row addresses stay in vector registers)
-  const T* pg[NVEC];
-  int off[NVEC];
-  bool ok[NVEC];
+  // Every load is unconditional and in bounds: rows past the rank re-read
+  // the group's last row, tokens past the item its last token, lanes past
+  // d_in the slice's last vector.  Their products are never stored (rows,
+  // tokens) or are zeroed before the reduction (lanes), so no load is ever
+  // skipped -- a skipped load's zero fill would make the compiler wait for
+  // older loads into the same registers.
+  int cl[NVEC];
+  bool lane_ok[NVEC];
 #pragma unroll
   for (int v = 0; v < NVEC; ++v) {
     const int c = v * 64 * EPV + lane * EPV;
-    const int col = col0 + c;
-    ok[v] = c < ncols;
-    off[v] = col & (pw - 1);
-    pg[v] = ok[v] ? page_ptr<E>(K, P.a_pages[slot0 + (col >> K.pw_log2)]) : nullptr;
+    lane_ok[v] = c < ncols;
+    cl[v] = lane_ok[v] ? c : ncols - EPV;
+  }
+  const T* pg[NVEC];
+  bool pok[NVEC];
+  if constexpr (WIDE) {  // the slice lies in one page: a wave-uniform lookup
+    bool ok;
+    const T* p = page_base<E>(K, cld(P.a_pages + slot0 + (col0 >> K.pw_log2)), ok);
+#pragma unroll
+    for (int v = 0; v < NVEC; ++v) {
+      pg[v] = p;
+      pok[v] = ok;
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < NVEC; ++v) pg[v] = page_base<E>(K, P.a_pages[slot0 + ((col0 + cl[v]) >> K.pw_log2)], pok[v]);
   }
   uint4 w[16][NVEC];
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr)
 #pragma unroll
-    for (int v = 0; v < NVEC; ++v)
-      w[rr][v] = (pg[v] != nullptr && rr < rows) ? ldg16(pg[v] + rr * pw + off[v]) : zero4();
+    for (int v = 0; v < NVEC; ++v) w[rr][v] = ldg16(pg[v] + min(rr, rows - 1) * pw + ((col0 + cl[v]) & (pw - 1)));
   uint4 x[NV][NVEC];
 #pragma unroll
   for (int tt = 0; tt < NV; ++tt) {
-    const int64_t row = tt < nt ? (int64_t)K.perm[t0 + tb + tt] * P.ldx + col0 : -1;
+    const int64_t row = (int64_t)cld(K.perm + t0 + tb + min(tt, nt - 1)) * P.ldx + col0;
 #pragma unroll
-    for (int v = 0; v < NVEC; ++v)
-      x[tt][v] = (row >= 0 && ok[v]) ? ldg16(X + row + v * 64 * EPV + lane * EPV) : zero4();
+    for (int v = 0; v < NVEC; ++v) x[tt][v] = ldg16(X + row + cl[v]);
   }
   static_assert(16 * NV == 32, "one 32-value wave reduction per item");
   float acc[32];
@@ -329,7 +342,10 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int 
     for (int tt = 0; tt < NV; ++tt) {
       float s = 0.0f;
 #pragma unroll
-      for (int v = 0; v < NVEC; ++v) s = dot16(w[rr][v], x[tt][v], s, E());
+      for (int v = 0; v < NVEC; ++v) {
+        const float d = dot16(w[rr][v], x[tt][v], 0.0f, E());
+        s += (lane_ok[v] && pok[v]) ? d : 0.0f;
+      }
       acc[rr * NV + tt] = s;
     }
   const float sum = wave_reduce_scatter32(acc, lane);
@@ -345,7 +361,7 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int 
 // the first of their MFMAs (two memory round trips per item).  The rank
 // groups of a token tile are consecutive items, so the tile's activations
 // are re-read from the L2 that holds them.
-template <class E>
+template <class E, bool WIDE>
 __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int q, int4 d0, int4 d1, int local,
                                             int lane) {
   typedef typename E::T T;
@@ -362,32 +378,39 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
   const int nt = min(16, n - tb);
   const int li = lane & 15, qq = lane >> 4;
   const int col0 = q * kKSlice;
-  const int ncols = min(kKSlice, P.d_in - col0);
+  const int ncols = min(kKSlice, P.d_in - col0);  // a multiple of 8
   const int pw = 1 << K.pw_log2;
   const int slot = cld(P.a_indptr + a) + g * ((P.d_in + pw - 1) >> K.pw_log2);
-  const bool one_page = pw >= kKSlice;
-  const T* pg1 = one_page ? page_ptr<E>(K, cld(P.a_pages + slot + (col0 >> K.pw_log2))) : nullptr;
-  const bool rok = g * 16 + li < r;
+  bool ok1 = true;
+  const T* pg1 = WIDE ? page_base<E>(K, cld(P.a_pages + slot + (col0 >> K.pw_log2)), ok1) : nullptr;
+  // unconditional in-bounds loads (see shrink_valu): rank rows past r re-read
+  // the group's last row (their outputs are never stored), tokens past the
+  // tile the tile's first token (never stored); K positions past d_in are
+  // zeroed at the product
+  const int lrow = min(li, r - g * 16 - 1);
   const T* X = reinterpret_cast<const T*>(P.X);
-  const int64_t xrow = li < nt ? (int64_t)K.perm[t0 + tb + li] * P.ldx : -1;
+  const int64_t xrow = (int64_t)K.perm[t0 + tb + (li < nt ? li : 0)] * P.ldx;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
   for (int st0 = 0; st0 < NSTEP; st0 += SIF) {
     uint4 av[SIF], xv[SIF];
+    bool okv[SIF];
 #pragma unroll
     for (int j = 0; j < SIF; ++j) {
       const int c = (st0 + j) * STEP + qq * EPV;
-      const bool ok = c < ncols;
-      const int col = col0 + c;
-      av[j] = zero4();
-      if (ok && rok) {
-        const T* pg = one_page ? pg1 : page_ptr<E>(K, P.a_pages[slot + (col >> K.pw_log2)]);
-        if (pg != nullptr) av[j] = ldg16(pg + li * pw + (col & (pw - 1)));
+      const int col = col0 + min(c, ncols - EPV);
+      okv[j] = c < ncols;
+      const T* pg = pg1;
+      if constexpr (!WIDE) {
+        bool okp;
+        pg = page_base<E>(K, P.a_pages[slot + (col >> K.pw_log2)], okp);
+        okv[j] = okv[j] && okp;
       }
-      xv[j] = (ok && xrow >= 0) ? ldg16(X + xrow + col) : zero4();
+      av[j] = ldg16(pg + lrow * pw + (col & (pw - 1)));
+      xv[j] = ldg16(X + xrow + col);
     }
 #pragma unroll
-    for (int j = 0; j < SIF; ++j) mma(acc, av[j], xv[j], E());
+    for (int j = 0; j < SIF; ++j) mma(acc, (okv[j] && ok1) ? av[j] : zero4(), xv[j], E());
   }
   const int k0 = g * 16 + qq * 4;
   if (li < nt) {
@@ -398,7 +421,9 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
   }
 }
 
-template <class E>
+// WIDE: pages hold at least one whole 512-column slice, so every page
+// lookup of an item is wave-uniform; chosen by the host from the page width.
+template <class E, bool WIDE>
 __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArgs) {
   const KArgs& K = kernel_args();
   const int S = cld(K.counts + kCountS);
@@ -416,7 +441,7 @@ __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArg
     const int u = rem - q * Um;
     const int s = cld(K.shr_item_m + u);
     const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
-    shrink_mfma<E>(K, K.p[p], q, d0, d1, u - d1.y, lane);
+    shrink_mfma<E, WIDE>(K, K.p[p], q, d0, d1, u - d1.y, lane);
   }
   total = 0;
   for (int p = 0; p < K.np; ++p) total += K.p[p].nq * Uv;
@@ -427,7 +452,7 @@ __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArg
     const int u = rem - q * Uv;
     const int s = cld(K.shr_item_v + u);
     const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
-    shrink_valu<E>(K, K.p[p], q, d0, d1, u - d1.y, lane);
+    shrink_valu<E, WIDE>(K, K.p[p], q, d0, d1, u - d1.y, lane);
   }
 }
 
@@ -853,7 +878,8 @@ __device__ __forceinline__ void store4(float* p, const float (&y)[4]) {
 // token (one 8- or 16-byte Y access).
 template <class E, int NKS, bool WIDE>
 __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P, int j0, int jend, int wc, int a,
-                                                 int r, int t0, int nt, float scale, const float* vs, int lane) {
+                                                 int r, int t0, int nt, float scale, float* vs, float* cw, int voff,
+                                                 int tb, int lane) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
   constexpr int KSTEP = 4 * EPV;
@@ -871,8 +897,23 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
   const int bbase = cld(P.b_indptr + a);
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
   T* Y = reinterpret_cast<T*>(P.Y);
-  // lanes of tokens past the tile read the tile's first row (never stored)
-  const int64_t row = K.perm[t0 + (li < nt ? li : 0)];
+  // Y_base / Y go through LDS in token rows: the MFMA result (a lane holds 4
+  // columns of one token) is written to the wave's LDS rows and read back so
+  // that each lane reads and writes one 16-byte chunk of a token row, a
+  // quarter-wave covering whole 128-byte row segments (the MFMA layout itself
+  // would touch 16 rows per quarter-wave with 8-byte accesses).
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = PART / EPC;           // chunks per token row of a part
+  constexpr int TPR = 64 / CPR;             // token rows per round of the wave
+  constexpr int ROUNDS = 16 / TPR;
+  constexpr int LDC = PART + 4;             // LDS row stride (floats)
+  const int ch = lane % CPR;
+  int64_t yrow[ROUNDS];
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    const int tk = rd * TPR + lane / CPR;
+    yrow[rd] = K.perm[t0 + min(tk, nt - 1)];  // tokens past the tile: the last one (never stored)
+  }
   const int G = rank_groups(r);
   // page of each of this lane's K steps; a step past the last rank group
   // reads the last group and is zeroed by the rank mask
@@ -883,13 +924,7 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
     const int g = min((ks * KSTEP + qq * EPV) >> 4, G - 1);
     pgk[ks] = page_base<E>(K, one_page ? cld(P.b_pages + bbase + g * ncolB + (j0 >> K.pw_log2)) : 0, okk[ks]);
   }
-  uint4 vv[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    const int k0 = ks * KSTEP + qq * EPV;
-    vv[ks] = (li < nt && k0 < r) ? pack_operand(vs + li * rs + k0, EPV, E()) : zero4();
-  }
-  auto load_part = [&](int part, uint4 (&bv)[CT][NKS], float (&ybv)[CT][4], bool (&okc)[CT][NKS]) {
+  auto load_part = [&](int part, uint4 (&bv)[CT][NKS], uint4 (&ybv)[ROUNDS], bool (&okc)[CT][NKS]) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       // columns past the block are clamped to its last column (never stored)
@@ -905,15 +940,27 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
         bv[ct][ks] = ldg16(pg + (j & (pw - 1)) * 16 + (k0 & 15));
         okc[ct][ks] = ok;
       }
-      const int c4 = min(part * PART + ct * 16 + qq * 4, jend - 4);
-      load4(Yb + row * P.ldyb + j0 + c4, ybv[ct]);
     }
+    const int col = min(part * PART + ch * EPC, jend - EPC);  // jend is a multiple of 8
+#pragma unroll
+    for (int rd = 0; rd < ROUNDS; ++rd) ybv[rd] = ldg16(Yb + yrow[rd] * P.ldyb + j0 + col);
   };
   uint4 bcur[CT][NKS], bnext[CT][NKS];
-  float ycur[CT][4], ynext[CT][4];
+  uint4 ycur[ROUNDS], ynext[ROUNDS];
   bool okcur[CT][NKS], oknext[CT][NKS];
-  const int np = ceil_div_i(jend, PART);
-  load_part(0, bcur, ycur, okcur);
+  const bool active = jend > 0;  // the wave has columns in this item
+  const int np = active ? ceil_div_i(jend, PART) : 0;
+  // the first part's B and Y_base are requested before v is staged, so the
+  // two memory round trips overlap
+  if (active) load_part(0, bcur, ycur, okcur);
+  stage_v_rows<kThreads>(K, P, voff, r, tb, nt, vs, threadIdx.x);
+  __syncthreads();
+  uint4 vv[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int k0 = ks * KSTEP + qq * EPV;
+    vv[ks] = (li < nt && k0 < r) ? pack_operand(vs + li * rs + k0, EPV, E()) : zero4();
+  }
   for (int part = 0; part < np; ++part) {
     if (part + 1 < np) load_part(part + 1, bnext, ynext, oknext);
     f4 acc[CT];
@@ -930,18 +977,36 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
         mma(acc[ct], w, vv[ks], E());
       }
     }
-    if (li < nt) {
+    // C[col][token] -> LDS token rows -> 16-byte chunks of Y rows
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const int c4 = part * PART + ct * 16 + qq * 4;
-        if (c4 < jend) {
-          float y[4];
+    for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f4*>(cw + li * LDC + ct * 16 + qq * 4) = acc[ct];
+    wave_sync();
+    const int colp = part * PART + ch * EPC;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] = ycur[ct][i] + scale * acc[ct][i];
-          store4(Y + row * P.ldy + j0 + c4, y);
+    for (int rd = 0; rd < ROUNDS; ++rd) {
+      const int tk = rd * TPR + lane / CPR;
+      if (tk < nt && colp < jend) {
+        const float* c = cw + tk * LDC + ch * EPC;
+        uint4 out;
+        if constexpr (EPC == 8) {
+          const f4 c0 = *reinterpret_cast<const f4*>(c), c1 = *reinterpret_cast<const f4*>(c + 4);
+          const uint4 yb = ycur[rd];
+          out.x = pack_bf2(bf_lo(yb.x) + scale * c0[0], bf_hi(yb.x) + scale * c0[1]);
+          out.y = pack_bf2(bf_lo(yb.y) + scale * c0[2], bf_hi(yb.y) + scale * c0[3]);
+          out.z = pack_bf2(bf_lo(yb.z) + scale * c1[0], bf_hi(yb.z) + scale * c1[1]);
+          out.w = pack_bf2(bf_lo(yb.w) + scale * c1[2], bf_hi(yb.w) + scale * c1[3]);
+        } else {
+          const f4 c0 = *reinterpret_cast<const f4*>(c);
+          const uint4 yb = ycur[rd];
+          out = make_uint4(__float_as_uint(__uint_as_float(yb.x) + scale * c0[0]),
+                           __float_as_uint(__uint_as_float(yb.y) + scale * c0[1]),
+                           __float_as_uint(__uint_as_float(yb.z) + scale * c0[2]),
+                           __float_as_uint(__uint_as_float(yb.w) + scale * c0[3]));
         }
+        *reinterpret_cast<uint4*>(Y + yrow[rd] * P.ldy + j0 + colp) = out;
       }
     }
+    wave_sync();  // the rows are rewritten by the next part
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
@@ -949,9 +1014,9 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
         bcur[ct][ks] = bnext[ct][ks];
         okcur[ct][ks] = oknext[ct][ks];
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ycur[ct][i] = ynext[ct][i];
     }
+#pragma unroll
+    for (int rd = 0; rd < ROUNDS; ++rd) ycur[rd] = ynext[rd];
   }
 }
 
@@ -960,7 +1025,7 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
 // columns [w*wc, (w+1)*wc) of the item.
 template <class E, bool WIDE>
 __device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int jb, int wc, int4 d0, int4 d1,
-                                            int local, float* vs, int wave, int lane) {
+                                            int local, float* vs, float* cw, int wave, int lane) {
   constexpr int KSTEP = 4 * E::kEpv;
   constexpr int MAXKS = LORA_MAX_RANK / KSTEP;
   const int a = d0.x, r = d0.y;
@@ -968,17 +1033,14 @@ __device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int 
   const int t0 = d0.z + tb;
   const int nt = min(kMfmaExpandTokens, d0.w - tb);
   const float scale = __int_as_float(d1.w) / (float)r;
-  stage_v_rows<kThreads>(K, P, d1.x, r, tb, nt, vs, threadIdx.x);
-  __syncthreads();
   const int j0 = (jb * kWaves + wave) * wc;
-  const int jend = min(wc, P.d_out - j0);
-  if (jend > 0) {
-    // K steps past the rank are skipped inside the body, so two variants
-    // cover every rank
-    const int nks = ceil_div_i(r, KSTEP);
-    if (nks <= MAXKS / 2) expand_mfma_body<E, MAXKS / 2, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
-    else expand_mfma_body<E, MAXKS, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, lane);
-  }
+  const int jend = min(wc, P.d_out - j0);  // <= 0: no columns for this wave (it still stages v)
+  // K steps past the rank are skipped inside the body, so two variants cover
+  // every rank; the choice is the same for the whole block (one segment)
+  const int nks = ceil_div_i(r, KSTEP);
+  if (nks <= MAXKS / 2)
+    expand_mfma_body<E, MAXKS / 2, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
+  else expand_mfma_body<E, MAXKS, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
   __syncthreads();  // the rows are restaged by the block's next item
 }
 
@@ -1009,7 +1071,9 @@ __device__ __forceinline__ void expand_copy(const KArgs& K, const KProj& P, int 
 template <class E, bool WIDE>
 __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArgs) {
   const KArgs& K = kernel_args();
-  __shared__ __attribute__((aligned(16))) float vs_all[kWaves][kMfmaExpandTokens * LORA_MAX_RANK];
+  // per-wave rows (MBGMV staging, MBGMM output tiles) and the block's staged
+  // v tile of an MBGMM item
+  __shared__ __attribute__((aligned(16))) float vs_all[kWaves + 1][kMfmaExpandTokens * LORA_MAX_RANK];
   const int S = cld(K.counts + kCountS);
   const int t_valid = cld(K.counts + kCountTValid);
   const int Um = S > 0 ? cld(K.counts + kCountExpandMfma) : 0;
@@ -1041,7 +1105,7 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
       const int u = rem - jb * Um;
       const int s = cld(K.exp_item_m + u);
       const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
-      expand_mfma<E, WIDE>(K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[0], wave, lane);
+      expand_mfma<E, WIDE>(K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[kWaves], vs_all[wave], wave, lane);
     }
   }
   int total = 0;
@@ -1281,8 +1345,14 @@ hipError_t launch_build_segments(const int32_t* ids, int T, int N, const int32_t
 }
 
 hipError_t launch_shrink(const KArgs& K, int dtype, int grid, hipStream_t stream) {
-  if (dtype == LORA_DTYPE_BF16) shrink_kernel<Bf16><<<grid, kThreads, 0, stream>>>(K);
-  else shrink_kernel<F32><<<grid, kThreads, 0, stream>>>(K);
+  const bool wide = (1 << K.pw_log2) >= kKSlice;
+  if (dtype == LORA_DTYPE_BF16) {
+    if (wide) shrink_kernel<Bf16, true><<<grid, kThreads, 0, stream>>>(K);
+    else shrink_kernel<Bf16, false><<<grid, kThreads, 0, stream>>>(K);
+  } else {
+    if (wide) shrink_kernel<F32, true><<<grid, kThreads, 0, stream>>>(K);
+    else shrink_kernel<F32, false><<<grid, kThreads, 0, stream>>>(K);
+  }
   return launch_err();
 }
 
@@ -1302,10 +1372,10 @@ hipError_t launch_expand(const KArgs& K, int dtype, int grid, hipStream_t stream
 hipError_t occupancy(int dtype, int* shrink_blocks, int* expand_blocks) {
   hipError_t e;
   if (dtype == LORA_DTYPE_BF16) {
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(shrink_blocks, shrink_kernel<Bf16>, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(shrink_blocks, shrink_kernel<Bf16, true>, kThreads, 0);
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(expand_blocks, expand_kernel<Bf16, true>, kThreads, 0);
   } else {
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(shrink_blocks, shrink_kernel<F32>, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(shrink_blocks, shrink_kernel<F32, true>, kThreads, 0);
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(expand_blocks, expand_kernel<F32, true>, kThreads, 0);
   }
   return e;
