@@ -383,13 +383,24 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
   const int slot = cld(P.a_indptr + a) + g * ((P.d_in + pw - 1) >> K.pw_log2);
   bool ok1 = true;
   const T* pg1 = WIDE ? page_base<E>(K, cld(P.a_pages + slot + (col0 >> K.pw_log2)), ok1) : nullptr;
-  // unconditional in-bounds loads (see shrink_valu): rank rows past r re-read
-  // the group's last row (their outputs are never stored), tokens past the
-  // tile the tile's first token (never stored); K positions past d_in are
-  // zeroed at the product
-  const int lrow = min(li, r - g * 16 - 1);
+  // Operands are loaded row-contiguously -- lane l reads chunk l & 3 of row
+  // l >> 2, so a quarter-wave covers 4 rows x 64 contiguous bytes -- and
+  // moved to the MFMA layout (lane L holds chunk L >> 4 of row L & 15) with a
+  // cross-lane permute.  Loaded in the MFMA layout directly, every
+  // quarter-wave would touch 16 rows (16 cache lines per 256 bytes).
+  // Loads are unconditional and in bounds (see shrink_valu): rank rows past
+  // r re-read the group's last row (their outputs are never stored), tokens
+  // past the tile its first token (never stored); K positions past d_in are
+  // zeroed at the product.
+  const int lr = lane >> 2, lk = lane & 3;
+  const int src = ((lane & 15) * 4 + (lane >> 4)) * 4;  // byte address of the source lane
+  const int lrow = min(lr, r - g * 16 - 1);
   const T* X = reinterpret_cast<const T*>(P.X);
-  const int64_t xrow = (int64_t)K.perm[t0 + tb + (li < nt ? li : 0)] * P.ldx;
+  const int64_t xrow = (int64_t)K.perm[t0 + tb + (lr < nt ? lr : 0)] * P.ldx;
+  auto permute = [src](uint4 v) {
+    return make_uint4(__builtin_amdgcn_ds_bpermute(src, (int)v.x), __builtin_amdgcn_ds_bpermute(src, (int)v.y),
+                      __builtin_amdgcn_ds_bpermute(src, (int)v.z), __builtin_amdgcn_ds_bpermute(src, (int)v.w));
+  };
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
   for (int st0 = 0; st0 < NSTEP; st0 += SIF) {
@@ -397,20 +408,30 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
     bool okv[SIF];
 #pragma unroll
     for (int j = 0; j < SIF; ++j) {
-      const int c = (st0 + j) * STEP + qq * EPV;
-      const int col = col0 + min(c, ncols - EPV);
-      okv[j] = c < ncols;
-      const T* pg = pg1;
+      const int cl = (st0 + j) * STEP + lk * EPV;       // this lane's load chunk
+      const int col = col0 + min(cl, ncols - EPV);
+      okv[j] = (st0 + j) * STEP + qq * EPV < ncols;     // the chunk it holds after the permute
       if constexpr (!WIDE) {
-        bool okp;
-        pg = page_base<E>(K, P.a_pages[slot + (col >> K.pw_log2)], okp);
-        okv[j] = okv[j] && okp;
+        // the page of the chunk this lane will hold decides its mask; the
+        // page of the chunk it loads, the address
+        bool okh, okl;
+        page_base<E>(K, P.a_pages[slot + ((col0 + min((st0 + j) * STEP + qq * EPV, ncols - EPV)) >> K.pw_log2)], okh);
+        okv[j] = okv[j] && okh;
+        const T* pl = page_base<E>(K, P.a_pages[slot + (col >> K.pw_log2)], okl);
+        av[j] = ldg16(pl + lrow * pw + (col & (pw - 1)));
+      } else {
+        av[j] = ldg16(pg1 + lrow * pw + (col & (pw - 1)));
       }
-      av[j] = ldg16(pg + lrow * pw + (col & (pw - 1)));
       xv[j] = ldg16(X + xrow + col);
     }
 #pragma unroll
-    for (int j = 0; j < SIF; ++j) mma(acc, (okv[j] && ok1) ? av[j] : zero4(), xv[j], E());
+    for (int j = 0; j < SIF; ++j) {
+      // permute with every lane active (a permute reads 0 from an inactive
+      // lane), then zero the K positions past d_in with a mask
+      const uint4 ap = permute(av[j]), xp = permute(xv[j]);
+      const uint32_t m = (okv[j] && ok1) ? 0xffffffffu : 0u;
+      mma(acc, make_uint4(ap.x & m, ap.y & m, ap.z & m, ap.w & m), xp, E());
+    }
   }
   const int k0 = g * 16 + qq * 4;
   if (li < nt) {
