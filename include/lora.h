@@ -31,9 +31,10 @@
  *    void*; NULL = the default stream) and never synchronises the device.
  *  - Host-side argument checks run before anything is enqueued; on error the
  *    call returns a negative status and enqueues nothing.  Data-dependent
- *    conditions found on the device (bad ids, bad ranks, page ids outside
- *    the pool) never abort: they are recorded in the segment counters
- *    (see lora_segments_t.counts) and the affected rows keep Y_base.
+ *    conditions found on the device never abort: tokens with bad ids or
+ *    ranks are counted (lora_segments_t.counts) and keep Y_base; a page id
+ *    outside the pool reads as zero weights and sets LORA_FLAG_PAGE_RANGE
+ *    in the counters' flag word.
  *  - No exception crosses this interface.
  *
  * Element types: LORA_DTYPE_BF16 -> X, Y_base, Y and the pool hold bf16;
