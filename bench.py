@@ -45,12 +45,18 @@ TRAFFIC_SUMMARY = "profiles/expand_kernel_bf16.llama7b_decode_T1024.hbm_traffic.
 CALIB_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(root: str = ROOT) -> str:
+    """Hash of the kernel sources with comments and blank space removed, so
+    that a documentation edit does not orphan a measurement."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(root, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
