@@ -303,3 +303,33 @@ def test_excluded_token_at_last_chunk_position():
     ids[5] = -1
     ranks = np.array([16, 8], np.int32)
     check_segments(_segments_gpu(ids, ranks), oracle.segments(ids, ranks))
+
+
+def test_graph_capture_replays_match_eager():
+    """The whole branch (segment build + apply) captured in a HIP graph:
+    every replay, with eager work and synchronisation in between, equals the
+    eager result bit for bit (the library records only kernel launches)."""
+    w = W.make_workload(2, dict(T=300, N=9, ranks_override=[8, 16, 64, 24, 1, 32, 128, 40, 8], page_width=512,
+                                projs=(("a", 2048, 1032), ("b", 1032, 2048))), keep_dense=False)
+    Yref, _ = gpu_apply(w)
+    b = batch.to_device(w)
+    segs = lora.Segments(w.T, w.N)
+    projs = [b.proj(p) for p in range(w.n_projs)]
+    ws = lora.workspace(w.T, w.N, w.n_projs, 2048)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lora.lora_apply(b.ids, segs, w.T, projs, b.adapters, b.pool, ws, side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        lora.lora_apply(b.ids, segs, w.T, projs, b.adapters, b.pool, ws, side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for y in b.Y:
+            y.fill_(7.0)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for p in range(w.n_projs):
+            assert np.array_equal(batch.device_to_host(b.Y[p]), Yref[p]), (rep, p)
