@@ -93,6 +93,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill + decode batch")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (the headline is otherwise the HIP-graph replay of the step)")
     ap.add_argument("--pool-layout", choices=["scattered", "contiguous"], default="scattered",
@@ -426,6 +427,39 @@ def main():
                    "frac_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                    "intensity_flop_per_byte": round(fl / by, 2)}
 
+    # ---------------------------------------------------------- mixed batch
+    # continuous batching: prefill chunks (MBGMM segments) and decode tokens
+    # (MBGMV segments) of 1000 adapters in one lora_apply
+    mixed = None
+    if not args.no_mixed:
+        w5 = W.make_workload(5, keep_dense=False)
+        from heterogeneous_adapters_amd import batch
+        b5 = batch.to_device(w5)
+        s5 = lora.Segments(w5.T, w5.N)
+        ws5 = lora.workspace(w5.T, w5.N, 1, 4096)
+        lora.lora_build_segments(b5.ids, b5.adapters, s5, ws5)
+        for _ in range(3):
+            lora.lora_apply(None, s5, w5.T, b5.projs, b5.adapters, b5.pool, ws5)
+        torch.cuda.synchronize()
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record()
+        for _ in range(args.prefill_steps):
+            lora.lora_apply(None, s5, w5.T, b5.projs, b5.adapters, b5.pool, ws5)
+        m1.record()
+        torch.cuda.synchronize()
+        ms = m0.elapsed_time(m1) / args.prefill_steps
+        by = traffic.algorithmic_bytes(w5.ids, w5.ranks, 4096, 4096, 2)
+        fl = traffic.algorithmic_flops(w5.ids, w5.ranks, 4096, 4096)
+        _, cnt = np.unique(w5.ids, return_counts=True)
+        mixed = {"workload": f"mixed-prefill-decode: {len(w5.seq_lens)} prefill chunks "
+                             f"({int(sum(w5.seq_lens))} tokens) + {W.CONFIGS[5]['ndecode']} decode tokens, "
+                             f"1000 adapters, 4096->4096",
+                 "T": int(w5.T), "segments": int(len(cnt)), "mbgmm_segments": int((cnt >= 16).sum()),
+                 "ms_per_call": round(ms, 4), "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+                 "frac_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+        del b5, w5
+
     out = {
         "metric": "adapter-branch HBM GB/s (decode MBGMV) + TFLOP/s (prefill MBGMM), % roofline",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -452,6 +486,7 @@ def main():
             "split_matches_apply": bool(split_same)}),
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "mixed": mixed,
         "graph_replay": graph,
         "setup_s": round(gen_s, 1),
     }

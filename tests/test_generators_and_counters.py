@@ -109,3 +109,25 @@ def test_page_tables_cover_pool_once():
             G = (ranks + 15) // 16
             assert np.array_equal(np.diff(t.a_indptr), G * ((t.d_in + 127) // 128))
             assert np.array_equal(np.diff(t.b_indptr), G * ((t.d_out + 127) // 128))
+
+
+def test_mixed_batch_ids_structure():
+    """Continuous-batching ids: each prefill chunk is one contiguous run of a
+    single adapter with its drawn length; the decode tail is bounded-Zipf and
+    reproducible from the seed."""
+    ids, ranks, alpha, lens = W.draw_ids_and_ranks(5)
+    c = W.CONFIGS[5]
+    assert len(lens) == c["nchunks"] and all(c["chunk_lo"] <= L <= c["chunk_hi"] for L in lens)
+    assert len(ids) == int(sum(lens)) + c["ndecode"]
+    pos = 0
+    for L in lens:
+        run = ids[pos:pos + L]
+        assert (run == run[0]).all() and 0 <= run[0] < c["N"]
+        pos += L
+    tail = ids[pos:]
+    assert tail.min() >= 0 and tail.max() < c["N"]
+    # the most popular decode adapter is id 0 (bounded Zipf, s = 1.2)
+    counts = np.bincount(tail, minlength=c["N"])
+    assert counts.argmax() == 0
+    ids2, _, _, _ = W.draw_ids_and_ranks(5)
+    assert np.array_equal(ids, ids2)

@@ -141,6 +141,9 @@ PARITY_CASES = {
     "hot_segments": (2, dict(T=700, N=3, ranks_override=[8, 64, 128], page_width=512,
                              projs=(("a", 4096, 1032),))),
     "pw64_contig": (1, dict(T=96, N=5, page_width=64, projs=(("q", 512, 512),))),
+    # continuous batching: prefill chunks (MBGMM) beside decode tokens (MBGMV)
+    "mixed": (5, dict(nchunks=3, chunk_lo=40, chunk_hi=120, ndecode=300, N=50, page_width=512,
+                      projs=(("a", 1024, 1536),))),
 }
 
 

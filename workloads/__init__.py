@@ -50,8 +50,8 @@ LLAMA7B_PROJS: Tuple[Tuple[str, int, int], ...] = (
     ("o_proj", 4096, 4096), ("gate_proj", 4096, 11008), ("up_proj", 4096, 11008),
     ("down_proj", 11008, 4096))
 
-# The five benchmark workloads.  Seeds: workload k uses seed 7 + k (7 is the
-# seed of the [MLSA] LRU simulator run).
+# The benchmark workloads.  Seeds: workload k uses seed 7 + k (7 is the seed
+# of the [MLSA] LRU simulator run).
 CONFIGS: Dict[int, dict] = {
     0: dict(name="tiny-decode-sgmv", phase="decode", T=16, N=4, rank_choices=(8,),
             ids="uniform", projs=(("proj", 256, 256),), layers=1, dtype="f32",
@@ -71,6 +71,16 @@ CONFIGS: Dict[int, dict] = {
     4: dict(name="llama2-7b-decode-step", phase="decode", T=1024, N=1000,
             rank_choices=(8, 16, 32, 64), ids="zipf", zipf_s=1.2,
             projs=LLAMA7B_PROJS, layers=32, dtype="bf16", page_width=4096,
+            scatter=True),
+    # A continuous-batching step (not one of the five): chunked-prefill
+    # segments of new requests next to single decode tokens of running ones
+    # in one batch ([MLSP] "Multi-Size Batched Gather Kernels": MBGMV and
+    # MBGMM segments side by side).  Chunk lengths uniform on
+    # [chunk_lo, chunk_hi], each chunk's adapter uniform over N; decode ids
+    # bounded-Zipf; chunks first, then decode tokens.
+    5: dict(name="mixed-prefill-decode", phase="mixed", nchunks=4, chunk_lo=256, chunk_hi=512,
+            ndecode=1024, N=1000, rank_choices=(8, 16, 32, 64), ids="mixed", zipf_s=1.2,
+            projs=(("q_proj", 4096, 4096),), layers=1, dtype="bf16", page_width=4096,
             scatter=True),
 }
 
@@ -251,6 +261,13 @@ def draw_ids_and_ranks(k: int, cfg: Optional[dict] = None):
         prng = random.Random(seed)
         seq_ad = [prng.randrange(c["N"]) for _ in range(c["nseq"])]
         ids = np.repeat(np.asarray(seq_ad, np.int32), seq_lens)
+    elif c["ids"] == "mixed":
+        lens = nrng.integers(c["chunk_lo"], c["chunk_hi"] + 1, size=c["nchunks"]).astype(np.int64)
+        prng = random.Random(seed)
+        chunk_ad = [prng.randrange(c["N"]) for _ in range(c["nchunks"])]
+        ids = np.concatenate([np.repeat(np.asarray(chunk_ad, np.int32), lens),
+                              zipf_ids(c["ndecode"], c["N"], c["zipf_s"], seed + 1)])
+        seq_lens = lens
     elif c["ids"] == "zipf":
         ids = zipf_ids(c["T"], c["N"], c["zipf_s"], seed)
     else:
