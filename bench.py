@@ -94,6 +94,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill + decode batch")
+    ap.add_argument("--no-padded", action="store_true", help="skip the padded-to-max-rank baseline")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (the headline is otherwise the HIP-graph replay of the step)")
     ap.add_argument("--pool-layout", choices=["scattered", "contiguous"], default="scattered",
@@ -460,6 +461,45 @@ def main():
                  "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
         del b5, w5
 
+    # ---------------------------------------------------------- padded baseline
+    # the cost of padding: the heterogeneous-rank decode batch of 128 adapters
+    # (up + down MLP projections) against the same adapters zero-padded to
+    # rank 64 (a fixed-rank slot layout), through the same kernels; GB/s is
+    # over the unpadded algorithmic bytes for both
+    padded = None
+    if not args.no_padded:
+        from heterogeneous_adapters_amd import batch
+
+        def time_calls(wk):
+            bk = batch.to_device(wk)
+            sk = lora.Segments(wk.T, wk.N)
+            wsk = lora.workspace(wk.T, wk.N, len(bk.projs), 11008)
+            lora.lora_build_segments(bk.ids, bk.adapters, sk, wsk)
+            for _ in range(3):
+                lora.lora_apply(None, sk, wk.T, bk.projs, bk.adapters, bk.pool, wsk)
+            torch.cuda.synchronize()
+            q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            q0.record()
+            for _ in range(args.prefill_steps):
+                lora.lora_apply(None, sk, wk.T, bk.projs, bk.adapters, bk.pool, wsk)
+            q1.record()
+            torch.cuda.synchronize()
+            return q0.elapsed_time(q1) / args.prefill_steps
+
+        w2 = W.make_workload(2)
+        w2p = W.pad_to_rank(w2, 64)
+        ms_h, ms_p = time_calls(w2), time_calls(w2p)
+        by = sum(traffic.algorithmic_bytes(w2.ids, w2.ranks, t.d_in, t.d_out, 2) for t in w2.tables)
+        byp = sum(traffic.algorithmic_bytes(w2p.ids, w2p.ranks, t.d_in, t.d_out, 2) for t in w2p.tables)
+        padded = {"workload": "hetero-rank-decode-mlp: T=512, 128 adapters ranks {8,16,32,64}, Zipf 1.1, "
+                              "up 4096->11008 + down 11008->4096; padded = every adapter zero-padded to rank 64",
+                  "heterogeneous_ms_per_call": round(ms_h, 4), "padded_ms_per_call": round(ms_p, 4),
+                  "padded_over_heterogeneous_time": round(ms_p / ms_h, 3),
+                  "heterogeneous_gbs": round(by / (ms_h * 1e-3) / 1e9, 1),
+                  "padded_gbs_of_unpadded_bytes": round(by / (ms_p * 1e-3) / 1e9, 1),
+                  "padded_bytes_over_unpadded": round(byp / by, 3)}
+        del w2, w2p
+
     out = {
         "metric": "adapter-branch HBM GB/s (decode MBGMV) + TFLOP/s (prefill MBGMM), % roofline",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -487,6 +527,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": prefill,
         "mixed": mixed,
+        "padded_baseline": padded,
         "graph_replay": graph,
         "setup_s": round(gen_s, 1),
     }

@@ -336,3 +336,17 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for p in range(w.n_projs):
             assert np.array_equal(batch.device_to_host(b.Y[p]), Yref[p]), (rep, p)
+
+
+def test_padded_slot_layout_matches_unpadded():
+    """The fixed-rank (padded) layout through the same kernels gives the same
+    Y as the heterogeneous-rank layout, within the bf16 tolerance, and both
+    match the oracle."""
+    w = W.make_workload(2, dict(T=400, N=8, ranks_override=[8, 16, 32, 64, 8, 24, 1, 40], page_width=512,
+                                projs=(("a", 2048, 1536),)))
+    wp = W.pad_to_rank(w, 64)
+    Y, _ = gpu_apply(w)
+    Yp, _ = gpu_apply(wp)
+    ref = W.as_f64(oracle_Y(w, 0), w.dtype)
+    assert rowwise_rel(W.as_f64(Y[0], w.dtype), ref) < TOL["bf16"]
+    assert rowwise_rel(W.as_f64(Yp[0], w.dtype), ref) < TOL["bf16"]

@@ -323,3 +323,20 @@ def test_thread_count_does_not_change_results():
         Y4 = oracle.apply(w.X[p], w.Y_base[p], w.ids, w.ranks, w.alpha, w.tables[p], w.pool,
                           w.page_width, w.dtype, nthreads=4)
         assert np.array_equal(Y1, Y4)
+
+
+def test_zero_padding_to_max_rank_changes_nothing():
+    """A fixed-rank slot layout (every adapter zero-padded to r_max, alpha
+    scaled by r_max / r) computes the same branch: the padded terms are
+    exact zeros and alpha'/r_max equals alpha/r bit for bit (division by a
+    power of two), so the oracle's Y is identical."""
+    w = W.make_workload(2, dict(T=90, N=6, ranks_override=[8, 16, 5, 64, 24, 1], page_width=256,
+                                projs=(("a", 512, 768),), dtype="f32"))
+    wp = W.pad_to_rank(w, 64)
+    assert (wp.ranks == 64).all()
+    y = oracle.apply(w.X[0], w.Y_base[0], w.ids, w.ranks, w.alpha, w.tables[0], w.pool, w.page_width, w.dtype)
+    yp = oracle.apply(wp.X[0], wp.Y_base[0], wp.ids, wp.ranks, wp.alpha, wp.tables[0], wp.pool, wp.page_width,
+                      wp.dtype)
+    assert np.array_equal(y, yp)
+    # and the padded pool really holds more pages (what the layout costs)
+    assert wp.num_pages > w.num_pages

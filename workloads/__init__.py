@@ -331,3 +331,44 @@ def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_bits_to_f32(a).astype(np.float64)
     return np.asarray(a, np.float64)
+
+
+def pad_to_rank(w: Workload, r_max: int, seed: int = 0) -> Workload:
+    """The same adapters stored the way a fixed-rank slot layout stores them:
+    every adapter at rank ``r_max``, A and B zero-filled beyond the adapter's
+    own rank, alpha scaled by r_max / r so that alpha / rank is unchanged
+    ([MLSA] "What vLLM actually gives you" and "Practical Recommendations":
+    slots sized by --max-lora-rank).  Needs the dense A and B (keep_dense)."""
+    if w.A is None or w.B is None:
+        raise ValueError("pad_to_rank needs a workload built with keep_dense=True")
+    if int(w.ranks.max()) > r_max:
+        raise ValueError("an adapter's rank exceeds r_max")
+    N = w.N
+    ranks = np.full(N, r_max, np.int32)
+    alpha = (w.alpha.astype(np.float64) * r_max / w.ranks.astype(np.float64)).astype(np.float32)
+    shapes = [(t.name, t.d_in, t.d_out) for t in w.tables]
+    pw = w.page_width
+    scatter = not all(np.array_equal(t.a_pages, np.sort(t.a_pages)) for t in w.tables)
+    tables, num_pages = plan_tables(ranks, shapes, pw, scatter, seed)
+    store_t = w.pool.dtype
+    fill = BF16_NAN if w.dtype == "bf16" else np.float32(np.nan)
+    pool = np.full((num_pages, PAGE_ROWS * pw), fill, dtype=store_t)
+    As, Bs = [], []
+    for p, (_, d_in, d_out) in enumerate(shapes):
+        tb = tables[p]
+        Ap, Bp = [], []
+        for a in range(N):
+            r = int(w.ranks[a])
+            Aa = np.zeros((d_in, r_max), store_t)
+            Aa[:, :r] = w.A[p][a]
+            Ba = np.zeros((r_max, d_out), store_t)
+            Ba[:r, :] = w.B[p][a]
+            pool[tb.a_pages[tb.a_indptr[a]:tb.a_indptr[a + 1]]] = pack_a_pages(Aa, pw, fill)
+            pool[tb.b_pages[tb.b_indptr[a]:tb.b_indptr[a + 1]]] = pack_b_pages(Ba, pw, fill)
+            Ap.append(Aa)
+            Bp.append(Ba)
+        As.append(Ap)
+        Bs.append(Bp)
+    return Workload(cfg=w.cfg, name=w.name + f"-padded-r{r_max}", dtype=w.dtype, T=w.T, N=N, ids=w.ids,
+                    ranks=ranks, alpha=alpha, page_width=pw, tables=tables, num_pages=num_pages, pool=pool,
+                    X=w.X, Y_base=w.Y_base, A=As, B=Bs, seq_lens=w.seq_lens)
