@@ -120,6 +120,11 @@ def groups_for(n_layers, names, mode):
     return out
 
 
+def log(msg: str) -> None:
+    """Progress on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def _read_csv(path):
     import csv
     with open(path, newline="") as f:
@@ -199,6 +204,7 @@ def main():
 
     torch.cuda.set_device(0)
     dev = "cuda"
+    log("generating the decode-step workload on the device")
     t_gen = time.perf_counter()
     dw = make_device_workload(4, dev, overrides=dict(scatter=args.pool_layout == "scattered"))
     T, N = dw.T, dw.N
@@ -221,17 +227,15 @@ def main():
     ws_ptr, ws_n = ctypes.c_void_p(ws.data_ptr()), ws.numel()
     gen_s = time.perf_counter() - t_gen
 
-    # algorithmic bytes / flops per call and per step
+    # algorithmic bytes / flops per call and per step; projections of a call
+    # that read one activation tensor (q/k/v, gate/up) count it once
     e = 2
-    call_bytes, call_flops = [], []
-    for g in groups:
-        bsum = fsum = 0
-        for i in g:
-            t = dw.tables[i]
-            bsum += traffic.algorithmic_bytes(dw.ids, dw.ranks, t.d_in, t.d_out, e)
-            fsum += traffic.algorithmic_flops(dw.ids, dw.ranks, t.d_in, t.d_out)
-        call_bytes.append(bsum)
-        call_flops.append(fsum)
+    call_split = [traffic.group_split_bytes(dw.ids, dw.ranks, [(dw.tables[i].d_in, dw.tables[i].d_out,
+                                                                dw.X[i].data_ptr()) for i in g], e)
+                  for g in groups]
+    call_bytes = [sum(sp) for sp in call_split]
+    call_flops = [sum(traffic.algorithmic_flops(dw.ids, dw.ranks, dw.tables[i].d_in, dw.tables[i].d_out) for i in g)
+                  for g in groups]
     step_bytes = sum(call_bytes)
     step_flops = sum(call_flops)
 
@@ -270,6 +274,7 @@ def main():
     if seg["flags"] != 0:
         raise RuntimeError(f"device flags {seg['flags']}")
 
+    log("eager steps timed; per-kernel leg")
     # per-kernel leg: the same groups through lora_shrink / lora_expand (the
     # two launches lora_apply makes, same grid), HIP events around each
     # launch on the library's stream; Y must come out bit-identical
@@ -296,6 +301,7 @@ def main():
     exp_ms = np.array([[ev[1].elapsed_time(ev[2]) for ev in row] for row in kev]).mean(axis=0)
     del vbuf
 
+    log("graph capture and replay")
     # The headline step: the same step captured once in a HIP graph and
     # replayed (a decode step is replayed, not re-launched, in serving; the
     # graph holds only kernel nodes).  Every warm-up replay is checked bit for
@@ -351,8 +357,7 @@ def main():
     mean_call_ms = call_ms.mean(axis=0)
     kernels = {}
     for kname, ms_g, part in (("shrink_kernel<Bf16>", shr_ms, 0), ("expand_kernel<Bf16, true>", exp_ms, 1)):
-        kb = [sum(traffic.split_bytes(dw.ids, dw.ranks, dw.tables[i].d_in, dw.tables[i].d_out, e)[part]
-                  for i in g) for g in groups]
+        kb = [sp[part] for sp in call_split]
         gb = float(np.sum(kb) / (ms_g.sum() * 1e-3) / 1e9)
         kernels[kname] = {"launches_per_step": len(groups), "mean_launch_us": round(float(ms_g.mean()) * 1e3, 2),
                           "algorithmic_bytes_per_launch": int(np.mean(kb)), "gbs": round(gb, 1),
@@ -364,6 +369,7 @@ def main():
                 "algorithmic_bytes_per_launch": dom["algorithmic_bytes_per_launch"],
                 "launches_per_step": len(groups)}
 
+    log("CPU oracle baseline")
     # ---------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -385,11 +391,12 @@ def main():
                 ref = oracle.apply(Xh, Ybh, dw.ids, dw.ranks, dw.alpha, htabs[j], hpool, dw.page_width, "bf16",
                                    nthreads=threads)
                 spent += time.perf_counter() - c0
-                t = dw.tables[i]
-                done_bytes += traffic.algorithmic_bytes(dw.ids, dw.ranks, t.d_in, t.d_out, e)
                 got = W.as_f64(tensor_bits(Y[i]), "bf16")
                 rf = W.as_f64(ref, "bf16")
                 worst = max(worst, float((np.abs(got - rf).max(axis=1) / np.abs(rf).max(axis=1)).max()))
+            # the layer's algorithmic bytes, a shared activation counted once (as for the GPU)
+            done_bytes += sum(traffic.group_split_bytes(dw.ids, dw.ranks, [(dw.tables[i].d_in, dw.tables[i].d_out,
+                                                                           dw.X[i].data_ptr()) for i in idx], e))
             layers += 1
             if spent >= args.cpu_seconds:
                 break
@@ -398,6 +405,7 @@ def main():
                          f"({done_bytes / 1e9:.2f} GB algorithmic, {spent:.1f} s)",
                "parity_max_rowwise_rel_err": float(f"{worst:.3e}")}
 
+    log("prefill leg")
     # ---------------------------------------------------------- prefill
     prefill = None
     if not args.no_prefill:
@@ -428,6 +436,43 @@ def main():
                    "frac_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                    "intensity_flop_per_byte": round(fl / by, 2)}
 
+    log("shared-activation leg")
+    # ---------------------------------------------------------- shared activation
+    # q/k/v of a prefill batch (config 3's 32 sequences, 3 x 4096->4096) in one
+    # call: one X tensor read by all three (the launch walks their shrink items
+    # side by side) against three separate copies of it
+    shared = None
+    if not args.no_prefill:
+        w6 = W.make_workload(3, dict(projs=(("q_proj", 4096, 4096), ("k_proj", 4096, 4096), ("v_proj", 4096, 4096))),
+                             keep_dense=False)
+        from heterogeneous_adapters_amd import batch
+        b6 = batch.to_device(w6)
+        s6 = lora.Segments(w6.T, w6.N)
+        ws6 = lora.workspace(w6.T, w6.N, 3, 4096)
+        lora.lora_build_segments(b6.ids, b6.adapters, s6, ws6)
+        res = {}
+        for mode in ("separate", "shared"):
+            for p in (1, 2):
+                b6.X[p] = b6.X[0] if mode == "shared" else b6.X[0].clone()
+            pj = [b6.proj(p) for p in range(3)]
+            for _ in range(2):
+                lora.lora_apply(None, s6, w6.T, pj, b6.adapters, b6.pool, ws6)
+            torch.cuda.synchronize()
+            x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            x0.record()
+            for _ in range(5):
+                lora.lora_apply(None, s6, w6.T, pj, b6.adapters, b6.pool, ws6)
+            x1.record()
+            torch.cuda.synchronize()
+            res[mode] = x0.elapsed_time(x1) / 5
+        sb = traffic.group_split_bytes(w6.ids, w6.ranks, [(4096, 4096, "x")] * 3, 2)
+        shared = {"workload": f"prefill q/k/v: T={w6.T}, 16 adapters, 3 x 4096->4096 in one call",
+                  "separate_x_ms_per_call": round(res["separate"], 4), "shared_x_ms_per_call": round(res["shared"], 4),
+                  "speedup": round(res["separate"] / res["shared"], 3),
+                  "shared_x_gbs": round(sum(sb) / (res["shared"] * 1e-3) / 1e9, 1)}
+        del b6, w6
+
+    log("mixed-batch leg")
     # ---------------------------------------------------------- mixed batch
     # continuous batching: prefill chunks (MBGMM segments) and decode tokens
     # (MBGMV segments) of 1000 adapters in one lora_apply
@@ -461,6 +506,7 @@ def main():
                  "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
         del b5, w5
 
+    log("padded-baseline leg")
     # ---------------------------------------------------------- padded baseline
     # the cost of padding: the heterogeneous-rank decode batch of 128 adapters
     # (up + down MLP projections) against the same adapters zero-padded to
@@ -526,6 +572,7 @@ def main():
             "split_matches_apply": bool(split_same)}),
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "shared_activation": shared,
         "mixed": mixed,
         "padded_baseline": padded,
         "graph_replay": graph,

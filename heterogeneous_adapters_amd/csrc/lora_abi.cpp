@@ -182,6 +182,15 @@ void fill_common(KArgs& K, const lora_segments_t* s, const lora_pool_t* pool, in
   K.T = s->T;
 }
 
+// Projections of one launch that read the same activations (q/k/v, gate/up
+// of a transformer block): the shrink then walks their items side by side so
+// the shared X rows are re-read from L2 rather than HBM.
+void mark_shared_x(KArgs& K) {
+  K.xshare = K.np > 1;
+  for (int i = 1; i < K.np; ++i)
+    if (K.p[i].X != K.p[0].X || K.p[i].ldx != K.p[0].ldx || K.p[i].d_in != K.p[0].d_in) K.xshare = 0;
+}
+
 lora_status_t run(const KArgs& K, int dtype, bool do_shrink, bool do_expand, hipStream_t stream) {
   const DeviceInfo* d = nullptr;
   if (lora_status_t st = device_info(&d)) return st;
@@ -296,6 +305,7 @@ static lora_status_t run_split(const lora_proj_t* projs, int32_t n_projs, const 
       const int nv = (shrink || v_slices == 0) ? lora_v_slices(p.d_in) : v_slices;
       K.p[i] = make_kproj(p, v[base + i], nv, pool->dtype);
     }
+    mark_shared_x(K);
     if (lora_status_t e = run(K, pool->dtype, shrink, !shrink, static_cast<hipStream_t>(stream))) return e;
   }
   return LORA_OK;
@@ -361,6 +371,7 @@ lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_
       float* v = reinterpret_cast<float*>(vbase + (size_t)i * vpp);
       K.p[i] = make_kproj(projs[base + i], v, lora_v_slices(projs[base + i].d_in), pool->dtype);
     }
+    mark_shared_x(K);
     if (lora_status_t e = run(K, pool->dtype, true, true, st)) return e;
   }
   return LORA_OK;

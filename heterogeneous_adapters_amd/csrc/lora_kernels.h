@@ -41,6 +41,7 @@ struct KArgs {
   int32_t pw_log2;
   int32_t T;
   int32_t np;
+  int32_t xshare;  // every projection of the launch reads the same X (same pointer, ldx, d_in)
 };
 
 struct SegOut {

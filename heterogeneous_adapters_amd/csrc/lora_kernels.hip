@@ -455,11 +455,23 @@ __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArg
   // so the two register footprints never share a loop body.
   int total = 0;
   for (int p = 0; p < K.np; ++p) total += K.p[p].nq * Um;
+  // Item order: projection-major, or -- when every projection of the launch
+  // reads the same X -- projection-minor, so the siblings' items for one
+  // (slice, item) run side by side and their X rows come from L2.
   for (WaveWalk it(total, wave); it.i < it.end; it.i += it.stride) {
-    int rem = it.i, p = 0;
-    while (rem >= K.p[p].nq * Um) { rem -= K.p[p].nq * Um; ++p; }
-    const int q = rem / Um;
-    const int u = rem - q * Um;
+    int p, q, u;
+    if (K.xshare) {
+      p = it.i % K.np;
+      const int rest = it.i / K.np;
+      q = rest / Um;
+      u = rest - q * Um;
+    } else {
+      int rem = it.i;
+      p = 0;
+      while (rem >= K.p[p].nq * Um) { rem -= K.p[p].nq * Um; ++p; }
+      q = rem / Um;
+      u = rem - q * Um;
+    }
     const int s = cld(K.shr_item_m + u);
     const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
     shrink_mfma<E, WIDE>(K, K.p[p], q, d0, d1, u - d1.y, lane);
@@ -467,10 +479,19 @@ __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArg
   total = 0;
   for (int p = 0; p < K.np; ++p) total += K.p[p].nq * Uv;
   for (WaveWalk it(total, wave); it.i < it.end; it.i += it.stride) {
-    int rem = it.i, p = 0;
-    while (rem >= K.p[p].nq * Uv) { rem -= K.p[p].nq * Uv; ++p; }
-    const int q = rem / Uv;
-    const int u = rem - q * Uv;
+    int p, q, u;
+    if (K.xshare) {
+      p = it.i % K.np;
+      const int rest = it.i / K.np;
+      q = rest / Uv;
+      u = rest - q * Uv;
+    } else {
+      int rem = it.i;
+      p = 0;
+      while (rem >= K.p[p].nq * Uv) { rem -= K.p[p].nq * Uv; ++p; }
+      q = rem / Uv;
+      u = rem - q * Uv;
+    }
     const int s = cld(K.shr_item_v + u);
     const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
     shrink_valu<E, WIDE>(K, K.p[p], q, d0, d1, u - d1.y, lane);

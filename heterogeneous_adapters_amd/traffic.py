@@ -20,6 +20,8 @@ Per projection call, with e bytes per activation/weight element:
         + 4*(T + 2*S + 3)                              token/segment metadata
   flops = sum_{valid t} 2*r_{a(t)}*(d_in + d_out)
 Unused page rows/columns and any split-K partial round trip are excluded.
+Projections of one call that read the same activations (q/k/v, gate/up of a
+transformer block) need X once: ``group_split_bytes`` counts it once.
 """
 from __future__ import annotations
 
@@ -83,3 +85,22 @@ def step_totals(ids, ranks, shapes: Sequence[Tuple[int, int]], elem_bytes: int):
         te += e
         tf += algorithmic_flops(ids, ranks, di, do)
     return tb, tf, ts, te
+
+
+def group_split_bytes(ids, ranks, projs, elem_bytes: int) -> Tuple[int, int, int]:
+    """(shrink, expand, metadata) bytes of one call over several projections.
+    projs: sequence of (d_in, d_out, x_key); projections with the same x_key
+    read one activation matrix, counted once."""
+    ids = np.asarray(ids)
+    t_valid = int(_valid(ids, np.asarray(ranks, np.int64)).sum())
+    shrink = expand = meta = 0
+    seen = set()
+    for d_in, d_out, key in projs:
+        s, e, m = split_bytes(ids, ranks, d_in, d_out, elem_bytes)
+        if key in seen:
+            s -= t_valid * d_in * elem_bytes
+        seen.add(key)
+        shrink += s
+        expand += e
+        meta += m
+    return shrink, expand, meta

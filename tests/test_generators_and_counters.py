@@ -131,3 +131,17 @@ def test_mixed_batch_ids_structure():
     assert counts.argmax() == 0
     ids2, _, _, _ = W.draw_ids_and_ranks(5)
     assert np.array_equal(ids, ids2)
+
+
+def test_group_bytes_count_a_shared_activation_once():
+    """q/k/v of one call reading one X: the group's shrink bytes hold X once,
+    everything else (weights, outputs) per projection."""
+    ids = np.array([0, 1, 1, 2, -1, 0], np.int32)
+    ranks = np.array([8, 16, 64], np.int32)
+    per = [traffic.split_bytes(ids, ranks, 4096, d_out, 2) for d_out in (4096, 1024, 1024)]
+    shared = traffic.group_split_bytes(ids, ranks, [(4096, 4096, "x"), (4096, 1024, "x"), (4096, 1024, "x")], 2)
+    separate = traffic.group_split_bytes(ids, ranks, [(4096, 4096, "a"), (4096, 1024, "b"), (4096, 1024, "c")], 2)
+    t_valid = 5
+    assert separate == tuple(map(sum, zip(*per)))
+    assert shared[0] == separate[0] - 2 * t_valid * 4096 * 2
+    assert shared[1:] == separate[1:]

@@ -350,3 +350,32 @@ def test_padded_slot_layout_matches_unpadded():
     ref = W.as_f64(oracle_Y(w, 0), w.dtype)
     assert rowwise_rel(W.as_f64(Y[0], w.dtype), ref) < TOL["bf16"]
     assert rowwise_rel(W.as_f64(Yp[0], w.dtype), ref) < TOL["bf16"]
+
+
+def test_shared_activation_group_matches_separate_inputs():
+    """q/k/v reading one X tensor: the launch walks the three projections'
+    shrink items side by side (shared X).  The result equals the same
+    projections run with three separate copies of X, bit for bit."""
+    w = W.make_workload(2, dict(T=350, N=7, ranks_override=[8, 16, 64, 24, 32, 8, 128], page_width=512,
+                                projs=(("q", 1536, 1536), ("k", 1536, 512), ("v", 1536, 512))))
+    ys = {}
+    for mode in ("separate", "shared"):
+        b = batch.to_device(w)
+        if mode == "shared":
+            for p in (1, 2):
+                b.X[p] = b.X[0]
+        else:
+            for p in (1, 2):
+                b.X[p] = b.X[0].clone()
+        segs = lora.Segments(w.T, w.N)
+        ws = lora.workspace(w.T, w.N, 3, 1536)
+        lora.lora_apply(b.ids, segs, w.T, [b.proj(p) for p in range(3)], b.adapters, b.pool, ws)
+        torch.cuda.synchronize()
+        ys[mode] = [batch.device_to_host(b.Y[p]) for p in range(3)]
+    for p in range(3):
+        assert np.array_equal(ys["shared"][p], ys["separate"][p])
+    # and the shared run against the oracle (X of projection 0 for all three)
+    Xh = batch.device_to_host(batch.to_device(w).X[0])
+    for p in range(3):
+        ref = oracle.apply(Xh, w.Y_base[p], w.ids, w.ranks, w.alpha, w.tables[p], w.pool, w.page_width, w.dtype)
+        assert rowwise_rel(W.as_f64(ys["shared"][p], w.dtype), W.as_f64(ref, w.dtype)) < TOL["bf16"]

@@ -68,10 +68,12 @@ CONFIGS: Dict[int, dict] = {
             N=16, rank_choices=(8, 16, 32, 64), ids="per-sequence",
             projs=(("proj", 4096, 4096),), layers=1, dtype="bf16",
             page_width=4096, scatter=True),
+    # q/k/v read one input (the attention block's normed hidden state), and
+    # so do gate/up (the MLP's): share_x makes them one activation tensor
     4: dict(name="llama2-7b-decode-step", phase="decode", T=1024, N=1000,
             rank_choices=(8, 16, 32, 64), ids="zipf", zipf_s=1.2,
             projs=LLAMA7B_PROJS, layers=32, dtype="bf16", page_width=4096,
-            scatter=True),
+            scatter=True, share_x=(("q_proj", "k_proj", "v_proj"), ("gate_proj", "up_proj"))),
     # A continuous-batching step (not one of the five): chunked-prefill
     # segments of new requests next to single decode tokens of running ones
     # in one batch ([MLSP] "Multi-Size Batched Gather Kernels": MBGMV and

@@ -113,8 +113,17 @@ def make_device_workload(k: int, device="cuda", overrides=None, chunk_pages: int
                         v[:, :, int(r_ok):] = nan
                         v[:, int(f_ok):, :] = nan
                     pool.index_copy_(0, idx, sub)
-    X = [torch.randn((T, di), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
-         for (_, di, _) in shapes]
+    # share_x: groups of projection names that read one input inside a layer
+    # (q/k/v, gate/up of a transformer block); their X is one tensor
+    share = {n: gi for gi, grp in enumerate(c.get("share_x", ())) for n in grp}
+    nproj = len(c["projs"])
+    xs = {}
+    X = []
+    for i, (n, di, _) in enumerate(shapes):
+        key = (i // nproj, ("g", share[n]) if n in share else ("p", n))
+        if key not in xs:
+            xs[key] = torch.randn((T, di), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+        X.append(xs[key])
     Yb = [torch.randn((T, do), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
           for (_, _, do) in shapes]
     return DeviceWorkload(cfg=k, name=c["name"], dtype="bf16", T=T, N=len(ranks), ids=ids, ranks=ranks,
