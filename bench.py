@@ -31,6 +31,7 @@ tokens, 16 adapters) in TFLOP/s against the bf16 MFMA peak.
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -95,6 +96,7 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill + decode batch")
     ap.add_argument("--no-padded", action="store_true", help="skip the padded-to-max-rank baseline")
+    ap.add_argument("--no-upload", action="store_true", help="skip the pool upload / overlap leg")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (the headline is otherwise the HIP-graph replay of the step)")
     ap.add_argument("--pool-layout", choices=["scattered", "contiguous"], default="scattered",
@@ -513,6 +515,7 @@ def main():
     # rank 64 (a fixed-rank slot layout), through the same kernels; GB/s is
     # over the unpadded algorithmic bytes for both
     padded = None
+    w2 = W.make_workload(2) if not (args.no_padded and args.no_upload) else None
     if not args.no_padded:
         from heterogeneous_adapters_amd import batch
 
@@ -532,7 +535,6 @@ def main():
             torch.cuda.synchronize()
             return q0.elapsed_time(q1) / args.prefill_steps
 
-        w2 = W.make_workload(2)
         w2p = W.pad_to_rank(w2, 64)
         ms_h, ms_p = time_calls(w2), time_calls(w2p)
         by = sum(traffic.algorithmic_bytes(w2.ids, w2.ranks, t.d_in, t.d_out, 2) for t in w2.tables)
@@ -544,7 +546,108 @@ def main():
                   "heterogeneous_gbs": round(by / (ms_h * 1e-3) / 1e9, 1),
                   "padded_gbs_of_unpadded_bytes": round(by / (ms_p * 1e-3) / 1e9, 1),
                   "padded_bytes_over_unpadded": round(byp / by, 3)}
-        del w2, w2p
+        del w2p
+
+    log("pool-upload leg")
+    # ------------------------------------------------------------ pool upload
+    # the pool manager's miss path on the same 128 adapters: every adapter's
+    # pages from pinned host memory into an empty device pool (cache
+    # admission, page assignment, one transfer per run of consecutive pages),
+    # the same bytes page by page onto scattered page ids, and the upload on
+    # its side stream while lora_apply calls run on the compute stream
+    upload = None
+    if not args.no_upload:
+        from heterogeneous_adapters_amd import batch
+        from heterogeneous_adapters_amd.pool import ManagedPool, host_tier_from_pool
+        hp = torch.from_numpy(np.ascontiguousarray(w2.pool).view(np.int16)).view(torch.bfloat16)
+        tier = host_tier_from_pool(hp, w2.tables, w2.N)
+        ipt = [(t.a_indptr, t.b_indptr) for t in w2.tables]
+        n_pg = int(tier.shape[0])
+        up_bytes = tier.numel() * 2
+        b2 = batch.to_device(w2)
+        s2 = lora.Segments(w2.T, w2.N)
+        ws2 = lora.workspace(w2.T, w2.N, len(b2.projs), 11008)
+        lora.lora_build_segments(b2.ids, b2.adapters, s2, ws2)
+        cur = torch.cuda.current_stream()
+
+        def ev():
+            return torch.cuda.Event(enable_timing=True)
+
+        def upload_alone():
+            mp = ManagedPool(ipt, tier, w2.page_width, n_pg)
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record(mp.upload_stream)
+            mp.ensure(range(w2.N))
+            e1.record(mp.upload_stream)
+            torch.cuda.synchronize()
+            assert mp.misses == w2.N and mp.pages_uploaded == n_pg
+            return e0.elapsed_time(e1), mp
+
+        upload_alone()  # warm-up (first transfers, allocator)
+        t_up, mp = upload_alone()
+        # page by page onto a random permutation of the pool (no runs to merge)
+        perm = np.random.default_rng(0).permutation(n_pg).astype(np.int32)
+        side = torch.cuda.Stream()
+        e0, e1 = ev(), ev()
+        e0.record(side)
+        lora.lora_upload_pages(mp.pool, tier, perm, stream=side)
+        e1.record(side)
+        torch.cuda.synchronize()
+        t_scatter = e0.elapsed_time(e1)
+        assert torch.equal(mp.base[torch.from_numpy(perm[:8].astype(np.int64)).cuda()].cpu().view(torch.int16),
+                           tier[:8].view(torch.int16))
+        del mp
+
+        def applies(k):
+            for _ in range(k):
+                lora.lora_apply(None, s2, w2.T, b2.projs, b2.adapters, b2.pool, ws2)
+
+        applies(3)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        applies(20)
+        e1.record()
+        torch.cuda.synchronize()
+        call_ms = e0.elapsed_time(e1) / 20
+        K = max(20, int(math.ceil(t_up / call_ms)))
+        e0, e1 = ev(), ev()
+        e0.record()
+        applies(K)
+        e1.record()
+        torch.cuda.synchronize()
+        t_apply = e0.elapsed_time(e1)
+        # both: the uploads are enqueued first (on the side stream, after a
+        # common start event), then the calls on the compute stream
+        mp = ManagedPool(ipt, tier, w2.page_width, n_pg)
+        torch.cuda.synchronize()
+        t0, ua, a0, a1 = ev(), ev(), ev(), ev()
+        t0.record(cur)
+        mp.upload_stream.wait_event(t0)
+        for a in range(w2.N):
+            hit, pages, _ = mp.cache.admit(a, mp.n_pages(a))
+            lora.lora_upload_pages(mp.pool, tier[mp.offsets[a]:mp.offsets[a + 1]], pages, stream=mp.upload_stream)
+        ua.record(mp.upload_stream)
+        a0.record(cur)
+        applies(K)
+        a1.record(cur)
+        torch.cuda.synchronize()
+        span = max(t0.elapsed_time(ua), t0.elapsed_time(a1))
+        upload = {"workload": f"hetero-rank-decode-mlp adapters: {w2.N} adapters ranks {{8,16,32,64}}, "
+                              f"up 4096->11008 + down 11008->4096, {n_pg} pages of 16x4096 bf16 "
+                              f"({up_bytes / 2 ** 20:.0f} MiB) from pinned host memory",
+                  "upload_ms": round(t_up, 3), "upload_gbs": round(up_bytes / (t_up * 1e-3) / 1e9, 1),
+                  "transfers": int(w2.N),
+                  "page_by_page_ms": round(t_scatter, 3),
+                  "page_by_page_gbs": round(up_bytes / (t_scatter * 1e-3) / 1e9, 1),
+                  "apply_calls": K, "apply_ms_alone": round(t_apply, 3),
+                  "apply_ms_during_upload": round(a0.elapsed_time(a1), 3),
+                  "upload_ms_during_apply": round(t0.elapsed_time(ua), 3),
+                  "both_span_ms": round(span, 3),
+                  "overlap_frac": round((t_up + t_apply - span) / min(t_up, t_apply), 3)}
+        del mp, b2, tier
+    w2 = None
 
     out = {
         "metric": "adapter-branch HBM GB/s (decode MBGMV) + TFLOP/s (prefill MBGMM), % roofline",
@@ -575,6 +678,7 @@ def main():
         "shared_activation": shared,
         "mixed": mixed,
         "padded_baseline": padded,
+        "pool_upload": upload,
         "graph_replay": graph,
         "setup_s": round(gen_s, 1),
     }

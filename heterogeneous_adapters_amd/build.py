@@ -14,7 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 # LORA_LIB_PATH selects another build of the library (tuning experiments)
 LIB_PATH = os.environ.get("LORA_LIB_PATH", os.path.join(HERE, "liblora.so"))
-SOURCES = [os.path.join(CSRC, "lora_kernels.hip"), os.path.join(CSRC, "lora_abi.cpp")]
+SOURCES = [os.path.join(CSRC, "lora_kernels.hip"), os.path.join(CSRC, "lora_abi.cpp"),
+           os.path.join(CSRC, "lora_pool.cpp")]
 ARCH = os.environ.get("LORA_OFFLOAD_ARCH", "gfx950")
 
 

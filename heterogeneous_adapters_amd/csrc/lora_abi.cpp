@@ -234,6 +234,7 @@ const char* lora_status_string(lora_status_t s) {
     case LORA_ERR_HIP: return "HIP runtime error";
     case LORA_ERR_UNSUPPORTED: return "unsupported dtype, page geometry or projection count";
     case LORA_ERR_ALIGNMENT: return "pointer or leading dimension not 16-byte aligned";
+    case LORA_ERR_POOL_FULL: return "too few evictable pages in the pool";
     default: return "unknown status";
   }
 }

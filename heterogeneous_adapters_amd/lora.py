@@ -50,7 +50,9 @@ class lora_segments_t(ctypes.Structure):
 _lib = None
 EXPORTS = ("lora_status_string", "lora_v_slices", "lora_segments_size", "lora_segments_init",
            "lora_workspace_size", "lora_build_segments", "lora_shrink", "lora_expand", "lora_apply",
-           "lora_validate_tables")
+           "lora_validate_tables", "lora_cache_create", "lora_cache_destroy", "lora_cache_free_pages",
+           "lora_cache_num_resident", "lora_cache_admit", "lora_cache_set_pinned", "lora_cache_release",
+           "lora_cache_lookup", "lora_upload_pages")
 
 
 class LoraError(RuntimeError):
@@ -85,8 +87,21 @@ def lib():
         L.lora_apply.argtypes = [_vp, P(lora_segments_t), _i32, P(lora_proj_t), _i32, P(lora_adapters_t),
                                  P(lora_pool_t), _vp, ctypes.c_size_t, _vp]
         L.lora_validate_tables.argtypes = [_i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
+        L.lora_cache_create.argtypes = [_i32, P(_vp)]
+        L.lora_cache_destroy.argtypes = [_vp]
+        L.lora_cache_destroy.restype = None
+        L.lora_cache_free_pages.argtypes = [_vp]
+        L.lora_cache_free_pages.restype = _i32
+        L.lora_cache_num_resident.argtypes = [_vp]
+        L.lora_cache_num_resident.restype = _i32
+        L.lora_cache_admit.argtypes = [_vp, _i64, _i32, _vp, P(_i32), _vp, _i32, P(_i32)]
+        L.lora_cache_set_pinned.argtypes = [_vp, _i64, _i32]
+        L.lora_cache_release.argtypes = [_vp, _i64]
+        L.lora_cache_lookup.argtypes = [_vp, _i64, _vp, _i32, P(_i32)]
+        L.lora_upload_pages.argtypes = [P(lora_pool_t), _vp, _vp, _i32, _vp]
         for name in ("lora_segments_init", "lora_build_segments", "lora_shrink", "lora_expand",
-                     "lora_apply", "lora_validate_tables"):
+                     "lora_apply", "lora_validate_tables", "lora_cache_create", "lora_cache_admit",
+                     "lora_cache_set_pinned", "lora_cache_release", "lora_cache_lookup", "lora_upload_pages"):
             getattr(L, name).restype = _i32
         _lib = L
     return _lib
@@ -263,6 +278,73 @@ def lora_validate_tables(rank, d_in: int, d_out: int, page_width: int, num_pages
     p = [a.ctypes.data_as(_vp) for a in arrs]
     return int(lib().lora_validate_tables(len(arrs[0]), p[0], d_in, d_out, page_width, num_pages,
                                           p[1], p[2], p[3], p[4]))
+
+
+# ------------------------------------------------- pool manager (lora_pool.h)
+class PageCache:
+    """Resident adapters of a page pool: page allocation and LRU eviction.
+    Host state only; not thread-safe."""
+
+    def __init__(self, num_pages: int):
+        h = _vp()
+        _check("lora_cache_create", lib().lora_cache_create(num_pages, ctypes.byref(h)))
+        self.h, self.num_pages = h, num_pages
+
+    def __del__(self):
+        h, self.h = getattr(self, "h", None), None
+        if h and _lib is not None:
+            _lib.lora_cache_destroy(h)
+
+    @property
+    def free_pages(self) -> int:
+        return int(lib().lora_cache_free_pages(self.h))
+
+    @property
+    def num_resident(self) -> int:
+        return int(lib().lora_cache_num_resident(self.h))
+
+    def admit(self, key: int, n_pages: int, max_evicted: Optional[int] = None):
+        """Returns (hit, pages (int32 numpy), evicted keys (int64 numpy, oldest first))."""
+        import numpy as np
+        max_evicted = self.num_pages if max_evicted is None else max_evicted
+        pages = np.empty(max(n_pages, 1), np.int32)
+        ev = np.empty(max(max_evicted, 1), np.int64)
+        hit, nev = _i32(), _i32()
+        _check("lora_cache_admit", lib().lora_cache_admit(
+            self.h, key, n_pages, pages.ctypes.data_as(_vp), ctypes.byref(hit), ev.ctypes.data_as(_vp),
+            max_evicted, ctypes.byref(nev)))
+        return bool(hit.value), pages[:n_pages], ev[:nev.value]
+
+    def lookup(self, key: int):
+        """Pages of a resident adapter (int32 numpy; empty if not resident),
+        without touching the recency order."""
+        import numpy as np
+        n = _i32()
+        _check("lora_cache_lookup", lib().lora_cache_lookup(self.h, key, None, 0, ctypes.byref(n)))
+        pages = np.empty(max(n.value, 1), np.int32)
+        _check("lora_cache_lookup", lib().lora_cache_lookup(self.h, key, pages.ctypes.data_as(_vp), n.value,
+                                                            ctypes.byref(n)))
+        return pages[:n.value]
+
+    def set_pinned(self, key: int, pinned: bool = True) -> None:
+        _check("lora_cache_set_pinned", lib().lora_cache_set_pinned(self.h, key, int(bool(pinned))))
+
+    def release(self, key: int) -> None:
+        _check("lora_cache_release", lib().lora_cache_release(self.h, key))
+
+
+def lora_upload_pages(pool: Pool, host_src: torch.Tensor, pages, stream=None) -> None:
+    """Copy host_src (n_pages, 16*page_width) into the pool pages listed in
+    ``pages`` (host int32 array), asynchronously on the stream.  host_src
+    should be pinned and must stay alive until the stream has passed the copy."""
+    import numpy as np
+    pg = np.ascontiguousarray(pages, np.int32)
+    if host_src.device.type != "cpu" or not host_src.is_contiguous() or host_src.dtype != pool.base.dtype:
+        raise ValueError("host_src must be a contiguous CPU tensor of the pool's dtype")
+    if host_src.dim() != 2 or host_src.shape[0] != len(pg) or host_src.shape[1] != pool.base.shape[1]:
+        raise ValueError("host_src must hold one pool page per page id")
+    _check("lora_upload_pages", lib().lora_upload_pages(ctypes.byref(pool.c), _ptr(host_src),
+                                                        pg.ctypes.data_as(_vp), len(pg), _stream(stream)))
 
 
 def hip_runtimes_mapped() -> list:

@@ -61,6 +61,7 @@ typedef int32_t lora_status_t;
 #define LORA_ERR_HIP (-5)         /* a HIP runtime call or kernel launch failed */
 #define LORA_ERR_UNSUPPORTED (-6) /* unknown dtype, page geometry, too many projections */
 #define LORA_ERR_ALIGNMENT (-7)   /* pointer or leading dimension not 16-byte aligned */
+#define LORA_ERR_POOL_FULL (-8)   /* too few evictable pages in the pool (lora_pool.h) */
 
 #define LORA_DTYPE_F32 0
 #define LORA_DTYPE_BF16 1

@@ -13,11 +13,11 @@ from heterogeneous_adapters_amd import lora
 from heterogeneous_adapters_amd.build import LIB_PATH
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "lora.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("lora.h", "lora_pool.h")]
 
 
 def header_functions():
-    txt = open(HEADER).read()
+    txt = "\n".join(open(h).read() for h in HEADERS)
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(lora_[a-z_]+)\s*\(", txt, flags=re.M)))
 
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings():
     L = lora.lib()
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert lora.lora_status_string(code) not in ("", "unknown status")
     assert lora.lora_status_string(-99) == "unknown status"
     ks = lora.LORA_KSLICE
