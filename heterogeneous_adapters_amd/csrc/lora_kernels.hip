@@ -745,7 +745,6 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
   const int pw = 1 << K.pw_log2;
   const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
   const int jblk = item.jb * (kValuSubBlocks * SUBW);
-  constexpr bool one_page = ONE_PAGE;  // the column block lies in one page of each group
   // first column this lane owns in each of the item's sub-blocks; a lane past
   // d_out works on the last column (never stored)
   int jc[NP];
