@@ -355,12 +355,14 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int 
     P.v[(int64_t)q * K.v_stride + d1.x + (int64_t)(tb + tt) * r + g * 16 + rr] = sum;
 }
 
-// MBGMM item (one wave): (segment, 16-token tile, rank group g, slice q):
-// C[rank][token] += A^T[rank][col] * X^T[col][token] over the slice's 512
-// columns, one 16x16 tile, with the operands of 8 K steps requested before
-// the first of their MFMAs (two memory round trips per item).  The rank
-// groups of a token tile are consecutive items, so the tile's activations
-// are re-read from the L2 that holds them.
+// MBGMM item (one wave): (segment, kMfmaShrinkTokens-token tile, rank group
+// g, slice q): C[rank][token] += A^T[rank][col] * X^T[col][token] over the
+// slice's 512 columns, as 16x16 MFMA tiles that share each A operand (so A,
+// re-read from L2 for every tile of the segment, is read once per 32 tokens),
+// with the operands of 8 / NTT K steps requested before the first of their
+// MFMAs (four memory round trips per item).  The rank groups of a token tile are
+// consecutive items, so the tile's activations are re-read from the L2 that
+// holds them.
 template <class E, bool WIDE>
 __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int q, int4 d0, int4 d1, int local,
                                             int lane) {
@@ -368,14 +370,15 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
   constexpr int EPV = E::kEpv;
   constexpr int STEP = 4 * EPV;
   constexpr int NSTEP = kKSlice / STEP;
-  constexpr int SIF = 8;
+  constexpr int NTT = kMfmaShrinkTokens / 16;  // 16-token MFMA tiles per item
+  constexpr int SIF = 8 / NTT;                 // K steps in flight: 8 (A + NTT X) operand pairs
   static_assert(NSTEP % SIF == 0, "steps in flight divide the slice");
   const int a = d0.x, r = d0.y, t0 = d0.z, n = d0.w;
   const int G = rank_groups(r);
   const int tt = local / G;
   const int g = local - tt * G;
-  const int tb = tt * 16;
-  const int nt = min(16, n - tb);
+  const int tb = tt * kMfmaShrinkTokens;
+  const int nt = min(kMfmaShrinkTokens, n - tb);
   const int li = lane & 15, qq = lane >> 4;
   const int col0 = q * kKSlice;
   const int ncols = min(kKSlice, P.d_in - col0);  // a multiple of 8
@@ -396,15 +399,19 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
   const int src = ((lane & 15) * 4 + (lane >> 4)) * 4;  // byte address of the source lane
   const int lrow = min(lr, r - g * 16 - 1);
   const T* X = reinterpret_cast<const T*>(P.X);
-  const int64_t xrow = (int64_t)K.perm[t0 + tb + (lr < nt ? lr : 0)] * P.ldx;
+  int64_t xrow[NTT];
+#pragma unroll
+  for (int s = 0; s < NTT; ++s) xrow[s] = (int64_t)K.perm[t0 + tb + (s * 16 + lr < nt ? s * 16 + lr : 0)] * P.ldx;
   auto permute = [src](uint4 v) {
     return make_uint4(__builtin_amdgcn_ds_bpermute(src, (int)v.x), __builtin_amdgcn_ds_bpermute(src, (int)v.y),
                       __builtin_amdgcn_ds_bpermute(src, (int)v.z), __builtin_amdgcn_ds_bpermute(src, (int)v.w));
   };
-  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  f4 acc[NTT];
+#pragma unroll
+  for (int s = 0; s < NTT; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
   for (int st0 = 0; st0 < NSTEP; st0 += SIF) {
-    uint4 av[SIF], xv[SIF];
+    uint4 av[SIF], xv[SIF][NTT];
     bool okv[SIF];
 #pragma unroll
     for (int j = 0; j < SIF; ++j) {
@@ -422,23 +429,30 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
       } else {
         av[j] = ldg16(pg1 + lrow * pw + (col & (pw - 1)));
       }
-      xv[j] = ldg16(X + xrow + col);
+#pragma unroll
+      for (int s = 0; s < NTT; ++s) xv[j][s] = ldg16(X + xrow[s] + col);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < SIF; ++j) {
       // permute with every lane active (a permute reads 0 from an inactive
       // lane), then zero the K positions past d_in with a mask
-      const uint4 ap = permute(av[j]), xp = permute(xv[j]);
+      const uint4 ap = permute(av[j]);
       const uint32_t m = (okv[j] && ok1) ? 0xffffffffu : 0u;
-      mma(acc, make_uint4(ap.x & m, ap.y & m, ap.z & m, ap.w & m), xp, E());
+      const uint4 am = make_uint4(ap.x & m, ap.y & m, ap.z & m, ap.w & m);
+#pragma unroll
+      for (int s = 0; s < NTT; ++s) mma(acc[s], am, permute(xv[j][s]), E());
     }
   }
   const int k0 = g * 16 + qq * 4;
-  if (li < nt) {
-    float* dst = P.v + (int64_t)q * K.v_stride + d1.x + (int64_t)(tb + li) * r + k0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (k0 + i < r) dst[i] = acc[i];
+  for (int s = 0; s < NTT; ++s) {
+    if (s * 16 + li < nt) {
+      float* dst = P.v + (int64_t)q * K.v_stride + d1.x + (int64_t)(tb + s * 16 + li) * r + k0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (k0 + i < r) dst[i] = acc[s][i];
+    }
   }
 }
 
@@ -933,7 +947,7 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
   const int pw = 1 << K.pw_log2;
   const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
   // [j0, j0+wc) is wc-aligned, so it lies in one page of each group when
-  // pw >= wc; always in a WIDE kernel (pw >= 512 >= wc)
+  // pw >= wc; always (wc <= pw is chosen by the caller)
   const bool one_page = WIDE || pw >= wc;
   const int bbase = cld(P.b_indptr + a);
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
@@ -1124,11 +1138,12 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
   float* vs = vs_all[wave];
   // MBGMM items first (whole-block items), then MBGMV items and the copies of
   // rows without an adapter (one wave each); each path walks its own item
-  // list.  The columns per wave of an MBGMM item (64..256) shrink until the
-  // items cover about twice the grid, so a few hot segments still spread
-  // over every compute unit.
+  // list.  The columns per wave of an MBGMM item (64..512, at most the page
+  // width) shrink until the items cover about twice the grid, so a few hot
+  // segments still spread over every compute unit; wide items stage a token
+  // tile's v once for more columns.
   if (Um > 0) {
-    int wc = 256, total = 0;
+    int wc = min(512, 1 << K.pw_log2), total = 0;
     for (;; wc >>= 1) {
       total = 0;
       for (int p = 0; p < K.np; ++p) total += ceil_div_i(K.p[p].d_out, kWaves * wc) * Um;

@@ -33,6 +33,10 @@ constexpr int kValuTokens = 2;            // tokens per MBGMV shrink item
 constexpr int kValuExpandTokens = 4;      // tokens per MBGMV expand item (a chunk of the segment)
 constexpr int kCopyTokens = 8;            // rows per copy item (tokens without an adapter)
 constexpr int kMfmaExpandTokens = 16;     // tokens per MBGMM expand item (one tile)
+#ifndef LORA_MFMA_SHRINK_TOKENS
+#define LORA_MFMA_SHRINK_TOKENS 32
+#endif
+constexpr int kMfmaShrinkTokens = LORA_MFMA_SHRINK_TOKENS;  // tokens per MBGMM shrink item (16-token tiles sharing A)
 constexpr int kProjsPerLaunch = 16;       // projection descriptors per launch
 constexpr int kSegChunk = 1024;           // tokens per segment-builder block
 #ifndef LORA_MFMA_MIN_TOKENS
@@ -61,7 +65,7 @@ LORA_HD inline int shrink_items_valu(int n, int r) {
   return is_mfma_segment(n) ? 0 : rank_groups(r) * ceil_div_i(n, kValuTokens);
 }
 LORA_HD inline int shrink_items_mfma(int n, int r) {
-  return is_mfma_segment(n) ? rank_groups(r) * ceil_div_i(n, 16) : 0;
+  return is_mfma_segment(n) ? rank_groups(r) * ceil_div_i(n, kMfmaShrinkTokens) : 0;
 }
 LORA_HD inline int valu_expand_parts(int r) { return rank_groups(r) == 1 ? 1 : rank_groups(r) == 2 ? 2 : 4; }
 LORA_HD inline int valu_expand_chunks(int n) { return ceil_div_i(n, kValuExpandTokens); }
