@@ -128,6 +128,17 @@ def test_segments_bit_exact_edges(case):
 
 
 # ------------------------------------------------------------------- apply
+def _tile_boundary_ids():
+    """Adapters 0-9 hold exactly 16, 17, 31, 32, 33, 47, 48, 63, 64 and 65
+    tokens (MBGMM segments around the 16- and 32-token tile sizes), adapters
+    10-14 one to three (MBGMV), interleaved by a seeded shuffle."""
+    counts = [16, 17, 31, 32, 33, 47, 48, 63, 64, 65, 1, 2, 3, 1, 2]
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    return np.random.default_rng(11).permutation(ids).astype(np.int32)
+
+
+_TILE_RANKS = [8, 16, 24, 32, 64, 128, 1, 40, 17, 96, 8, 16, 32, 64, 128]
+
 PARITY_CASES = {
     "cfg0": (0, {}),
     "cfg1": (1, {}),
@@ -141,6 +152,12 @@ PARITY_CASES = {
     "hot_segments": (2, dict(T=700, N=3, ranks_override=[8, 64, 128], page_width=512,
                              projs=(("a", 4096, 1032),))),
     "pw64_contig": (1, dict(T=96, N=5, page_width=64, projs=(("q", 512, 512),))),
+    # segment lengths on both sides of the MBGMM tile sizes; page width 256 puts
+    # the fp32 case on the wide kernel with MBGMM items as wide as a page
+    "tile_lengths_bf16": (2, dict(N=15, ranks_override=_TILE_RANKS, ids_override=_tile_boundary_ids(),
+                                  page_width=256, projs=(("a", 1000, 1032), ("b", 1032, 520)))),
+    "tile_lengths_f32": (2, dict(N=15, ranks_override=_TILE_RANKS, ids_override=_tile_boundary_ids(),
+                                 page_width=256, dtype="f32", projs=(("a", 1000, 1032), ("b", 1032, 520)))),
     # continuous batching: prefill chunks (MBGMM) beside decode tokens (MBGMV)
     "mixed": (5, dict(nchunks=3, chunk_lo=40, chunk_hi=120, ndecode=300, N=50, page_width=512,
                       projs=(("a", 1024, 1536),))),
