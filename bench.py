@@ -97,6 +97,11 @@ def parse():
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill + decode batch")
     ap.add_argument("--no-padded", action="store_true", help="skip the padded-to-max-rank baseline")
     ap.add_argument("--no-upload", action="store_true", help="skip the pool upload / overlap leg")
+    ap.add_argument("--no-configs", action="store_true", help="skip the configs 1-2 leg (config 3 still runs)")
+    ap.add_argument("--only", choices=["prefill", "configs"],
+                    help="run only this leg and print its JSON (for profiling one workload)")
+    ap.add_argument("--rotate-bytes", type=float, default=1.0,
+                    help="GB of input/pool copies the configs leg rotates over (more than the 256 MB MALL)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (the headline is otherwise the HIP-graph replay of the step)")
     ap.add_argument("--pool-layout", choices=["scattered", "contiguous"], default="scattered",
@@ -163,8 +168,9 @@ def summarize_profile(dirs, command):
         for (name, ctr), disp in per.items():
             if "neg_kernel" in name:
                 calib[ctr] = (CALIB_BYTES / 1024) / float(np.median(list(disp.values())))
-        lines.append(f"counters (rocprofv3 --pmc), KiB per dispatch as read; calibration: a plain elementwise "
-                     f"copy (torch.neg) of {CALIB_BYTES >> 20} MiB fp32 reads and writes exactly that many bytes")
+        lines.append("counters (rocprofv3 --pmc), per dispatch as read (FETCH_SIZE and WRITE_SIZE in KiB)"
+                     + (f"; calibration: a plain elementwise copy (torch.neg) of {CALIB_BYTES >> 20} MiB fp32 reads "
+                        "and writes exactly that many bytes" if calib else ""))
         for (name, ctr), disp in sorted(per.items()):
             if "lora::" in name or "neg_kernel" in name:
                 vals = np.array(list(disp.values()))
@@ -172,7 +178,13 @@ def summarize_profile(dirs, command):
                              f"max {vals.max():12.1f}  {name[:90]}")
         for ctr, f in sorted(calib.items()):
             lines.append(f"{ctr.lower()}_scale: {f:.4f}")
-        for kname, key in (("shrink_kernel<lora::Bf16>", "shrink"), ("expand_kernel<lora::Bf16, true>", "expand")):
+        # MFMA activity (derived counters MfmaUtil: % of SIMD cycles with the
+        # matrix core busy; MfmaFlopsBF16: 512 x bf16 MFMA ops issued)
+        for (name, ctr), disp in sorted(per.items()):
+            if "lora::" in name and ctr in ("MfmaUtil", "MfmaFlopsBF16"):
+                key = "mfma_util_pct" if ctr == "MfmaUtil" else "mfma_bf16_flops_per_dispatch"
+                lines.append(f"{key} {float(np.mean(list(disp.values()))):.4g}  {name[:90]}")
+        for kname, key in (("shrink_kernel<lora::Bf16, true>", "shrink"), ("expand_kernel<lora::Bf16, true>", "expand")):
             tot, have = 0.0, 0
             for (name, ctr), disp in per.items():
                 if kname in name and ctr in calib:
@@ -185,6 +197,80 @@ def summarize_profile(dirs, command):
                 if key == "expand":
                     lines.append(f"hbm_bytes_per_launch: {tot:.0f}")
     print("\n".join(lines))
+
+
+CONFIG_NAMES = {1: "uniform-rank-decode-q_proj: T=256, 32 adapters rank 16, Zipf 1.1, 4096->4096",
+                2: "hetero-rank-decode-mlp: T=512, 128 adapters ranks {8,16,32,64}, Zipf 1.1, "
+                   "up 4096->11008 + down 11008->4096, scattered pages",
+                3: "prefill-mbgmm: 32 sequences of 128..2048 tokens, 16 adapters ranks {8,16,32,64}, 4096->4096"}
+
+
+def configs_leg(which, steps, rotate_gb):
+    """Configs 1-3 through lora_apply with the timing protocol of a
+    cache-cold run: K device copies of the inputs and the pool (together at
+    least rotate_gb GB, more than the 256 MB MALL) are used in turn, so every
+    call reads its bytes from HBM.  HIP events around every call; the median
+    is reported, and the segment build is timed on its own."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from heterogeneous_adapters_amd import batch, lora, traffic
+
+    out = {}
+    for k in which:
+        w = W.make_workload(k, keep_dense=False)
+        b0 = batch.to_device(w)
+        per_copy = (b0.pool.base.numel() * b0.pool.base.element_size()
+                    + sum(t.numel() * t.element_size() for t in b0.X + b0.Y_base + b0.Y))
+        K = max(1, int(np.ceil(rotate_gb * 1e9 / per_copy)))
+        copies = [b0]
+        for _ in range(K - 1):
+            pool = b0.pool.base.clone()
+            X = [x.clone() for x in b0.X]
+            Yb = [y.clone() for y in b0.Y_base]
+            Y = [torch.empty_like(y) for y in Yb]
+            copies.append(batch.DeviceBatch(b0.T, b0.dtype, b0.ids, b0.adapters, lora.Pool(pool, w.page_width),
+                                            b0.tables, X, Yb, Y))
+        projs = [[c.proj(p) for p in range(w.n_projs)] for c in copies]
+        segs = lora.Segments(w.T, w.N)
+        ws = lora.workspace(w.T, w.N, w.n_projs, max(t.d_in for t in w.tables))
+        seg_ms = []
+        for i in range(steps + 3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lora.lora_build_segments(b0.ids, b0.adapters, segs, ws)
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                seg_ms.append(e0.elapsed_time(e1))
+        n_calls = max(steps, 2 * K)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+        for i in range(K):  # one warm-up pass over every copy
+            c = copies[i % K]
+            lora.lora_apply(None, segs, w.T, projs[i % K], c.adapters, c.pool, ws)
+        torch.cuda.synchronize()
+        for i in range(n_calls):
+            c = copies[i % K]
+            ev[i][0].record()
+            lora.lora_apply(None, segs, w.T, projs[i % K], c.adapters, c.pool, ws)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        by = sum(traffic.algorithmic_bytes(w.ids, w.ranks, t.d_in, t.d_out, 2) for t in w.tables)
+        fl = sum(traffic.algorithmic_flops(w.ids, w.ranks, t.d_in, t.d_out) for t in w.tables)
+        tf = fl / (ms * 1e-3) / 1e12
+        out[str(k)] = {"workload": CONFIG_NAMES[k] + f" (T={w.T})", "copies_rotated": K,
+                       "bytes_rotated_gb": round(K * per_copy / 1e9, 2), "calls": n_calls,
+                       "ms_per_call_median": round(ms, 4), "algorithmic_mb": round(by / 1e6, 1),
+                       "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+                       "frac_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "tflops": round(tf, 2), "frac_bf16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                       "intensity_flop_per_byte": round(fl / by, 2),
+                       "segment_build_us_median": round(float(np.median(seg_ms)) * 1e3, 1)}
+        del copies, projs, b0, w
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -205,6 +291,10 @@ def main():
     from heterogeneous_adapters_amd import lora, traffic
 
     torch.cuda.set_device(0)
+    if args.only:
+        which = [3] if args.only == "prefill" else [1, 2, 3]
+        print(json.dumps({"configs": configs_leg(which, args.prefill_steps, args.rotate_bytes)}), flush=True)
+        return
     dev = "cuda"
     log("generating the decode-step workload on the device")
     t_gen = time.perf_counter()
@@ -407,36 +497,16 @@ def main():
                          f"({done_bytes / 1e9:.2f} GB algorithmic, {spent:.1f} s)",
                "parity_max_rowwise_rel_err": float(f"{worst:.3e}")}
 
-    log("prefill leg")
-    # ---------------------------------------------------------- prefill
-    prefill = None
-    if not args.no_prefill:
-        del projs, arrays
-        w3 = W.make_workload(3, keep_dense=False)
-        from heterogeneous_adapters_amd import batch
-        b3 = batch.to_device(w3)
-        s3 = lora.Segments(w3.T, w3.N)
-        ws3 = lora.workspace(w3.T, w3.N, 1, 4096)
-        lora.lora_build_segments(b3.ids, b3.adapters, s3, ws3)
-        for _ in range(3):
-            lora.lora_apply(None, s3, w3.T, b3.projs, b3.adapters, b3.pool, ws3)
-        torch.cuda.synchronize()
-        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        p0.record()
-        for _ in range(args.prefill_steps):
-            lora.lora_apply(None, s3, w3.T, b3.projs, b3.adapters, b3.pool, ws3)
-        p1.record()
-        torch.cuda.synchronize()
-        ms = p0.elapsed_time(p1) / args.prefill_steps
-        fl = traffic.algorithmic_flops(w3.ids, w3.ranks, 4096, 4096)
-        by = traffic.algorithmic_bytes(w3.ids, w3.ranks, 4096, 4096, 2)
-        tf = fl / (ms * 1e-3) / 1e12
-        prefill = {"workload": f"prefill-mbgmm: 32 sequences, T={w3.T}, 16 adapters, 4096->4096",
-                   "ms_per_call": round(ms, 4), "tflops": round(tf, 2),
-                   "frac_bf16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                   "gbs": round(by / (ms * 1e-3) / 1e9, 1),
-                   "frac_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                   "intensity_flop_per_byte": round(fl / by, 2)}
+    log("configs leg (configs 1-3, cache-cold rotation)")
+    # ---------------------------------------------------------- configs 1-3
+    # the small benchmark workloads, each rotated over >= 1 GB of copies so
+    # its bytes come from HBM; config 3 is the prefill (MBGMM) line
+    prefill, configs = None, None
+    del projs, arrays
+    which = ([] if args.no_configs else [1, 2]) + ([] if args.no_prefill else [3])
+    if which:
+        configs = configs_leg(which, args.prefill_steps, args.rotate_bytes)
+        prefill = configs.get("3")
 
     log("shared-activation leg")
     # ---------------------------------------------------------- shared activation
@@ -675,6 +745,7 @@ def main():
             "split_matches_apply": bool(split_same)}),
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "configs": configs,
         "shared_activation": shared,
         "mixed": mixed,
         "padded_baseline": padded,
