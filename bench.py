@@ -496,6 +496,27 @@ def main():
                "sample": f"{layers} of {nl} layers x 7 projections, all {T} tokens "
                          f"({done_bytes / 1e9:.2f} GB algorithmic, {spent:.1f} s)",
                "parity_max_rowwise_rel_err": float(f"{worst:.3e}")}
+        # the small workloads on all threads and on one (best of 3; configs 2
+        # and 3 on one thread: a single run), over the same algorithmic bytes
+        per_cfg = {}
+        for k in (0, 1, 2, 3):
+            wk = W.make_workload(k, keep_dense=False)
+            by = sum(traffic.algorithmic_bytes(wk.ids, wk.ranks, t.d_in, t.d_out, 2 if wk.dtype == "bf16" else 4)
+                     for t in wk.tables)
+            res = {}
+            for nth in (threads, 1):
+                best = float("inf")
+                for _ in range(1 if (k >= 2 and nth == 1) else 3):
+                    c0 = time.perf_counter()
+                    for p in range(wk.n_projs):
+                        oracle.apply(wk.X[p], wk.Y_base[p], wk.ids, wk.ranks, wk.alpha, wk.tables[p], wk.pool,
+                                     wk.page_width, wk.dtype, nthreads=nth)
+                    best = min(best, time.perf_counter() - c0)
+                res[nth] = best
+            per_cfg[str(k)] = {"ms": round(res[threads] * 1e3, 2), "gbs": round(by / res[threads] / 1e9, 3),
+                               "ms_1_thread": round(res[1] * 1e3, 2), "gbs_1_thread": round(by / res[1] / 1e9, 3)}
+            del wk
+        cpu["configs"] = per_cfg
 
     log("configs leg (configs 1-3, cache-cold rotation)")
     # ---------------------------------------------------------- configs 1-3

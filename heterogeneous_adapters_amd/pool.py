@@ -52,6 +52,7 @@ class ManagedPool:
         self.tables = [(i32(a_ip), i32(a_pg), i32(b_ip), i32(b_pg))
                        for (a_ip, b_ip), (a_pg, b_pg) in zip(self.indptrs, self.host_pages)]
         self.upload_stream = torch.cuda.Stream(device=device)
+        self.pinned = set()  # adapters pinned by ensure() and not yet unpinned
         self.hits = self.misses = self.evictions = self.pages_uploaded = 0
 
     def n_pages(self, a: int) -> int:
@@ -73,22 +74,37 @@ class ManagedPool:
         ``compute_stream`` (it may still read the evicted pages)."""
         compute_stream = compute_stream or torch.cuda.current_stream()
         want = [int(a) for a in dict.fromkeys(int(x) for x in adapters)]
-        missed, plan, evicted_any = [], [], False
         for a in want:
             if not 0 <= a < self.N:
                 raise ValueError(f"adapter {a} outside 0..{self.N - 1}")
-            hit, pages, ev = self.cache.admit(a, self.n_pages(a))
-            # pin at once so that a later admission of this batch cannot evict it
-            self.cache.set_pinned(a, True)
-            evicted_any |= len(ev) > 0
-            self.evictions += len(ev)
-            if hit:
-                self.hits += 1
-            else:
-                self.misses += 1
-                missed.append(a)
-                plan.append((a, pages))
-            self._write_tables(a, pages)
+        missed, plan, evicted_any, newly_pinned = [], [], False, []
+        try:
+            for a in want:
+                hit, pages, ev = self.cache.admit(a, self.n_pages(a))
+                if not hit:
+                    plan.append((a, pages))
+                # pin at once so that a later admission of this batch cannot evict it
+                self.cache.set_pinned(a, True)
+                if a not in self.pinned:
+                    self.pinned.add(a)
+                    newly_pinned.append(a)
+                evicted_any |= len(ev) > 0
+                self.evictions += len(ev)
+                if hit:
+                    self.hits += 1
+                else:
+                    self.misses += 1
+                    missed.append(a)
+                self._write_tables(a, pages)
+        except lora.LoraError:
+            # the batch does not fit: nothing of it stays pinned, and adapters
+            # admitted by this call (pages assigned, nothing uploaded) leave
+            for a in newly_pinned:
+                self.pinned.discard(a)
+                self.cache.set_pinned(a, False)
+            for a, _ in plan:
+                self.cache.release(a)
+            raise
         if plan:
             if evicted_any:
                 self.upload_stream.wait_stream(compute_stream)
@@ -110,6 +126,7 @@ class ManagedPool:
         evicted by later admissions (which then order their uploads after it)."""
         for a in dict.fromkeys(int(x) for x in adapters):
             self.cache.set_pinned(a, False)
+            self.pinned.discard(a)
 
     def proj(self, p: int, X: torch.Tensor, Y_base: torch.Tensor, Y: torch.Tensor) -> lora.Proj:
         a_ip, a_pg, b_ip, b_pg = self.tables[p]

@@ -90,3 +90,28 @@ def test_upload_coalesces_runs_and_scatters():
         assert torch.equal(host[p], src[i])
     untouched = sorted(set(range(40)) - set(ids.tolist()))
     assert bool((host[untouched] == -1.0).all())
+
+
+def test_managed_pool_rolls_back_a_batch_that_does_not_fit():
+    """A batch whose adapters cannot all be resident raises; nothing of it
+    stays pinned, adapters it admitted are released, earlier pins hold."""
+    ranks = [8, 16, 64, 24, 32, 8, 1, 40, 128, 16]
+    w = W.make_workload(2, dict(T=32, N=len(ranks), ranks_override=ranks, page_width=512, dtype="f32",
+                                projs=(("a", 1024, 768), ("b", 768, 1096))))
+    tier = host_tier_from_pool(_host_pool_tensor(w), w.tables, w.N)
+    mp = ManagedPool([(t.a_indptr, t.b_indptr) for t in w.tables], tier, w.page_width, capacity=60)
+    sizes = [mp.n_pages(a) for a in range(w.N)]
+    assert (sizes[0], sizes[2], sizes[7]) == (9, 36, 27)
+    mp.ensure([0])
+    with pytest.raises(lora.LoraError):
+        mp.ensure([2, 7])  # 9 pinned + 36 + 27 > 60
+    assert mp.pinned == {0}
+    assert len(mp.cache.lookup(0)) == 9 and len(mp.cache.lookup(2)) == 0 and len(mp.cache.lookup(7)) == 0
+    assert mp.cache.free_pages == 51
+    mp.unpin([0])
+    mp.ensure([2, 3])  # 36 + 18 fit once adapter 0 may go
+    torch.cuda.synchronize()
+    assert mp.pinned == {2, 3}
+    for a in (2, 3):
+        got = mp.base[torch.from_numpy(mp.cache.lookup(a).astype(np.int64)).cuda()].cpu()
+        assert torch.equal(got.view(torch.int32), tier[mp.offsets[a]:mp.offsets[a + 1]].view(torch.int32))
