@@ -577,50 +577,79 @@ __device__ __forceinline__ void stage_v(const KArgs& K, const KProj& P, int voff
 // exact in fp32.  Layout per token and rank group g (16 dwords): for each
 // half h of the group's 16 ranks, 4 dwords of hi pairs (ranks 8h+2j,
 // 8h+2j+1) then 4 dwords of lo pairs.  Ranks >= r are zero.
+// The staging of M (token, rank pair) entries per lane, in steps: set up
+// the entries, load one round of SF slices, add it, store the pairs.  A
+// caller may issue the first round before other loads and add it later.
 template <int M>
-__device__ __forceinline__ void stage_v_split_pass(const KArgs& K, const KProj& P, const float* src, int p0,
-                                                   int np, int r, int G, uint32_t* vs, int lane) {
-  const int hp = G * 8;  // rank pairs per token
+struct SplitStage {
+  static constexpr int SF = M >= 8 ? 1 : 8 / M;  // slices per round
   float acc[M][2];
+  float x[SF][M][2];
   int e[M], kk[M], dst[M];
+};
+
+template <int M>
+__device__ __forceinline__ void split_setup(SplitStage<M>& st, int p0, int np, int r, int G, int lane) {
+  const int hp = G * 8;  // rank pairs per token
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int p = p0 + lane + 64 * m;
     const int t = p / hp, kp = p - t * hp;  // pair kp = ranks 2kp, 2kp+1
-    kk[m] = p < np ? 2 * kp : LORA_MAX_RANK;  // past the end: nothing loaded or stored
-    e[m] = t * r + 2 * kp;
-    dst[m] = t * (G * 16) + (kp >> 3) * 16 + ((kp >> 2) & 1) * 8 + (kp & 3);
-    acc[m][0] = acc[m][1] = 0.0f;
+    st.kk[m] = p < np ? 2 * kp : LORA_MAX_RANK;  // past the end: nothing loaded or stored
+    st.e[m] = t * r + 2 * kp;
+    st.dst[m] = t * (G * 16) + (kp >> 3) * 16 + ((kp >> 2) & 1) * 8 + (kp & 3);
+    st.acc[m][0] = st.acc[m][1] = 0.0f;
   }
-  constexpr int SF = M >= 8 ? 1 : 8 / M;
-  for (int q = 0; q < P.nv; q += SF) {
-    float x[SF][M][2];
+}
+
+template <int M>
+__device__ __forceinline__ void split_load(const KArgs& K, const KProj& P, const float* src, int q, int r,
+                                           SplitStage<M>& st) {
 #pragma unroll
-    for (int j = 0; j < SF; ++j)
+  for (int j = 0; j < SplitStage<M>::SF; ++j)
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const float* a = src + (int64_t)(q + j) * K.v_stride + e[m];
-        const bool ok = q + j < P.nv;
-        x[j][m][0] = ok && kk[m] < r ? a[0] : 0.0f;
-        x[j][m][1] = ok && kk[m] + 1 < r ? a[1] : 0.0f;
-      }
+    for (int m = 0; m < M; ++m) {
+      const float* a = src + (int64_t)(q + j) * K.v_stride + st.e[m];
+      const bool ok = q + j < P.nv;
+      st.x[j][m][0] = ok && st.kk[m] < r ? a[0] : 0.0f;
+      st.x[j][m][1] = ok && st.kk[m] + 1 < r ? a[1] : 0.0f;
+    }
+}
+
+template <int M>
+__device__ __forceinline__ void split_add(SplitStage<M>& st) {
 #pragma unroll
-    for (int j = 0; j < SF; ++j)
+  for (int j = 0; j < SplitStage<M>::SF; ++j)
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        acc[m][0] += x[j][m][0];
-        acc[m][1] += x[j][m][1];
-      }
-  }
+    for (int m = 0; m < M; ++m) {
+      st.acc[m][0] += st.x[j][m][0];
+      st.acc[m][1] += st.x[j][m][1];
+    }
+}
+
+template <int M>
+__device__ __forceinline__ void split_store(const SplitStage<M>& st, uint32_t* vs) {
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    if (kk[m] < LORA_MAX_RANK) {
-      const uint32_t hi = pack_bf2(acc[m][0], acc[m][1]);
-      const uint32_t lo = pack_bf2(acc[m][0] - bf_lo(hi), acc[m][1] - bf_hi(hi));
-      vs[dst[m]] = hi;
-      vs[dst[m] + 4] = lo;
+    if (st.kk[m] < LORA_MAX_RANK) {
+      const uint32_t hi = pack_bf2(st.acc[m][0], st.acc[m][1]);
+      const uint32_t lo = pack_bf2(st.acc[m][0] - bf_lo(hi), st.acc[m][1] - bf_hi(hi));
+      vs[st.dst[m]] = hi;
+      vs[st.dst[m] + 4] = lo;
     }
   }
+}
+
+template <int M>
+__device__ __forceinline__ void stage_v_split_pass(const KArgs& K, const KProj& P, const float* src, int p0,
+                                                   int np, int r, int G, uint32_t* vs, int lane) {
+  SplitStage<M> st;
+  split_setup<M>(st, p0, np, r, G, lane);
+  for (int q = 0; q < P.nv; q += SplitStage<M>::SF) {
+    split_load<M>(K, P, src, q, r, st);
+    split_add<M>(st);
+  }
+  split_store<M>(st, vs);
 }
 
 __device__ __forceinline__ void stage_v_split(const KArgs& K, const KProj& P, int voff, int r, int n, uint32_t* vs,
@@ -815,14 +844,41 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
 #pragma unroll
     for (int sb = 0; sb < NP; ++sb) dst[sb] = sb < nsub ? load_dword(Yb + row * P.ldyb + jc[sb]) : 0u;
   };
+  // Vector memory returns in issue order, so data loaded after the weights
+  // is waited for behind them.  When the chunk's v needs at most one
+  // (token, rank pair) per lane, the first round of its loads goes out before
+  // the weights, and summing it overlaps their round trip.
+  [[maybe_unused]] SplitStage<1> st1;
+  [[maybe_unused]] const float* vsrc = P.v + d1.x + tb * r;
+  [[maybe_unused]] const bool early = EPV == 8 && n * G * 8 <= 64;
+  if constexpr (EPV == 8) {
+    if (early) {
+      split_setup<1>(st1, 0, n * G * 8, r, G, lane);
+      split_load<1>(K, P, vsrc, 0, r, st1);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   load_batch(0);
   load_yb(0, yb);
   // the next item's metadata, while this item's loads are in flight
   __builtin_amdgcn_sched_barrier(0);
   prefetch();
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (EPV == 8) stage_v_split(K, P, d1.x + tb * r, r, n, reinterpret_cast<uint32_t*>(vs), lane);
-  else stage_v(K, P, d1.x, r, tb, n, vs, lane);
+  if constexpr (EPV == 8) {
+    if (early) {
+      split_add<1>(st1);
+      for (int q = SplitStage<1>::SF; q < P.nv; q += SplitStage<1>::SF) {
+        split_load<1>(K, P, vsrc, q, r, st1);
+        split_add<1>(st1);
+      }
+      split_store<1>(st1, reinterpret_cast<uint32_t*>(vs));
+      wave_sync();
+    } else {
+      stage_v_split(K, P, d1.x + tb * r, r, n, reinterpret_cast<uint32_t*>(vs), lane);
+    }
+  } else {
+    stage_v(K, P, d1.x, r, tb, n, vs, lane);
+  }
   for (int t = 0; t < n; ++t) {
     if (t + 1 < n) load_yb(t + 1, ybn);
     float acc[NP][CPL];  // per pair
