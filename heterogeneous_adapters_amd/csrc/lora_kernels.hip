@@ -518,33 +518,67 @@ __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArg
 // v is nt*r contiguous floats in every partial slice.  Each thread sums M of
 // them over the slices, SF slices' loads in flight at a time (M*SF = 16);
 // every element is summed in ascending slice order whatever M and SF are.
-template <int NT, int M, int SF>
-__device__ __forceinline__ void stage_v_pass(const KArgs& K, const KProj& P, const float* src, int e0, int ne,
-                                             int r, int rs, float* vs, int tid) {
+// In steps, so that a caller may issue the first round of loads before
+// other loads and add it later.
+template <int M, int SF>
+struct RowStage {
   float acc[M];
+  float x[SF][M];
+};
+
+template <int NT, int M, int SF>
+__device__ __forceinline__ void row_load(const KArgs& K, const KProj& P, const float* src, int q, int e0, int ne,
+                                         int tid, RowStage<M, SF>& st) {
 #pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-  for (int q = 0; q < P.nv; q += SF) {
-    float x[SF][M];
+  for (int j = 0; j < SF; ++j)
 #pragma unroll
-    for (int j = 0; j < SF; ++j)
+    for (int m = 0; m < M; ++m) {
+      const int e = e0 + tid + NT * m;
+      st.x[j][m] = (q + j < P.nv && e < ne) ? src[(int64_t)(q + j) * K.v_stride + e] : 0.0f;
+    }
+}
+
+template <int M, int SF>
+__device__ __forceinline__ void row_add(RowStage<M, SF>& st) {
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const int e = e0 + tid + NT * m;
-        x[j][m] = (q + j < P.nv && e < ne) ? src[(int64_t)(q + j) * K.v_stride + e] : 0.0f;
-      }
+  for (int j = 0; j < SF; ++j)
 #pragma unroll
-    for (int j = 0; j < SF; ++j)
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] += x[j][m];
-  }
+    for (int m = 0; m < M; ++m) st.acc[m] += st.x[j][m];
+}
+
+template <int NT, int M, int SF>
+__device__ __forceinline__ void row_store(const RowStage<M, SF>& st, int e0, int ne, int r, int rs, float* vs,
+                                          int tid) {
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int e = e0 + tid + NT * m;
     if (e < ne) {
       const int t = e / r;
-      vs[t * rs + (e - t * r)] = acc[m];
+      vs[t * rs + (e - t * r)] = st.acc[m];
     }
+  }
+}
+
+template <int NT, int M, int SF>
+__device__ __forceinline__ void stage_v_pass(const KArgs& K, const KProj& P, const float* src, int e0, int ne,
+                                             int r, int rs, float* vs, int tid) {
+  RowStage<M, SF> st;
+#pragma unroll
+  for (int m = 0; m < M; ++m) st.acc[m] = 0.0f;
+  for (int q = 0; q < P.nv; q += SF) {
+    row_load<NT, M, SF>(K, P, src, q, e0, ne, tid, st);
+    row_add<M, SF>(st);
+  }
+  row_store<NT, M, SF>(st, e0, ne, r, rs, vs, tid);
+}
+
+// zero the rank padding (ranks r .. G*16) of nt staged rows
+template <int NT>
+__device__ __forceinline__ void stage_v_pad(int r, int nt, float* vs, int tid) {
+  const int rs = rank_groups(r) * 16;
+  for (int idx = tid; idx < nt * (rs - r); idx += NT) {
+    const int t = idx / (rs - r);
+    vs[t * rs + r + (idx - t * (rs - r))] = 0.0f;
   }
 }
 
@@ -557,10 +591,7 @@ __device__ __forceinline__ void stage_v_rows(const KArgs& K, const KProj& P, int
   if (ne <= 2 * NT) stage_v_pass<NT, 2, 8>(K, P, src, 0, ne, r, rs, vs, tid);
   else
     for (int e0 = 0; e0 < ne; e0 += NT * 8) stage_v_pass<NT, 8, 2>(K, P, src, e0, ne, r, rs, vs, tid);
-  for (int idx = tid; idx < nt * (rs - r); idx += NT) {  // zero the rank padding of every row
-    const int t = idx / (rs - r);
-    vs[t * rs + r + (idx - t * (rs - r))] = 0.0f;
-  }
+  stage_v_pad<NT>(r, nt, vs, tid);
 }
 
 // one wave stages its own rows
@@ -1061,10 +1092,32 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
   bool okcur[CT][NKS], oknext[CT][NKS];
   const bool active = jend > 0;  // the wave has columns in this item
   const int np = active ? ceil_div_i(jend, PART) : 0;
-  // the first part's B and Y_base are requested before v is staged, so the
-  // two memory round trips overlap
+  // The tile's v is staged while the first part's B and Y_base are in
+  // flight.  Vector memory returns in issue order, so when the tile needs
+  // one round of staging loads (at most two entries per thread), that round
+  // goes out first and is summed without waiting for the part's loads.
+  const int ne = nt * r;
+  const float* vsrc = P.v + voff + (int64_t)tb * r;
+  const bool early = ne <= 2 * kThreads;
+  RowStage<2, 8> st0;
+  if (early) {
+    st0.acc[0] = st0.acc[1] = 0.0f;
+    row_load<kThreads, 2, 8>(K, P, vsrc, 0, 0, ne, threadIdx.x, st0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   if (active) load_part(0, bcur, ycur, okcur);
-  stage_v_rows<kThreads>(K, P, voff, r, tb, nt, vs, threadIdx.x);
+  __builtin_amdgcn_sched_barrier(0);
+  if (early) {
+    row_add<2, 8>(st0);
+    for (int q = 8; q < P.nv; q += 8) {
+      row_load<kThreads, 2, 8>(K, P, vsrc, q, 0, ne, threadIdx.x, st0);
+      row_add<2, 8>(st0);
+    }
+    row_store<kThreads, 2, 8>(st0, 0, ne, r, rs, vs, threadIdx.x);
+    stage_v_pad<kThreads>(r, nt, vs, threadIdx.x);
+  } else {
+    stage_v_rows<kThreads>(K, P, voff, r, tb, nt, vs, threadIdx.x);
+  }
   __syncthreads();
   uint4 vv[NKS];
 #pragma unroll
