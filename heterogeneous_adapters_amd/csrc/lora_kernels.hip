@@ -322,11 +322,8 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int 
 #pragma unroll
     for (int v = 0; v < NVEC; ++v) pg[v] = page_base<E>(K, P.a_pages[slot0 + ((col0 + cl[v]) >> K.pw_log2)], pok[v]);
   }
-  uint4 w[16][NVEC];
-#pragma unroll
-  for (int rr = 0; rr < 16; ++rr)
-#pragma unroll
-    for (int v = 0; v < NVEC; ++v) w[rr][v] = ldg16(pg[v] + min(rr, rows - 1) * pw + ((col0 + cl[v]) & (pw - 1)));
+  // X first, then the rows in product order: vector memory returns in issue
+  // order, so the products of row rr wait only for X and rows 0..rr
   uint4 x[NV][NVEC];
 #pragma unroll
   for (int tt = 0; tt < NV; ++tt) {
@@ -334,6 +331,13 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int 
 #pragma unroll
     for (int v = 0; v < NVEC; ++v) x[tt][v] = ldg16(X + row + cl[v]);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 w[16][NVEC];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+    for (int v = 0; v < NVEC; ++v) w[rr][v] = ldg16(pg[v] + min(rr, rows - 1) * pw + ((col0 + cl[v]) & (pw - 1)));
+  __builtin_amdgcn_sched_barrier(0);
   static_assert(16 * NV == 32, "one 32-value wave reduction per item");
   float acc[32];
 #pragma unroll
