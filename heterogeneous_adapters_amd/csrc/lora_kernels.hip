@@ -14,13 +14,14 @@
 //   shrink_kernel
 //       v = X A for every segment ([MLSP] SGMV shrink), read straight from
 //       the paged pool ([MLSP] "Unified Paging Architecture").  Short
-//       segments take the MBGMV path (vector ALU, token rows staged in LDS,
-//       wavefront reductions); long ones the MBGMM path (16x16 MFMA tiles).
-//       Each work item covers one 1024-column slice of d_in and writes a
-//       partial v; the expand sums the slices in ascending order, so every
-//       result is bitwise deterministic.
+//       segments take the MBGMV path (vector ALU dot products, wavefront
+//       reductions across d_in); long ones the MBGMM path (16x16 MFMA
+//       tiles).  Each work item covers one 512-column slice of d_in and
+//       writes a partial v; the expand sums the slices in ascending order,
+//       so every result is bitwise deterministic.
 //   expand_kernel
-//       Y = Y_base + (alpha/r) v B ([MLSP] SGMV expand), same two paths.
+//       Y = Y_base + (alpha/r) v B ([MLSP] SGMV expand), same two paths; v
+//       of an item's tokens is staged in LDS.
 //
 // Both compute kernels are persistent grids that walk a device-side item
 // list (no host read-back of the segment count).  Items are dealt to the 8
@@ -724,11 +725,6 @@ __device__ __forceinline__ float b_elem(const uint4 (&b)[4], int c, int k, F32) 
   return __uint_as_float((&b[0].x)[c * 16 + k]);
 }
 
-// MBGMV expand item (one wave): (segment, <= 8 tokens, column block).  Each
-// lane owns CPL adjacent output columns (2 in bf16, 1 in fp32) whose 16-rank
-// rows are adjacent in the B page: 64 contiguous bytes per lane and rank
-// group, 4 KiB per wave.  The B loads of up to four rank groups and the
-// Y_base loads are issued before v is staged.
 // Metadata of one MBGMV expand item, loaded one item ahead (scalar loads
 // issued while the previous item's weight loads are in flight): the
 // segment descriptor, the adapter's B-table offset and the page ids of its
@@ -1014,10 +1010,10 @@ __device__ __forceinline__ void store4(float* p, const float (&y)[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(y[0], y[1], y[2], y[3]);
 }
 
-// MBGMM expand item (one wave): (segment, one 16-token tile, column block of
-// 1024 columns in bf16 / 512 in fp32).  v of the tile is staged once; the
-// block is walked in parts of four 16-column tiles, the B operands and
-// Y_base values of part p+1 requested while part p is multiplied.
+// MBGMM expand item, one wave's share: (segment, 16-token tile, wc output
+// columns).  v of the tile is staged once (by the block); the columns are
+// walked in parts of CT 16-column tiles, the B operands and Y_base values of
+// part p+1 requested while part p is multiplied.
 // C[col][token] += B^T[col][rank] * v^T[rank][token]: B pages hold the 16
 // ranks of an output column contiguously, so each lane's operand is one
 // 16-byte load, and a lane's four C values are four adjacent columns of one
