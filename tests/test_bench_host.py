@@ -1,0 +1,99 @@
+"""Host-side logic of bench.py (no GPU): the rocprofv3 summary it writes
+under profiles/, the kernel-source hash that ties a summary to the sources,
+the one-GPU refusal and the decode-step grouping."""
+import csv
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+EXPAND = "void lora::expand_kernel<lora::Bf16, true>(lora::KArgs)"
+SHRINK = "void lora::shrink_kernel<lora::Bf16, true>(lora::KArgs)"
+COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(at::TensorIteratorBase&)>"
+
+
+def _write_csv(path, header, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_summary_scales_counters_by_the_calibration_copy(tmp_path, capsys):
+    """FETCH_SIZE reading half the calibration copy's bytes gives a scale of
+    2; WRITE_SIZE reading them exactly, 1; per-launch bytes follow."""
+    d = tmp_path / "prof"
+    d.mkdir()
+    calib_kib = bench.CALIB_BYTES / 1024
+    rows = []
+    disp = 0
+    for name, fetch, write in ((COPY, calib_kib / 2, calib_kib), (EXPAND, 1000.0, 300.0), (EXPAND, 3000.0, 500.0),
+                               (SHRINK, 700.0, 10.0)):
+        disp += 1
+        rows.append([disp, name, "FETCH_SIZE", fetch])
+        rows.append([disp, name, "WRITE_SIZE", write])
+    _write_csv(d / "run_counter_collection.csv", ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+    bench.summarize_profile([str(d)], "rocprofv3 --pmc ... (test)")
+    out = capsys.readouterr().out.splitlines()
+    assert out[0] == "command: rocprofv3 --pmc ... (test)"
+    assert out[1] == f"kernel_source_hash: {bench.kernel_source_hash()}"
+    vals = dict(l.split(": ") for l in out if ": " in l and not l.startswith(("command", "kernel_source")))
+    assert float(vals["fetch_size_scale"]) == pytest.approx(2.0)
+    assert float(vals["write_size_scale"]) == pytest.approx(1.0)
+    assert int(vals["expand_fetch_size_bytes_per_launch"]) == 2000 * 1024 * 2
+    assert int(vals["expand_write_size_bytes_per_launch"]) == 400 * 1024
+    assert int(vals["hbm_bytes_per_launch"]) == 2000 * 2048 + 400 * 1024
+    assert int(vals["shrink_hbm_bytes_per_launch"]) == 700 * 2048 + 10 * 1024
+
+
+def test_summary_of_kernel_stats_and_mfma_counters(tmp_path, capsys):
+    d = tmp_path / "prof"
+    d.mkdir()
+    _write_csv(d / "x_kernel_stats.csv", ["Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs", "MaxNs", "Percentage"],
+               [[EXPAND, 4, 240000, 60000, 50000, 70000, 60.0], [COPY, 1, 160000, 160000, 160000, 160000, 40.0]])
+    _write_csv(d / "m_counter_collection.csv", ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"],
+               [[1, EXPAND, "MfmaUtil", 3.0], [2, EXPAND, "MfmaUtil", 4.0], [1, EXPAND, "MfmaFlopsBF16", 1e9]])
+    bench.summarize_profile([str(d)], "")
+    out = capsys.readouterr().out
+    line = [l for l in out.splitlines() if EXPAND in l and "avg_us" not in l and "Mfma" not in l
+            and not l.startswith("mfma")][0].split()
+    assert line[:6] == ["4", "60.00", "50.00", "70.00", "0.240", "60.00"]
+    assert f"mfma_util_pct 3.5  {EXPAND}" in out
+    assert f"mfma_bf16_flops_per_dispatch 1e+09  {EXPAND}" in out
+    assert "lora::" in out and "neg_kernel" not in out.split("kernel stats")[1].split("counters")[0]
+
+
+def test_kernel_hash_ignores_comments_but_not_code(tmp_path):
+    for rel in bench.KERNEL_SOURCES:
+        os.makedirs(tmp_path / os.path.dirname(rel), exist_ok=True)
+        shutil.copy(os.path.join(ROOT, rel), tmp_path / rel)
+    h0 = bench.kernel_source_hash(str(tmp_path))
+    assert h0 == bench.kernel_source_hash()
+    first = tmp_path / bench.KERNEL_SOURCES[0]
+    text = first.read_text()
+    first.write_text("// a new comment line\n/* and a block\n comment */\n" + text.replace("\n", "\n  ", 3))
+    assert bench.kernel_source_hash(str(tmp_path)) == h0
+    first.write_text(text + "\nstatic int lora_extra_symbol = 1;\n")
+    assert bench.kernel_source_hash(str(tmp_path)) != h0
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+
+
+def test_layer_grouping_follows_the_block_dependencies():
+    names = ["q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj"]
+    g = bench.groups_for(2, names, "layer")
+    assert g[:4] == [[0, 1, 2], [3], [4, 5], [6]]
+    assert g[4:] == [[7, 8, 9], [10], [11, 12], [13]]
+    assert sorted(i for grp in g for i in grp) == list(range(14))
+    a = bench.groups_for(32, names, "all")
+    assert all(len(grp) <= 16 for grp in a) and sum(len(grp) for grp in a) == 224
