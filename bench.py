@@ -454,6 +454,21 @@ def main():
         kernels[kname] = {"launches_per_step": len(groups), "mean_launch_us": round(float(ms_g.mean()) * 1e3, 2),
                           "algorithmic_bytes_per_launch": int(np.mean(kb)), "gbs": round(gb, 1),
                           "frac_hbm_peak": round(gb / HBM_PEAK_GBS, 4)}
+    # the same two kernels by projection group (q/k/v, o, gate/up, down), as
+    # mean launch time and GB/s over the layers
+    by_group = {}
+    for gi, g in enumerate(groups):
+        key = "+".join(names[i % len(names)].replace("_proj", "") for i in g)
+        d = by_group.setdefault(key, {"shrink_us": [], "expand_us": [], "shrink_b": [], "expand_b": []})
+        d["shrink_us"].append(shr_ms[gi] * 1e3)
+        d["expand_us"].append(exp_ms[gi] * 1e3)
+        d["shrink_b"].append(call_split[gi][0])
+        d["expand_b"].append(call_split[gi][1])
+    for key, d in by_group.items():
+        su, eu = float(np.mean(d["shrink_us"])), float(np.mean(d["expand_us"]))
+        by_group[key] = {"shrink_us": round(su, 2), "shrink_gbs": round(float(np.mean(d["shrink_b"])) / su / 1e3, 1),
+                         "expand_us": round(eu, 2), "expand_gbs": round(float(np.mean(d["expand_b"])) / eu / 1e3, 1)}
+    kernels["by_group"] = by_group
     dom = kernels["expand_kernel<Bf16, true>"]
     roofline = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": dom["frac_hbm_peak"], "traffic": load_traffic(kernel_source_hash()),

@@ -278,22 +278,75 @@ __device__ const KArgs& kernel_args();
 // 64 lanes are reduced across the wave.  All loads are issued before the
 // first product, so an item costs one memory round trip after its page
 // lookup.
-template <class E, bool WIDE>
-__device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int q, int4 d0, int4 d1, int local, int lane) {
+// Metadata of one MBGMV shrink item, loaded one item ahead (scalar loads
+// issued while the previous item's loads are in flight): the segment
+// descriptor, the adapter's A-table slot, the page id of the slice (when the
+// slice lies in one page) and the activation rows of its tokens.
+struct ShrinkItem {
+  int p, q;           // projection, 512-column slice
+  int4 d0, d1;        // segment descriptor
+  int g, tb, nt;      // rank group, first token (in the segment), tokens
+  int slot0, pid;     // A-table slot of the group's first page; page id of the slice
+  int xr[kValuTokens];  // activation rows of the tokens (past nt: the last one)
+};
+
+template <bool WIDE>
+__device__ __forceinline__ ShrinkItem fetch_shrink_item(const KArgs& K, int i, int Uv) {
+  ShrinkItem it;
+  int u;
+  if (K.xshare) {
+    it.p = i % K.np;
+    const int rest = i / K.np;
+    it.q = rest / Uv;
+    u = rest - it.q * Uv;
+  } else {
+    int rem = i, p = 0;
+    while (rem >= K.p[p].nq * Uv) { rem -= K.p[p].nq * Uv; ++p; }
+    it.p = p;
+    it.q = rem / Uv;
+    u = rem - it.q * Uv;
+  }
+  const KProj& P = K.p[it.p];
+  const int s = cld(K.shr_item_v + u);
+  it.d0 = cld4(K.seg_desc + 2 * s);
+  it.d1 = cld4(K.seg_desc + 2 * s + 1);
+  const int local = u - it.d1.y;
+  const int n = it.d0.w;
+  const int nch = ceil_div_i(n, kValuTokens);
+  it.g = local / nch;
+  it.tb = (local - it.g * nch) * kValuTokens;
+  it.nt = min(kValuTokens, n - it.tb);
+  it.slot0 = cld(P.a_indptr + it.d0.x) + it.g * ((P.d_in + (1 << K.pw_log2) - 1) >> K.pw_log2);
+  it.pid = WIDE ? cld(P.a_pages + it.slot0 + ((it.q * kKSlice) >> K.pw_log2)) : 0;
+#pragma unroll
+  for (int tt = 0; tt < kValuTokens; ++tt) it.xr[tt] = cld(K.perm + it.d0.z + it.tb + min(tt, it.nt - 1));
+  return it;
+}
+
+// MBGMV item (one wave): (segment, rank group g, <= 2 tokens, 512-column
+// slice q).  Each lane streams one 16-byte vector (8 bf16 / 4 fp32 columns)
+// of each of the group's 16 page rows -- a wave reads 1 KiB contiguous per
+// row -- together with the same columns of the tokens' activation rows (the
+// gathered activations of [MLSP] SGMV), forms partial dot products, and the
+// 64 lanes are reduced across the wave.  All loads are issued before the
+// first product, so an item costs one memory round trip; the next item's
+// metadata is fetched while they are in flight.
+template <class E, bool WIDE, class Prefetch>
+__device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, const ShrinkItem& item, int lane,
+                                            Prefetch&& prefetch) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
   constexpr int NVEC = kKSlice / (64 * EPV);  // vectors per lane and row (bf16 1, fp32 2)
   constexpr int NV = kValuTokens;
-  const int a = d0.x, r = d0.y, t0 = d0.z, n = d0.w;
-  const int nch = ceil_div_i(n, NV);
-  const int g = local / nch;
-  const int tb = (local - g * nch) * NV;
-  const int nt = min(NV, n - tb);
+  const int q = item.q;
+  const int4 d1 = item.d1;
+  const int r = item.d0.y;
+  const int g = item.g, tb = item.tb, nt = item.nt;
   const int col0 = q * kKSlice;
   const int ncols = min(kKSlice, P.d_in - col0);  // a multiple of 8
   const int pw = 1 << K.pw_log2;
   const int rows = min(16, r - g * 16);
-  const int slot0 = cld(P.a_indptr + a) + g * ((P.d_in + pw - 1) >> K.pw_log2);
+  const int slot0 = item.slot0;
   const T* X = reinterpret_cast<const T*>(P.X);
   // Every load is unconditional and in bounds: rows past the rank re-read
   // the group's last row, tokens past the item its last token, lanes past
@@ -313,7 +366,7 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int 
   bool pok[NVEC];
   if constexpr (WIDE) {  // the slice lies in one page: a wave-uniform lookup
     bool ok;
-    const T* p = page_base<E>(K, cld(P.a_pages + slot0 + (col0 >> K.pw_log2)), ok);
+    const T* p = page_base<E>(K, item.pid, ok);
 #pragma unroll
     for (int v = 0; v < NVEC; ++v) {
       pg[v] = p;
@@ -328,7 +381,7 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int 
   uint4 x[NV][NVEC];
 #pragma unroll
   for (int tt = 0; tt < NV; ++tt) {
-    const int64_t row = (int64_t)cld(K.perm + t0 + tb + min(tt, nt - 1)) * P.ldx + col0;
+    const int64_t row = (int64_t)item.xr[tt] * P.ldx + col0;
 #pragma unroll
     for (int v = 0; v < NVEC; ++v) x[tt][v] = ldg16(X + row + cl[v]);
   }
@@ -338,6 +391,8 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, int 
   for (int rr = 0; rr < 16; ++rr)
 #pragma unroll
     for (int v = 0; v < NVEC; ++v) w[rr][v] = ldg16(pg[v] + min(rr, rows - 1) * pw + ((col0 + cl[v]) & (pw - 1)));
+  __builtin_amdgcn_sched_barrier(0);
+  prefetch();
   __builtin_amdgcn_sched_barrier(0);
   static_assert(16 * NV == 32, "one 32-value wave reduction per item");
   float acc[32];
@@ -471,7 +526,13 @@ __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArg
   const int Um = cld(K.counts + kCountShrinkMfma), Uv = cld(K.counts + kCountShrinkValu);
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   // MBGMM items first, then MBGMV items; each path walks its own item list,
-  // so the two register footprints never share a loop body.
+  // so the two register footprints never share a loop body.  The wave's
+  // first MBGMV item's metadata is requested before the MBGMM pass.
+  int total_v = 0;
+  for (int p = 0; p < K.np; ++p) total_v += K.p[p].nq * Uv;
+  WaveWalk iv(total_v, wave);
+  ShrinkItem cur;
+  if (iv.i < iv.end) cur = fetch_shrink_item<WIDE>(K, iv.i, Uv);
   int total = 0;
   for (int p = 0; p < K.np; ++p) total += K.p[p].nq * Um;
   // Item order: projection-major, or -- when every projection of the launch
@@ -495,25 +556,17 @@ __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArg
     const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
     shrink_mfma<E, WIDE>(K, K.p[p], q, d0, d1, u - d1.y, lane);
   }
-  total = 0;
-  for (int p = 0; p < K.np; ++p) total += K.p[p].nq * Uv;
-  for (WaveWalk it(total, wave); it.i < it.end; it.i += it.stride) {
-    int p, q, u;
-    if (K.xshare) {
-      p = it.i % K.np;
-      const int rest = it.i / K.np;
-      q = rest / Uv;
-      u = rest - q * Uv;
-    } else {
-      int rem = it.i;
-      p = 0;
-      while (rem >= K.p[p].nq * Uv) { rem -= K.p[p].nq * Uv; ++p; }
-      q = rem / Uv;
-      u = rem - q * Uv;
-    }
-    const int s = cld(K.shr_item_v + u);
-    const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
-    shrink_valu<E, WIDE>(K, K.p[p], q, d0, d1, u - d1.y, lane);
+  if (iv.i >= iv.end) return;
+  for (;;) {
+    const int ni = iv.i + iv.stride;
+    const bool more = ni < iv.end;
+    ShrinkItem nxt;
+    shrink_valu<E, WIDE>(K, K.p[cur.p], cur, lane, [&]() {
+      if (more) nxt = fetch_shrink_item<WIDE>(K, ni, Uv);
+    });
+    if (!more) break;
+    cur = nxt;
+    iv.i = ni;
   }
 }
 
@@ -790,11 +843,10 @@ __device__ __forceinline__ uint32_t pack_cols(const float (&y)[1]) { return __fl
 // per sub-block and rank group.  A segment with 1, 2 or more rank groups
 // covers the block in 1, 2 or 4 parts of nsub = 4, 2 or 1 sub-blocks, so
 // every item holds four (sub-block, rank group) pairs -- 16 KiB of B per wave
-// in bf16 -- all requested at once with the first token's Y_base.  Pair i
-// is (sub-block i % nsub, group g0 + i / nsub).  v of the chunk's tokens is
-// staged once; the tokens are then produced one at a time from the B
-// registers, the next token's Y_base requested before the current token's
-// products.
+// in bf16 -- all requested at once with the Y_base rows of every token of
+// the chunk.  Pair i is (sub-block i % nsub, group g0 + i / nsub).  v of the
+// chunk's tokens is staged once; the tokens are then produced one at a time
+// from the B registers.
 template <class E, bool ONE_PAGE, class Prefetch>
 __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P, const ValuItem& item, float* vs,
                                                  int lane, Prefetch&& prefetch) {
@@ -868,12 +920,19 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
   };
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
   T* Y = reinterpret_cast<T*>(P.Y);
-  // Y_base of one token (one dword per sub-block), requested one token ahead
-  uint32_t yb[NP], ybn[NP];
-  auto load_yb = [&](int t, uint32_t (&dst)[NP]) {
-    const int64_t row = cld(K.perm + t0 + t);
+  // Y_base of every token of the chunk (one dword per sub-block), requested
+  // with the weights: a token's row loaded after the previous token's
+  // products would cost each token one more memory round trip.  Loads are
+  // unconditional (tokens past the chunk re-read its last row, sub-blocks
+  // past the part re-read a valid column); such values are never stored.
+  uint32_t ybt[kValuExpandTokens][NP];
+  auto load_yb_all = [&]() {
 #pragma unroll
-    for (int sb = 0; sb < NP; ++sb) dst[sb] = sb < nsub ? load_dword(Yb + row * P.ldyb + jc[sb]) : 0u;
+    for (int t = 0; t < kValuExpandTokens; ++t) {
+      const int64_t row = cld(K.perm + t0 + min(t, n - 1));
+#pragma unroll
+      for (int sb = 0; sb < NP; ++sb) ybt[t][sb] = load_dword(Yb + row * P.ldyb + jc[sb]);
+    }
   };
   // Vector memory returns in issue order, so data loaded after the weights
   // is waited for behind them.  When the chunk's v needs at most one
@@ -890,7 +949,7 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
   }
   __builtin_amdgcn_sched_barrier(0);
   load_batch(0);
-  load_yb(0, yb);
+  load_yb_all();
   // the next item's metadata, while this item's loads are in flight
   __builtin_amdgcn_sched_barrier(0);
   prefetch();
@@ -911,7 +970,7 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
     stage_v(K, P, d1.x, r, tb, n, vs, lane);
   }
   for (int t = 0; t < n; ++t) {
-    if (t + 1 < n) load_yb(t + 1, ybn);
+    uint32_t (&yb)[NP] = ybt[0];  // token t's row; the rows move up one slot per token
     float acc[NP][CPL];  // per pair
 #pragma unroll
     for (int i = 0; i < NP; ++i)
@@ -940,9 +999,11 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
 #pragma unroll
           for (int q = 0; q < 4; ++q) vv[q] = vt[q];
         }
-        uint4 w[4];
+        // masked in place: the masks do not depend on the token, so masking
+        // the registers again for the next token changes nothing
+        uint4 (&w)[4] = b[i];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = okp[i] ? b[i][q] : zero4();
+        for (int q = 0; q < 4; ++q) w[q] = okp[i] ? w[q] : zero4();
         if (r - g * 16 < 16) {  // the last group of a rank below a multiple of 16: mask ranks >= r
 #pragma unroll
           for (int c = 0; c < CPL; ++c)
@@ -989,7 +1050,9 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
       }
     }
 #pragma unroll
-    for (int sb = 0; sb < NP; ++sb) yb[sb] = ybn[sb];
+    for (int tt = 0; tt + 1 < kValuExpandTokens; ++tt)
+#pragma unroll
+      for (int sb = 0; sb < NP; ++sb) ybt[tt][sb] = ybt[tt + 1][sb];
   }
 }
 
@@ -1248,15 +1311,17 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
   // MBGMM items first (whole-block items), then MBGMV items and the copies of
   // rows without an adapter (one wave each); each path walks its own item
   // list.  The columns per wave of an MBGMM item (64..512, at most the page
-  // width) shrink until the items cover about twice the grid, so a few hot
-  // segments still spread over every compute unit; wide items stage a token
-  // tile's v once for more columns.
+  // width) shrink until the items cover the grid once, so a few hot segments
+  // still spread over every compute unit; wide items stage a token tile's v
+  // once for more columns.  (Covering the grid twice over, with narrower
+  // items, left each block two or three items in a row, each one memory
+  // round trip.)
   if (Um > 0) {
     int wc = min(512, 1 << K.pw_log2), total = 0;
     for (;; wc >>= 1) {
       total = 0;
       for (int p = 0; p < K.np; ++p) total += ceil_div_i(K.p[p].d_out, kWaves * wc) * Um;
-      if (wc == 64 || total >= 2 * (int)gridDim.x) break;
+      if (wc == 64 || total >= (int)gridDim.x) break;
     }
     for (WaveWalk it(total, 0, 1); it.i < it.end; it.i += it.stride) {
       int rem = it.i, p = 0;

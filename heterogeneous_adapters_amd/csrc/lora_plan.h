@@ -30,7 +30,10 @@ constexpr int kThreads = 256;             // work-group size (4 wave64)
 constexpr int kWaves = kThreads / 64;
 constexpr int kKSlice = 512;              // input columns per shrink item (one partial slice)
 constexpr int kValuTokens = 2;            // tokens per MBGMV shrink item
-constexpr int kValuExpandTokens = 4;      // tokens per MBGMV expand item (a chunk of the segment)
+#ifndef LORA_VALU_EXPAND_TOKENS
+#define LORA_VALU_EXPAND_TOKENS 2
+#endif
+constexpr int kValuExpandTokens = LORA_VALU_EXPAND_TOKENS;  // tokens per MBGMV expand item (a chunk of the segment)
 constexpr int kCopyTokens = 8;            // rows per copy item (tokens without an adapter)
 constexpr int kMfmaExpandTokens = 16;     // tokens per MBGMM expand item (one tile)
 #ifndef LORA_MFMA_SHRINK_TOKENS
@@ -57,7 +60,7 @@ LORA_HD inline bool is_mfma_segment(int n) { return n >= kMfmaMinTokens; }
 
 // Work items of one segment, per 512-column shrink slice or per expand
 // column block.  MBGMV shrink: (rank group, <= kValuTokens tokens); MBGMM
-// shrink: (16-token tile, rank group); MBGMV expand: (part, chunk of <= 4
+// shrink: (16-token tile, rank group); MBGMV expand: (part, chunk of <= 2
 // tokens), the column block split in 1, 2 or 4 parts for 1, 2 or more rank
 // groups (every part holds at most 4 (sub-block, rank group) pairs of B);
 // MBGMM expand: one 16-token tile.
@@ -97,9 +100,10 @@ LORA_HD inline PlanLayout plan_layout(int T, int N) {
   // MBGMM shrink items <= 8*(T/16 + S) <= 9T; MBGMV <= 8*(T/2 + S) <= 12T
   L.shrink_valu = L.shrink_mfma + align64(9 * t + 1);
   L.expand_mfma = L.shrink_valu + align64(12 * t + 1);
-  // MBGMM expand items <= T/16 + S <= 2T; MBGMV <= 4*(T/4 + S) <= 5T
+  // MBGMM expand items <= T/16 + S <= 2T; MBGMV <= 4*(T/K + S) <= (4/K + 4)T
+  // for chunks of K = kValuExpandTokens tokens
   L.expand_valu = L.expand_mfma + align64(2 * t + 1);
-  L.total = L.expand_valu + align64(5 * t + 1);
+  L.total = L.expand_valu + align64((4 / kValuExpandTokens + 4) * t + 1);
   return L;
 }
 
