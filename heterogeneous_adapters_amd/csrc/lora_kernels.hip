@@ -1073,6 +1073,10 @@ __device__ __forceinline__ void store4(float* p, const float (&y)[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(y[0], y[1], y[2], y[3]);
 }
 
+// LDS floats per wave row set of the expand: a staged 16-token v tile
+// (16 x LORA_MAX_RANK) or 16 output rows of up to 128 columns plus padding.
+constexpr int kExpandRowFloats = kMfmaExpandTokens * (LORA_MAX_RANK + 4);
+
 // MBGMM expand item, one wave's share: (segment, 16-token tile, wc output
 // columns).  v of the tile is staged once (by the block); the columns are
 // walked in parts of CT 16-column tiles, the B operands and Y_base values of
@@ -1089,8 +1093,8 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
   constexpr int EPV = E::kEpv;
   constexpr int KSTEP = 4 * EPV;
   // 16-column tiles per part: the operands of two parts (current and next)
-  // stay within 64 VGPRs.
-  constexpr int CT = NKS >= 8 ? 1 : 8 / NKS > 4 ? 4 : 8 / NKS;
+  // stay within 64 VGPRs (bf16: 128 columns for r <= 32, 64 for r <= 64).
+  constexpr int CT = NKS >= 8 ? 1 : 8 / NKS;
   constexpr int PART = 16 * CT;
   const int li = lane & 15, qq = lane >> 4;
   const int rs = rank_groups(r) * 16;
@@ -1112,6 +1116,7 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
   constexpr int TPR = 64 / CPR;             // token rows per round of the wave
   constexpr int ROUNDS = 16 / TPR;
   constexpr int LDC = PART + 4;             // LDS row stride (floats)
+  static_assert(16 * LDC <= kExpandRowFloats, "output rows fit the wave's LDS rows");
   const int ch = lane % CPR;
   int64_t yrow[ROUNDS];
 #pragma unroll
@@ -1265,7 +1270,9 @@ __device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int 
   // K steps past the rank are skipped inside the body, so two variants cover
   // every rank; the choice is the same for the whole block (one segment)
   const int nks = ceil_div_i(r, KSTEP);
-  if (nks <= MAXKS / 2)
+  if (nks <= MAXKS / 4)  // bf16: one K step (r <= 32), so twice the columns per part
+    expand_mfma_body<E, MAXKS / 4, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
+  else if (nks <= MAXKS / 2)
     expand_mfma_body<E, MAXKS / 2, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
   else expand_mfma_body<E, MAXKS, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
   __syncthreads();  // the rows are restaged by the block's next item
@@ -1300,7 +1307,7 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
   const KArgs& K = kernel_args();
   // per-wave rows (MBGMV staging, MBGMM output tiles) and the block's staged
   // v tile of an MBGMM item
-  __shared__ __attribute__((aligned(16))) float vs_all[kWaves + 1][kMfmaExpandTokens * LORA_MAX_RANK];
+  __shared__ __attribute__((aligned(16))) float vs_all[kWaves + 1][kExpandRowFloats];
   const int S = cld(K.counts + kCountS);
   const int t_valid = cld(K.counts + kCountTValid);
   const int Um = S > 0 ? cld(K.counts + kCountExpandMfma) : 0;
@@ -1310,7 +1317,7 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
   float* vs = vs_all[wave];
   // MBGMM items first (whole-block items), then MBGMV items and the copies of
   // rows without an adapter (one wave each); each path walks its own item
-  // list.  The columns per wave of an MBGMM item (64..512, at most the page
+  // list.  The columns per wave of an MBGMM item (128..512, at most the page
   // width) shrink until the items cover the grid once, so a few hot segments
   // still spread over every compute unit; wide items stage a token tile's v
   // once for more columns.  (Covering the grid twice over, with narrower
@@ -1321,7 +1328,7 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
     for (;; wc >>= 1) {
       total = 0;
       for (int p = 0; p < K.np; ++p) total += ceil_div_i(K.p[p].d_out, kWaves * wc) * Um;
-      if (wc == 64 || total >= (int)gridDim.x) break;
+      if (wc <= 128 || total >= (int)gridDim.x) break;
     }
     for (WaveWalk it(total, 0, 1); it.i < it.end; it.i += it.stride) {
       int rem = it.i, p = 0;
