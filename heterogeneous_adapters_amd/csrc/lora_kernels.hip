@@ -249,6 +249,41 @@ struct WaveWalk {
   }
 };
 
+// The expand's MBGMV walk when the first Gm blocks of each XCD run the MBGMM
+// items: the waves of the other blocks take R rounds of the XCD's MBGMV
+// items among themselves (R: the MBGMV items that take as long as one
+// block's MBGMM items), then every wave takes items in turn.
+struct TwoClassWalk {
+  int i, end, nV, W, ib, ka;  // ka: first-phase items left after the current one (-1: second phase)
+  __device__ TwoClassWalk(int total, int Gm, int R, int wv) {
+    const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
+    const int x = blockIdx.x % nx, beta = blockIdx.x / nx, G = gridDim.x / nx;
+    const int lo = (int)(((int64_t)total * x) / nx);
+    end = (int)(((int64_t)total * (x + 1)) / nx);
+    W = G * kWaves;
+    nV = (G - Gm) * kWaves;
+    ib = lo + R * nV + beta * kWaves + wv;
+    if (beta >= Gm && R > 0) {
+      i = lo + (beta - Gm) * kWaves + wv;
+      ka = R - 1;
+    } else {
+      i = ib;
+      ka = -1;
+    }
+  }
+  __device__ int next() {
+    if (ka > 0) {
+      --ka;
+      return i + nV;
+    }
+    if (ka == 0) {
+      ka = -1;
+      return ib;
+    }
+    return i + W;
+  }
+};
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -659,13 +694,12 @@ __device__ __forceinline__ void stage_v(const KArgs& K, const KProj& P, int voff
   wave_sync();
 }
 
-// v of all n tokens of a segment as bf16 (hi, lo) pairs in the wave's LDS
-// rows, for products with packed bf16 B on the dot2 instructions: every fp32
-// value x (the ascending-slice sum) becomes hi = bf16(x), lo = bf16(x - hi),
-// so x = hi + lo to a relative 2^-17 and each product with a bf16 weight is
-// exact in fp32.  Layout per token and rank group g (16 dwords): for each
-// half h of the group's 16 ranks, 4 dwords of hi pairs (ranks 8h+2j,
-// 8h+2j+1) then 4 dwords of lo pairs.  Ranks >= r are zero.
+// v of the tokens of a chunk as packed bf16 pairs in the wave's LDS rows,
+// for products with packed bf16 B on the dot2 instructions: every fp32 value
+// (the ascending-slice sum) is rounded to bf16 once, as the MBGMM path rounds
+// its MFMA operand (relative 2^-9; the products and their sums stay fp32).
+// Layout per token and rank group g (8 dwords): pairs (ranks 2j, 2j+1),
+// j = 0..7.  Ranks >= r are zero.
 // The staging of M (token, rank pair) entries per lane, in steps: set up
 // the entries, load one round of SF slices, add it, store the pairs.  A
 // caller may issue the first round before other loads and add it later.
@@ -686,7 +720,7 @@ __device__ __forceinline__ void split_setup(SplitStage<M>& st, int p0, int np, i
     const int t = p / hp, kp = p - t * hp;  // pair kp = ranks 2kp, 2kp+1
     st.kk[m] = p < np ? 2 * kp : LORA_MAX_RANK;  // past the end: nothing loaded or stored
     st.e[m] = t * r + 2 * kp;
-    st.dst[m] = t * (G * 16) + (kp >> 3) * 16 + ((kp >> 2) & 1) * 8 + (kp & 3);
+    st.dst[m] = t * (G * 8) + kp;
     st.acc[m][0] = st.acc[m][1] = 0.0f;
   }
 }
@@ -719,14 +753,8 @@ __device__ __forceinline__ void split_add(SplitStage<M>& st) {
 template <int M>
 __device__ __forceinline__ void split_store(const SplitStage<M>& st, uint32_t* vs) {
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    if (st.kk[m] < LORA_MAX_RANK) {
-      const uint32_t hi = pack_bf2(st.acc[m][0], st.acc[m][1]);
-      const uint32_t lo = pack_bf2(st.acc[m][0] - bf_lo(hi), st.acc[m][1] - bf_hi(hi));
-      vs[st.dst[m]] = hi;
-      vs[st.dst[m] + 4] = lo;
-    }
-  }
+  for (int m = 0; m < M; ++m)
+    if (st.kk[m] < LORA_MAX_RANK) vs[st.dst[m]] = pack_bf2(st.acc[m][0], st.acc[m][1]);
 }
 
 template <int M>
@@ -755,16 +783,12 @@ __device__ __forceinline__ void stage_v_split(const KArgs& K, const KProj& P, in
 }
 
 // dot products of one 16-byte B vector (8 ranks of one column, packed bf16
-// pairs) with the split v of one token: 4 pairs x (hi, lo).
-__device__ __forceinline__ float dot_split(uint4 w, uint4 vh, uint4 vl, float acc) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, vh.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, vh.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, vh.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, vh.w), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, vl.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, vl.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, vl.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, vl.w), acc, false);
+// pairs) with the bf16 v of the same 8 ranks of one token.
+__device__ __forceinline__ float dot8(uint4 w, uint4 v, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, v.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, v.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, v.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, v.w), acc, false);
   return acc;
 }
 
@@ -989,15 +1013,21 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
         }
         load_batch(g0);
       }
-      uint4 vv[4];  // v of the current group: bf16 {hi 0-7, lo 0-7, hi 8-15, lo 8-15}; fp32 ranks 0-15
+      uint4 vv[4];  // v of the current group: bf16 ranks {0-7, 8-15}; fp32 ranks 0-15
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
         const int g = g0 + i / nsub;
         if (g >= G) continue;
         if (i % nsub == 0) {  // first pair of a group: its v, once
-          const uint4* vt = reinterpret_cast<const uint4*>(vs + t * rs + g * 16);
+          if constexpr (EPV == 8) {
+            const uint4* vt = reinterpret_cast<const uint4*>(reinterpret_cast<const uint32_t*>(vs) + t * (G * 8) + g * 8);
+            vv[0] = vt[0];
+            vv[1] = vt[1];
+          } else {
+            const uint4* vt = reinterpret_cast<const uint4*>(vs + t * rs + g * 16);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) vv[q] = vt[q];
+            for (int q = 0; q < 4; ++q) vv[q] = vt[q];
+          }
         }
         // masked in place: the masks do not depend on the token, so masking
         // the registers again for the next token changes nothing
@@ -1013,10 +1043,9 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
               w[c * (16 / EPV) + v] = kn >= EPV ? w[c * (16 / EPV) + v] : keep_first(w[c * (16 / EPV) + v], kn, E());
             }
         }
-        if constexpr (EPV == 8) {  // bf16: packed B against split v (see stage_v_split)
+        if constexpr (EPV == 8) {  // bf16: packed B against packed bf16 v (see stage_v_split)
 #pragma unroll
-          for (int c = 0; c < CPL; ++c)
-            acc[i][c] = dot_split(w[c * 2 + 1], vv[2], vv[3], dot_split(w[c * 2], vv[0], vv[1], acc[i][c]));
+          for (int c = 0; c < CPL; ++c) acc[i][c] = dot8(w[c * 2 + 1], vv[1], dot8(w[c * 2], vv[0], acc[i][c]));
         } else {
 #pragma unroll
           for (int k4 = 0; k4 < 4; ++k4)
@@ -1270,7 +1299,7 @@ __device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int 
   // K steps past the rank are skipped inside the body, so two variants cover
   // every rank; the choice is the same for the whole block (one segment)
   const int nks = ceil_div_i(r, KSTEP);
-  if (nks <= MAXKS / 4)  // bf16: one K step (r <= 32), so twice the columns per part
+  if (WIDE && nks <= MAXKS / 4)  // bf16: one K step (r <= 32), so twice the columns per part
     expand_mfma_body<E, MAXKS / 4, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
   else if (nks <= MAXKS / 2)
     expand_mfma_body<E, MAXKS / 2, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
@@ -1323,6 +1352,9 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
   // once for more columns.  (Covering the grid twice over, with narrower
   // items, left each block two or three items in a row, each one memory
   // round trip.)
+  int Gm = 0, R = 0;  // MBGMM blocks per XCD, MBGMM items per MBGMM block
+  int total_v = 0;
+  for (int p = 0; p < K.np; ++p) total_v += K.p[p].njs * (Uv + (K.p[p].Y != K.p[p].Yb ? ncopy : 0));
   if (Um > 0) {
     int wc = min(512, 1 << K.pw_log2), total = 0;
     for (;; wc >>= 1) {
@@ -1330,8 +1362,19 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
       for (int p = 0; p < K.np; ++p) total += ceil_div_i(K.p[p].d_out, kWaves * wc) * Um;
       if (wc <= 128 || total >= (int)gridDim.x) break;
     }
-    for (WaveWalk it(total, 0, 1); it.i < it.end; it.i += it.stride) {
-      int rem = it.i, p = 0;
+    // When the MBGMM items are a small share of the launch's items (a decode
+    // batch with a few hot adapters: under one in eight), they go to the
+    // first third of each XCD's blocks (one per CU), so the other waves start
+    // streaming MBGMV weights at once and the MBGMM items' round trips overlap
+    // them; otherwise (prefill, mixed batches) to every block.
+    const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
+    const int x = blockIdx.x % nx, beta = blockIdx.x / nx, G = gridDim.x / nx;
+    const int lo_m = (int)(((int64_t)total * x) / nx), end_m = (int)(((int64_t)total * (x + 1)) / nx);
+    const int m = end_m - lo_m;
+    Gm = m <= 0 ? 0 : 8 * (int64_t)total >= total_v ? G : min(max(G / 3, 1), m);
+    R = Gm > 0 ? ceil_div_i(6 * m, 10 * Gm) : 0;  // an MBGMM item took ~0.6 MBGMV item times
+    for (int i = beta < Gm ? lo_m + beta : end_m; i < end_m; i += Gm) {
+      int rem = i, p = 0;
       int nb = ceil_div_i(K.p[0].d_out, kWaves * wc);
       while (rem >= nb * Um) {
         rem -= nb * Um;
@@ -1345,13 +1388,11 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
       expand_mfma<E, WIDE>(K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[kWaves], vs_all[wave], wave, lane);
     }
   }
-  int total = 0;
-  for (int p = 0; p < K.np; ++p) total += K.p[p].njs * (Uv + (K.p[p].Y != K.p[p].Yb ? ncopy : 0));
-  WaveWalk it(total, wave);
+  TwoClassWalk it(total_v, Gm, R, wave);
   if (it.i >= it.end) return;
   ValuItem cur = fetch_valu_item<E>(K, it.i, Uv, ncopy);
   for (;;) {
-    const int ni = it.i + it.stride;
+    const int ni = it.next();
     const bool more = ni < it.end;
     ValuItem nxt;
     if (cur.copy) {
