@@ -236,35 +236,37 @@ __device__ __forceinline__ float wave_reduce_scatter32(float (&v)[32], int lane)
 // an adapter slice are read through the same L2.  Every wave walks its own
 // items: no work-group barrier couples the waves.
 struct WaveWalk {
-  int i, end, stride;
+  int i, end, stride, lo;
   // `walkers` items are taken per block at a time (kWaves: one per wave; 1:
   // whole-block items), `w` is this walker's index in the block.
   __device__ WaveWalk(int total, int w, int walkers = kWaves) {
     const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
     const int x = blockIdx.x % nx;
-    const int lo = (int)(((int64_t)total * x) / nx);
+    lo = (int)(((int64_t)total * x) / nx);
     end = (int)(((int64_t)total * (x + 1)) / nx);
     i = lo + (int)(blockIdx.x / nx) * walkers + w;
     stride = (gridDim.x / nx) * walkers;
   }
 };
 
-// The expand's MBGMV walk when the first Gm blocks of each XCD run the MBGMM
-// items: the waves of the other blocks take R rounds of the XCD's MBGMV
-// items among themselves (R: the MBGMV items that take as long as one
-// block's MBGMM items), then every wave takes items in turn.
+// The MBGMV walk when the first Wm waves of each XCD run the MBGMM items:
+// the other waves take R rounds of the XCD's MBGMV items among themselves (R:
+// the MBGMV items that take as long as one wave's MBGMM items), then every
+// wave takes items in turn.
 struct TwoClassWalk {
   int i, end, nV, W, ib, ka;  // ka: first-phase items left after the current one (-1: second phase)
-  __device__ TwoClassWalk(int total, int Gm, int R, int wv) {
+  __device__ TwoClassWalk(int total, int Wm, int R, int wv) {
     const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
-    const int x = blockIdx.x % nx, beta = blockIdx.x / nx, G = gridDim.x / nx;
+    const int x = blockIdx.x % nx, G = gridDim.x / nx;
+    const int w = (int)(blockIdx.x / nx) * kWaves + wv;  // walker index inside the XCD
     const int lo = (int)(((int64_t)total * x) / nx);
     end = (int)(((int64_t)total * (x + 1)) / nx);
     W = G * kWaves;
-    nV = (G - Gm) * kWaves;
-    ib = lo + R * nV + beta * kWaves + wv;
-    if (beta >= Gm && R > 0) {
-      i = lo + (beta - Gm) * kWaves + wv;
+    Wm = min(Wm, W);
+    nV = W - Wm;
+    ib = lo + R * nV + w;
+    if (w >= Wm && R > 0) {
+      i = lo + (w - Wm);
       ka = R - 1;
     } else {
       i = ib;
@@ -551,6 +553,9 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
   }
 }
 
+// MBGMV rounds one MBGMM shrink item is worth (measured: 2 and 4 were slower)
+constexpr int kShrinkMfmaRounds = 3;
+
 // WIDE: pages hold at least one whole 512-column slice, so every page
 // lookup of an item is wave-uniform; chosen by the host from the page width.
 template <class E, bool WIDE>
@@ -565,11 +570,22 @@ __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArg
   // first MBGMV item's metadata is requested before the MBGMM pass.
   int total_v = 0;
   for (int p = 0; p < K.np; ++p) total_v += K.p[p].nq * Uv;
-  WaveWalk iv(total_v, wave);
-  ShrinkItem cur;
-  if (iv.i < iv.end) cur = fetch_shrink_item<WIDE>(K, iv.i, Uv);
   int total = 0;
   for (int p = 0; p < K.np; ++p) total += K.p[p].nq * Um;
+  // The MBGMM items go to the first waves of each XCD's walk.  When they are
+  // a small share of the items (under one in eight: a decode batch's hot
+  // adapters), those waves skip the first rounds of MBGMV items: an MBGMM
+  // item is four rounds of loads against one for an MBGMV item.
+  int Wm = 0, R = 0;
+  if (total > 0 && 8 * (int64_t)total < total_v) {
+    WaveWalk im(total, wave);
+    const int m = im.end - im.lo;
+    Wm = min(m, im.stride);
+    R = kShrinkMfmaRounds * ceil_div_i(m, im.stride);
+  }
+  TwoClassWalk iv(total_v, Wm, R, wave);
+  ShrinkItem cur;
+  if (iv.i < iv.end) cur = fetch_shrink_item<WIDE>(K, iv.i, Uv);
   // Item order: projection-major, or -- when every projection of the launch
   // reads the same X -- projection-minor, so the siblings' items for one
   // (slice, item) run side by side and their X rows come from L2.
@@ -593,7 +609,7 @@ __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArg
   }
   if (iv.i >= iv.end) return;
   for (;;) {
-    const int ni = iv.i + iv.stride;
+    const int ni = iv.next();
     const bool more = ni < iv.end;
     ShrinkItem nxt;
     shrink_valu<E, WIDE>(K, K.p[cur.p], cur, lane, [&]() {
@@ -1388,7 +1404,7 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
       expand_mfma<E, WIDE>(K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[kWaves], vs_all[wave], wave, lane);
     }
   }
-  TwoClassWalk it(total_v, Gm, R, wave);
+  TwoClassWalk it(total_v, Gm * kWaves, R, wave);
   if (it.i >= it.end) return;
   ValuItem cur = fetch_valu_item<E>(K, it.i, Uv, ncopy);
   for (;;) {
