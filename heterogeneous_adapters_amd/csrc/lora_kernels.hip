@@ -344,9 +344,9 @@ __device__ __forceinline__ ShrinkItem fetch_shrink_item(const KArgs& K, int i, i
     u = rem - it.q * Uv;
   }
   const KProj& P = K.p[it.p];
-  const int s = cld(K.shr_item_v + u);
-  it.d0 = cld4(K.seg_desc + 2 * s);
-  it.d1 = cld4(K.seg_desc + 2 * s + 1);
+  const int4* dv = reinterpret_cast<const int4*>(K.shr_item_v) + 2 * u;  // the segment's descriptor
+  it.d0 = cld4(dv);
+  it.d1 = cld4(dv + 1);
   const int local = u - it.d1.y;
   const int n = it.d0.w;
   const int nch = ceil_div_i(n, kValuTokens);
@@ -849,9 +849,9 @@ __device__ __forceinline__ ValuItem fetch_valu_item(const KArgs& K, int i, int U
     it.local = u - Uv;
     return it;
   }
-  const int s = cld(K.exp_item_v + u);
-  it.d0 = cld4(K.seg_desc + 2 * s);
-  it.d1 = cld4(K.seg_desc + 2 * s + 1);
+  const int4* dv = reinterpret_cast<const int4*>(K.exp_item_v) + 2 * u;  // the segment's descriptor
+  it.d0 = cld4(dv);
+  it.d1 = cld4(dv + 1);
   it.local = u - it.d1.z;
   constexpr int CB = kValuSubBlocks * 64 * (4 / (int)sizeof(typename E::T));
   const int pw = 1 << K.pw_log2;
@@ -1527,13 +1527,27 @@ __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N,
       out.seg_adapter[si] = a;
       out.seg_indptr[si] = pre[0];
       out.v_indptr[si] = pre[2];
-      int32_t* shr = mf ? out.shr_item_m + pre[3] : out.shr_item_v + pre[4];
-      for (int i = 0; i < (mf ? vals[3] : vals[4]); ++i) shr[i] = si;
-      int32_t* exq = mf ? out.exp_item_m + pre[5] : out.exp_item_v + pre[6];
-      for (int i = 0; i < (mf ? vals[5] : vals[6]); ++i) exq[i] = si;
+      const int4 d0 = make_int4(a, r, pre[0], cnt);
+      const int4 d1 = make_int4(pre[2], mf ? pre[3] : pre[4], mf ? pre[5] : pre[6], __float_as_int(alpha[a]));
       int4* desc = reinterpret_cast<int4*>(out.seg_desc) + 2 * si;
-      desc[0] = make_int4(a, r, pre[0], cnt);
-      desc[1] = make_int4(pre[2], mf ? pre[3] : pre[4], mf ? pre[5] : pre[6], __float_as_int(alpha[a]));
+      desc[0] = d0;
+      desc[1] = d1;
+      if (mf) {
+        for (int i = 0; i < vals[3]; ++i) out.shr_item_m[pre[3] + i] = si;
+        for (int i = 0; i < vals[5]; ++i) out.exp_item_m[pre[5] + i] = si;
+      } else {  // MBGMV tables: the descriptor per item
+        static_assert(kValuItemInts == 8, "two int4 per MBGMV item");
+        int4* sv = reinterpret_cast<int4*>(out.shr_item_v) + 2 * pre[4];
+        for (int i = 0; i < vals[4]; ++i) {
+          sv[2 * i] = d0;
+          sv[2 * i + 1] = d1;
+        }
+        int4* ev = reinterpret_cast<int4*>(out.exp_item_v) + 2 * pre[6];
+        for (int i = 0; i < vals[6]; ++i) {
+          ev[2 * i] = d0;
+          ev[2 * i + 1] = d1;
+        }
+      }
       for (int c = 0; c < nchunk; ++c) hist[(int64_t)c * W + a] += pre[0];
     }
     __syncthreads();

@@ -85,8 +85,12 @@ constexpr int kNumCounts = 16;
 
 // The internal plan area: per-segment descriptors (2 x int4: {adapter,
 // rank, first token, tokens}, {v offset, first shrink item, first expand
-// item, alpha bits}) and the item -> segment tables of the two paths.
+// item, alpha bits}) and the item tables of the two paths.  The MBGMM
+// tables map an item to its segment; the MBGMV tables hold the segment's
+// descriptor itself (kValuItemInts int32 per item), so the walk of the many
+// short decode items reaches the descriptor in one load, not two.
 // Offsets in int32 units, each a multiple of 64.
+constexpr int kValuItemInts = 8;
 struct PlanLayout {
   long long seg_desc, shrink_mfma, shrink_valu, expand_mfma, expand_valu, total;
 };
@@ -99,11 +103,11 @@ LORA_HD inline PlanLayout plan_layout(int T, int N) {
   L.shrink_mfma = align64(8 * (smax > 0 ? smax : 1));
   // MBGMM shrink items <= 8*(T/16 + S) <= 9T; MBGMV <= 8*(T/2 + S) <= 12T
   L.shrink_valu = L.shrink_mfma + align64(9 * t + 1);
-  L.expand_mfma = L.shrink_valu + align64(12 * t + 1);
+  L.expand_mfma = L.shrink_valu + align64(kValuItemInts * (12 * t + 1));
   // MBGMM expand items <= T/16 + S <= 2T; MBGMV <= 4*(T/K + S) <= (4/K + 4)T
   // for chunks of K = kValuExpandTokens tokens
   L.expand_valu = L.expand_mfma + align64(2 * t + 1);
-  L.total = L.expand_valu + align64((4 / kValuExpandTokens + 4) * t + 1);
+  L.total = L.expand_valu + align64(kValuItemInts * ((4 / kValuExpandTokens + 4) * t + 1));
   return L;
 }
 
