@@ -452,30 +452,30 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, cons
     P.v[(int64_t)q * K.v_stride + d1.x + (int64_t)(tb + tt) * r + g * 16 + rr] = sum;
 }
 
-// MBGMM item (one wave): (segment, kMfmaShrinkTokens-token tile, rank group
-// g, slice q): C[rank][token] += A^T[rank][col] * X^T[col][token] over the
-// slice's 512 columns, as 16x16 MFMA tiles that share each A operand (so A,
-// re-read from L2 for every tile of the segment, is read once per 32 tokens),
+// MBGMM item (one wave): (segment, 16*NTT-token tile, rank group g, slice q):
+// C[rank][token] += A^T[rank][col] * X^T[col][token] over the slice's 512
+// columns, as NTT 16x16 MFMA tiles that share each A operand (so A, re-read
+// from L2 for every tile of the segment, is read once per 16*NTT tokens),
 // with the operands of 8 / NTT K steps requested before the first of their
-// MFMAs (four memory round trips per item).  The rank groups of a token tile are
-// consecutive items, so the tile's activations are re-read from the L2 that
-// holds them.
-template <class E, bool WIDE>
+// MFMAs (2*NTT memory round trips per item).  The rank groups of a token tile
+// are consecutive items, so the tile's activations are re-read from the L2
+// that holds them.
+template <class E, bool WIDE, int NTT>
 __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int q, int4 d0, int4 d1, int local,
                                             int lane) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
   constexpr int STEP = 4 * EPV;
   constexpr int NSTEP = kKSlice / STEP;
-  constexpr int NTT = kMfmaShrinkTokens / 16;  // 16-token MFMA tiles per item
+  constexpr int TILE = 16 * NTT;  // tokens per item
   constexpr int SIF = 8 / NTT;                 // K steps in flight: 8 (A + NTT X) operand pairs
   static_assert(NSTEP % SIF == 0, "steps in flight divide the slice");
   const int a = d0.x, r = d0.y, t0 = d0.z, n = d0.w;
   const int G = rank_groups(r);
   const int tt = local / G;
   const int g = local - tt * G;
-  const int tb = tt * kMfmaShrinkTokens;
-  const int nt = min(kMfmaShrinkTokens, n - tb);
+  const int tb = tt * TILE;
+  const int nt = min(TILE, n - tb);
   const int li = lane & 15, qq = lane >> 4;
   const int col0 = q * kKSlice;
   const int ncols = min(kKSlice, P.d_in - col0);  // a multiple of 8
@@ -605,7 +605,10 @@ __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArg
     }
     const int s = cld(K.shr_item_m + u);
     const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
-    shrink_mfma<E, WIDE>(K, K.p[p], q, d0, d1, u - d1.y, lane);
+    if (shrink_tile_tokens(d0.w) == kMfmaShrinkTokensLong)
+      shrink_mfma<E, WIDE, kMfmaShrinkTokensLong / 16>(K, K.p[p], q, d0, d1, u - d1.y, lane);
+    else
+      shrink_mfma<E, WIDE, kMfmaShrinkTokensShort / 16>(K, K.p[p], q, d0, d1, u - d1.y, lane);
   }
   if (iv.i >= iv.end) return;
   for (;;) {

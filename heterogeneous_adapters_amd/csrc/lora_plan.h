@@ -36,10 +36,12 @@ constexpr int kValuTokens = 2;            // tokens per MBGMV shrink item
 constexpr int kValuExpandTokens = LORA_VALU_EXPAND_TOKENS;  // tokens per MBGMV expand item (a chunk of the segment)
 constexpr int kCopyTokens = 8;            // rows per copy item (tokens without an adapter)
 constexpr int kMfmaExpandTokens = 16;     // tokens per MBGMM expand item (one tile)
-#ifndef LORA_MFMA_SHRINK_TOKENS
-#define LORA_MFMA_SHRINK_TOKENS 32
-#endif
-constexpr int kMfmaShrinkTokens = LORA_MFMA_SHRINK_TOKENS;  // tokens per MBGMM shrink item (16-token tiles sharing A)
+// Tokens per MBGMM shrink item (16-token MFMA tiles sharing each A operand):
+// 64 for segments of at least kMfmaLongSegment tokens (prefill sequences: A
+// is re-read from L2 once per 64 tokens), 32 for shorter ones (a decode
+// batch's hot adapters and prefill chunks of a mixed batch: items of half
+// the load rounds, twice as many).
+constexpr int kMfmaShrinkTokensShort = 32, kMfmaShrinkTokensLong = 64, kMfmaLongSegment = 512;
 constexpr int kProjsPerLaunch = 16;       // projection descriptors per launch
 constexpr int kSegChunk = 1024;           // tokens per segment-builder block
 #ifndef LORA_MFMA_MIN_TOKENS
@@ -57,6 +59,7 @@ LORA_HD inline int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 LORA_HD inline int rank_groups(int r) { return (r + 15) >> 4; }
 
 LORA_HD inline bool is_mfma_segment(int n) { return n >= kMfmaMinTokens; }
+LORA_HD inline int shrink_tile_tokens(int n) { return n >= kMfmaLongSegment ? kMfmaShrinkTokensLong : kMfmaShrinkTokensShort; }
 
 // Work items of one segment, per 512-column shrink slice or per expand
 // column block.  MBGMV shrink: (rank group, <= kValuTokens tokens); MBGMM
@@ -68,7 +71,7 @@ LORA_HD inline int shrink_items_valu(int n, int r) {
   return is_mfma_segment(n) ? 0 : rank_groups(r) * ceil_div_i(n, kValuTokens);
 }
 LORA_HD inline int shrink_items_mfma(int n, int r) {
-  return is_mfma_segment(n) ? rank_groups(r) * ceil_div_i(n, kMfmaShrinkTokens) : 0;
+  return is_mfma_segment(n) ? rank_groups(r) * ceil_div_i(n, shrink_tile_tokens(n)) : 0;
 }
 LORA_HD inline int valu_expand_parts(int r) { return rank_groups(r) == 1 ? 1 : rank_groups(r) == 2 ? 2 : 4; }
 LORA_HD inline int valu_expand_chunks(int n) { return ceil_div_i(n, kValuExpandTokens); }

@@ -139,6 +139,19 @@ def _tile_boundary_ids():
 
 _TILE_RANKS = [8, 16, 24, 32, 64, 128, 1, 40, 17, 96, 8, 16, 32, 64, 128]
 
+
+def _long_tile_ids():
+    """Adapters 0-6 hold 511, 512, 513, 575, 576, 577 and 639 tokens (both
+    sides of the segment length that switches the MBGMM shrink from 32- to
+    64-token items, and of its 64-token tiles), adapters 7-8 one and two
+    (MBGMV), interleaved by a seeded shuffle."""
+    counts = [511, 512, 513, 575, 576, 577, 639, 1, 2]
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    return np.random.default_rng(13).permutation(ids).astype(np.int32)
+
+
+_LONG_TILE_RANKS = [8, 16, 24, 32, 64, 128, 40, 16, 64]
+
 PARITY_CASES = {
     "cfg0": (0, {}),
     "cfg1": (1, {}),
@@ -158,6 +171,10 @@ PARITY_CASES = {
                                   page_width=256, projs=(("a", 1000, 1032), ("b", 1032, 520)))),
     "tile_lengths_f32": (2, dict(N=15, ranks_override=_TILE_RANKS, ids_override=_tile_boundary_ids(),
                                  page_width=256, dtype="f32", projs=(("a", 1000, 1032), ("b", 1032, 520)))),
+    "long_tile_lengths_bf16": (2, dict(N=9, ranks_override=_LONG_TILE_RANKS, ids_override=_long_tile_ids(),
+                                       page_width=512, projs=(("a", 1032, 520),))),
+    "long_tile_lengths_f32": (2, dict(N=9, ranks_override=_LONG_TILE_RANKS, ids_override=_long_tile_ids(),
+                                      page_width=256, dtype="f32", projs=(("a", 1032, 520),))),
     # continuous batching: prefill chunks (MBGMM) beside decode tokens (MBGMV)
     "mixed": (5, dict(nchunks=3, chunk_lo=40, chunk_hi=120, ndecode=300, N=50, page_width=512,
                       projs=(("a", 1024, 1536),))),
