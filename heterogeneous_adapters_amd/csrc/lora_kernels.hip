@@ -574,8 +574,9 @@ __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArg
   for (int p = 0; p < K.np; ++p) total += K.p[p].nq * Um;
   // The MBGMM items go to the first waves of each XCD's walk.  When they are
   // a small share of the items (under one in eight: a decode batch's hot
-  // adapters), those waves skip the first rounds of MBGMV items: an MBGMM
-  // item is four rounds of loads against one for an MBGMV item.
+  // adapters, whose segments are short enough for 32-token items), those
+  // waves skip the first rounds of MBGMV items: a 32-token MBGMM item is four
+  // rounds of loads against one for an MBGMV item.
   int Wm = 0, R = 0;
   if (total > 0 && 8 * (int64_t)total < total_v) {
     WaveWalk im(total, wave);
@@ -1371,7 +1372,7 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
   // once for more columns.  (Covering the grid twice over, with narrower
   // items, left each block two or three items in a row, each one memory
   // round trip.)
-  int Gm = 0, R = 0;  // MBGMM blocks per XCD, MBGMM items per MBGMM block
+  int Gm = 0, R = 0;  // MBGMM blocks per XCD; first MBGMV rounds the other blocks take alone
   int total_v = 0;
   for (int p = 0; p < K.np; ++p) total_v += K.p[p].njs * (Uv + (K.p[p].Y != K.p[p].Yb ? ncopy : 0));
   if (Um > 0) {

@@ -30,10 +30,10 @@ constexpr int kThreads = 256;             // work-group size (4 wave64)
 constexpr int kWaves = kThreads / 64;
 constexpr int kKSlice = 512;              // input columns per shrink item (one partial slice)
 constexpr int kValuTokens = 2;            // tokens per MBGMV shrink item
-#ifndef LORA_VALU_EXPAND_TOKENS
-#define LORA_VALU_EXPAND_TOKENS 2
-#endif
-constexpr int kValuExpandTokens = LORA_VALU_EXPAND_TOKENS;  // tokens per MBGMV expand item (a chunk of the segment)
+// Tokens per MBGMV expand item (a chunk of the segment).  Every token's
+// Y_base row is requested with the item's weights, so the chunk's rows live
+// in registers for the whole item: 2 fits beside 16 KiB of B, 4 spills.
+constexpr int kValuExpandTokens = 2;
 constexpr int kCopyTokens = 8;            // rows per copy item (tokens without an adapter)
 constexpr int kMfmaExpandTokens = 16;     // tokens per MBGMM expand item (one tile)
 // Tokens per MBGMM shrink item (16-token MFMA tiles sharing each A operand):
