@@ -68,6 +68,17 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 }
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Y is written once and read by nothing in the launch or the next one, so its
+// stores carry the non-temporal hint: they do not fill L2 and the MALL with
+// dirty lines that the next launch's weights and metadata would have to
+// displace (measured: the shrink after an expand 3.5 % faster, prefill 2 %).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void stg16_nt(void* p, uint4 u) {
+  __builtin_nontemporal_store(u32x4{u.x, u.y, u.z, u.w}, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void stg4_nt(void* p, uint32_t u) {
+  __builtin_nontemporal_store(u, reinterpret_cast<uint32_t*>(p));
+}
 
 // Loads of metadata that no kernel of the call writes (segments, page
 // tables), through the constant address space so that wave-uniform
@@ -873,8 +884,6 @@ __device__ __forceinline__ ValuItem fetch_valu_item(const KArgs& K, int i, int U
 // bf16 or one fp32), kept packed until used.
 template <class T>
 __device__ __forceinline__ uint32_t load_dword(const T* p) { return *reinterpret_cast<const uint32_t*>(p); }
-template <class T>
-__device__ __forceinline__ void store_dword(T* p, uint32_t u) { *reinterpret_cast<uint32_t*>(p) = u; }
 __device__ __forceinline__ float unpack_col(uint32_t u, int c, Bf16) { return c == 0 ? bf_lo(u) : bf_hi(u); }
 __device__ __forceinline__ float unpack_col(uint32_t u, int, F32) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t pack_cols(const float (&y)[2]) { return pack_bf2(y[0], y[1]); }
@@ -1095,7 +1104,7 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
         float y[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) y[c] = unpack_col(yb[sb], c, E()) + scale * acc[sb][c];
-        store_dword(Y + row * P.ldy + jc[sb], pack_cols(y));
+        stg4_nt(Y + row * P.ldy + jc[sb], pack_cols(y));
       }
     }
 #pragma unroll
@@ -1284,7 +1293,7 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
                            __float_as_uint(__uint_as_float(yb.z) + scale * c0[2]),
                            __float_as_uint(__uint_as_float(yb.w) + scale * c0[3]));
         }
-        *reinterpret_cast<uint4*>(Y + yrow[rd] * P.ldy + j0 + colp) = out;
+        stg16_nt(Y + yrow[rd] * P.ldy + j0 + colp, out);
       }
     }
     wave_sync();  // the rows are rewritten by the next part
@@ -1343,7 +1352,7 @@ __device__ __forceinline__ void expand_copy(const KArgs& K, const KProj& P, int 
 #pragma unroll
     for (int sb = 0; sb < kValuSubBlocks; ++sb) {
       const int j = (jb * kValuSubBlocks + sb) * SUBW + lane * CPL;
-      if (j < P.d_out) store_dword(Y + row * P.ldy + j, load_dword(Yb + row * P.ldyb + j));
+      if (j < P.d_out) stg4_nt(Y + row * P.ldy + j, load_dword(Yb + row * P.ldyb + j));
     }
   }
 }
