@@ -1517,10 +1517,18 @@ __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N,
     const int a = base + threadIdx.x;
     int cnt = 0;
     if (a < N) {
-      for (int c = 0; c < nchunk; ++c) {
-        const int h = hist[(int64_t)c * W + a];
-        hist[(int64_t)c * W + a] = cnt;  // prefix within this adapter's tokens
-        cnt += h;
+      // prefix within this adapter's tokens over the chunks; each batch's
+      // loads are issued before its stores, so a long batch (many chunks)
+      // costs one memory round trip per 16 chunks, not one per chunk
+      for (int c0 = 0; c0 < nchunk; c0 += 16) {
+        int h[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) h[j] = c0 + j < nchunk ? hist[(int64_t)(c0 + j) * W + a] : 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (c0 + j < nchunk) hist[(int64_t)(c0 + j) * W + a] = cnt;
+          cnt += h[j];
+        }
       }
     }
     const int r = (a < N && cnt > 0) ? rank[a] : 0;
@@ -1561,7 +1569,14 @@ __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N,
           ev[2 * i + 1] = d1;
         }
       }
-      for (int c = 0; c < nchunk; ++c) hist[(int64_t)c * W + a] += pre[0];
+      for (int c0 = 0; c0 < nchunk; c0 += 16) {
+        int h[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) h[j] = c0 + j < nchunk ? hist[(int64_t)(c0 + j) * W + a] : 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (c0 + j < nchunk) hist[(int64_t)(c0 + j) * W + a] = h[j] + pre[0];
+      }
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1576,12 +1591,19 @@ __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N,
     out.seg_indptr[S] = t_valid;
     out.v_indptr[S] = carry[2];
     int run = t_valid, n_invalid = 0;
-    for (int c = 0; c < nchunk; ++c) {
-      const int base_only = hist[(int64_t)c * W + N];
-      const int bad = hist[(int64_t)c * W + N + 1];
-      hist[(int64_t)c * W + N] = run;
-      run += base_only + bad;
-      n_invalid += bad;
+    for (int c0 = 0; c0 < nchunk; c0 += 16) {
+      int base_only[16], bad[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        base_only[j] = c0 + j < nchunk ? hist[(int64_t)(c0 + j) * W + N] : 0;
+        bad[j] = c0 + j < nchunk ? hist[(int64_t)(c0 + j) * W + N + 1] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (c0 + j < nchunk) hist[(int64_t)(c0 + j) * W + N] = run;
+        run += base_only[j] + bad[j];
+        n_invalid += bad[j];
+      }
     }
     out.counts[kCountS] = S;
     out.counts[kCountInvalid] = n_invalid;
