@@ -97,6 +97,8 @@ def parse():
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill + decode batch")
     ap.add_argument("--no-padded", action="store_true", help="skip the padded-to-max-rank baseline")
     ap.add_argument("--no-upload", action="store_true", help="skip the pool upload / overlap leg")
+    ap.add_argument("--no-stream-ref", action="store_true",
+                    help="skip the streaming reference (a plain device copy and read of 1 GiB)")
     ap.add_argument("--no-configs", action="store_true", help="skip the configs 1-2 leg (config 3 still runs)")
     ap.add_argument("--only", choices=["prefill", "configs"],
                     help="run only this leg and print its JSON (for profiling one workload)")
@@ -271,6 +273,42 @@ def configs_leg(which, steps, rotate_gb):
         del copies, projs, b0, w
         torch.cuda.empty_cache()
     return out
+
+
+def stream_reference(dev, reps=20):
+    """Streaming rates of this GPU measured in the same run, the secondary
+    reference for the GB/s figures: a plain device-to-device copy of 1 GiB
+    (1 GiB read + 1 GiB written) and a row-wise integer max over the same GiB
+    viewed as int32 (read only; a float sum reads at about half that rate),
+    HIP events around each call, medians over `reps` calls after warm-up."""
+    import numpy as np
+    import torch
+
+    n = CALIB_BYTES // 2
+    src = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(src)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    copy_ms = timed(lambda: dst.copy_(src))
+    rows = src.view(torch.int32).view(-1, 4096)
+    read_ms = timed(lambda: rows.amax(dim=1))
+    del src, dst, rows
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(2 * CALIB_BYTES / (copy_ms * 1e-3) / 1e9, 1),
+            "read_gbs": round(CALIB_BYTES / (read_ms * 1e-3) / 1e9, 1), "bytes": CALIB_BYTES, "reps": reps}
 
 
 def main():
@@ -789,6 +827,12 @@ def main():
         "graph_replay": graph,
         "setup_s": round(gen_s, 1),
     }
+    if not args.no_stream_ref:
+        log("streaming reference")
+        ref = stream_reference(dev)
+        ref["value_over_copy"] = round(gbs / ref["copy_gbs"], 4)
+        ref["value_over_read"] = round(gbs / ref["read_gbs"], 4)
+        out["stream_reference"] = ref
     print(json.dumps(out), flush=True)
     if args.calibration_copy:
         a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
