@@ -329,7 +329,6 @@ lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_
                          int32_t n_projs, const lora_adapters_t* adapters, const lora_pool_t* pool, void* ws,
                          size_t ws_bytes, void* stream) {
   if (T < 0 || n_projs < 0 || (n_projs > 0 && !projs)) return LORA_ERR_INVALID_ARG;
-  if (!ids && !segs) return LORA_ERR_INVALID_ARG;
   if (T > 0 && !ids && !segs) return LORA_ERR_INVALID_ARG;
   if (lora_status_t st = check_adapters(adapters)) return st;
   if (lora_status_t st = check_pool(pool)) return st;
@@ -357,7 +356,9 @@ lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_
   }
   char* hist = w + seg_total;
   char* vbase = hist + hist_bytes(T, adapters->num_adapters);
-  if (ids) {
+  // An empty batch is built whatever ids is (it needs none): a null ids
+  // then cannot leave the kernels reading counts of a buffer never built.
+  if (ids || T == 0) {
     if (lora_status_t e = build_into(ids, T, adapters, S, reinterpret_cast<int32_t*>(hist), st)) return e;
   }
   if (n_projs == 0) return LORA_OK;

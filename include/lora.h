@@ -214,7 +214,12 @@ lora_status_t lora_expand(const lora_proj_t* projs, int32_t n_projs, const lora_
  * expand, two kernel launches per group of up to 16 projections.
  *   ids != NULL, segs != NULL : build segments into *segs, then apply
  *   ids != NULL, segs == NULL : build segments inside the workspace
- *   ids == NULL, segs != NULL : reuse prebuilt segments
+ *   ids == NULL, segs != NULL : reuse prebuilt segments (built by
+ *                               lora_build_segments or an earlier call)
+ * T = 0 (the empty batch) needs neither ids nor segs: its segments are
+ * always built (into the workspace when segs is NULL), all counts zero, and
+ * nothing else is written.  Descriptor pointers must still
+ * be valid (non-null, aligned).
  * projs: host array of n_projs descriptors.  T must equal the segments' T.
  * ws: device workspace of lora_workspace_size(T, N, n_projs, max d_in) bytes.
  * Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED, WORKSPACE, HIP. */

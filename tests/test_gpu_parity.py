@@ -317,6 +317,44 @@ def test_in_place_equals_out_of_place():
     assert np.array_equal(Y0[0], Y1[0])
 
 
+def test_empty_batch():
+    """T = 0: every entry point accepts the empty batch, its kernels find no
+    items and nothing is written (the buffers of a real batch stand behind
+    the descriptors, so a stray row store would show).  torch hands an empty
+    ids tensor over as a null pointer, which lora_apply reads as "reuse
+    segments"; at T = 0 it builds them all the same, so a buffer holding a
+    stale flags word (every item count zero) comes back cleared."""
+    w = W.make_workload(2, dict(T=64, N=5, projs=(("a", 1024, 512), ("b", 512, 1024)), page_width=256),
+                        keep_dense=False)
+    b = batch.to_device(w)
+    for y in b.Y:
+        y.fill_(3.0)
+    projs = [b.proj(p, False) for p in range(w.n_projs)]
+    ids0 = b.ids[:0]
+    want = oracle.segments(w.ids[:0], w.ranks)
+    segs = lora.Segments(0, w.N)
+    ws = lora.workspace(0, w.N, w.n_projs, 1024)
+    segs.counts().zero_()
+    segs.counts()[lora.COUNT_FLAGS] = 5
+    lora.lora_apply(ids0, segs, 0, projs, b.adapters, b.pool, ws)
+    check_segments(segs.arrays(), want)
+    stride = lora.LORA_MAX_RANK
+    vs = [torch.zeros(lora.lora_v_slices(t.d_in) * stride, dtype=torch.float32, device="cuda") for t in w.tables]
+    segs.counts()[lora.COUNT_FLAGS] = 5
+    lora.lora_build_segments(ids0, b.adapters, segs, ws)
+    check_segments(segs.arrays(), want)
+    lora.lora_shrink(projs, b.adapters, segs, b.pool, vs, stride)
+    lora.lora_expand(projs, b.adapters, segs, b.pool, vs, 0, stride)
+    lora.lora_apply(None, segs, 0, projs, b.adapters, b.pool, ws)
+    lora.lora_apply(ids0, None, 0, projs, b.adapters, b.pool, lora.workspace(0, w.N, w.n_projs, 1024))
+    torch.cuda.synchronize()
+    check_segments(segs.arrays(), want)
+    for y in b.Y:
+        assert bool((y.float() == 3.0).all())
+    for v in vs:
+        assert bool((v == 0).all())
+
+
 def test_many_projections_in_one_call():
     """More projections than one launch holds: the call is split in groups."""
     w = W.make_workload(2, dict(T=64, N=5, projs=(("a", 256, 512),), layers=19, page_width=256),
