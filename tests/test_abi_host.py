@@ -33,6 +33,19 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, f), f
 
 
+def test_binding_constants_match_header():
+    txt = open(HEADERS[0]).read()
+    defs = dict(re.findall(r"^#define (LORA_[A-Z_0-9]+) \(?([^/\n]*?)\)?\s*(?:/\*.*)?$", txt, flags=re.M))
+    for name in ("LORA_MAX_RANK", "LORA_MAX_ADAPTERS", "LORA_KSLICE", "LORA_DTYPE_F32", "LORA_DTYPE_BF16"):
+        assert eval(defs[name].strip()) == getattr(lora, name), name
+    # an adapter count past the limit is refused before any device work
+    b = _Buf()
+    s = lora.lora_segments_t()
+    L = lora.lib()
+    assert L.lora_segments_size(8, lora.LORA_MAX_ADAPTERS) > 0
+    assert L.lora_segments_init(ctypes.c_void_p(b.p()), 1 << 14, 8, lora.LORA_MAX_ADAPTERS + 1, ctypes.byref(s)) == -1
+
+
 def test_status_strings():
     L = lora.lib()
     for code in range(-8, 1):

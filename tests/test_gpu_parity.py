@@ -101,7 +101,7 @@ def test_segments_bit_exact_configs(k):
 
 
 @pytest.mark.parametrize("case", ["T1", "all_base", "invalid_mix", "bad_rank", "one_adapter_long",
-                                  "many_adapters", "ragged_chunks"])
+                                  "many_adapters", "ragged_chunks", "max_adapters"])
 def test_segments_bit_exact_edges(case):
     rng = np.random.default_rng(hash(case) % 2 ** 31)
     if case == "T1":
@@ -120,9 +120,14 @@ def test_segments_bit_exact_edges(case):
     elif case == "many_adapters":
         ranks = rng.choice([8, 16, 32, 64], 5000).astype(np.int32)
         ids = rng.integers(0, 5000, 700).astype(np.int32)
-    else:
+    elif case == "ragged_chunks":
         ranks = rng.choice([1, 24, 128], 7).astype(np.int32)
         ids = rng.integers(0, 7, 2 * 1024 + 17).astype(np.int32)
+    else:  # the largest adapter count the ABI accepts: sparse ids, two hot adapters at both ends
+        N = lora.LORA_MAX_ADAPTERS
+        ranks = rng.integers(1, lora.LORA_MAX_RANK + 1, N).astype(np.int32)
+        ids = np.concatenate([rng.integers(0, N, 2500), np.full(300, N - 1), np.zeros(200), [-1, N, N + 5]])
+        ids = rng.permutation(ids.astype(np.int32)).astype(np.int32)
     print(f"segments edge {case}: T={len(ids)} N={len(ranks)}", flush=True)
     check_segments(_segments_gpu(ids, ranks), oracle.segments(ids, ranks))
 
@@ -175,6 +180,13 @@ PARITY_CASES = {
                                        page_width=512, projs=(("a", 1032, 520),))),
     "long_tile_lengths_f32": (2, dict(N=9, ranks_override=_LONG_TILE_RANKS, ids_override=_long_tile_ids(),
                                       page_width=256, dtype="f32", projs=(("a", 1032, 520),))),
+    # very wide projections: 65 and 41 split-K slices, the last 8 columns wide,
+    # and ragged last column blocks, on the wide-page bf16 and narrow-page fp32
+    # kernels, with MBGMV and MBGMM segments
+    "wide_dims_bf16": (2, dict(T=200, N=6, ranks_override=[1, 16, 33, 64, 128, 8], page_width=512,
+                               projs=(("a", 32776, 16392),))),
+    "wide_dims_f32": (2, dict(T=120, N=6, ranks_override=[1, 16, 33, 64, 128, 8], page_width=128,
+                              dtype="f32", projs=(("a", 20488, 12296),))),
     # continuous batching: prefill chunks (MBGMM) beside decode tokens (MBGMV)
     "mixed": (5, dict(nchunks=3, chunk_lo=40, chunk_hi=120, ndecode=300, N=50, page_width=512,
                       projs=(("a", 1024, 1536),))),
@@ -315,6 +327,28 @@ def test_in_place_equals_out_of_place():
     Y0, _ = gpu_apply(w, in_place=False)
     Y1, _ = gpu_apply(w, in_place=True)
     assert np.array_equal(Y0[0], Y1[0])
+
+
+def test_wide_f32_against_float64_definition():
+    """The fp32 oracle sums d_in products in sequence, so its own error grows
+    about as sqrt(d_in) * 2^-24: at d_in = 20488 it lies 9e-6 from the float64
+    value of the definition.  The HIP path (512-input partial sums added in
+    ascending order) is checked here against that float64 value directly."""
+    k, kw = PARITY_CASES["wide_dims_f32"]
+    w = W.make_workload(k, kw, keep_dense=True)
+    Ys, _ = gpu_apply(w)
+    X = np.asarray(w.X[0], np.float64)
+    Y64 = np.asarray(w.Y_base[0], np.float64).copy()
+    for t in range(w.T):
+        a = int(w.ids[t])
+        if 0 <= a < w.N:
+            A = np.asarray(w.A[0][a], np.float64)
+            B = np.asarray(w.B[0][a], np.float64)
+            Y64[t] += float(w.alpha[a]) / int(w.ranks[a]) * ((X[t] @ A) @ B)
+    err_gpu = rowwise_rel(W.as_f64(Ys[0], w.dtype), Y64)
+    err_oracle = rowwise_rel(W.as_f64(oracle_Y(w, 0), w.dtype), Y64)
+    print(f"  vs float64 definition: HIP {err_gpu:.3e}, oracle {err_oracle:.3e}", flush=True)
+    assert err_gpu < TOL["f32"]
 
 
 def test_empty_batch():
