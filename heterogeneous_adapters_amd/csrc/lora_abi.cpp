@@ -191,15 +191,36 @@ void mark_shared_x(KArgs& K) {
     if (K.p[i].X != K.p[0].X || K.p[i].ldx != K.p[0].ldx || K.p[i].d_in != K.p[0].d_in) K.xshare = 0;
 }
 
+// The size limits of every launch group of a call, checked before the call
+// enqueues anything (bounds as in run()).
+lora_status_t check_limits(const lora_proj_t* projs, int32_t n_projs, int32_t T, int dtype) {
+  if (T > LORA_MAX_TOKENS) return LORA_ERR_UNSUPPORTED;
+  const int cols = expand_cols(dtype == LORA_DTYPE_BF16);
+  for (int base = 0; base < n_projs; base += kProjsPerLaunch) {
+    int64_t bs = 0, be = 0;
+    for (int i = base; i < std::min(n_projs, base + kProjsPerLaunch); ++i) {
+      bs += (int64_t)lora_v_slices(projs[i].d_in) * (21LL * T + 2);
+      be += (int64_t)ceil_div_i(projs[i].d_out, cols) * (6LL * T + 2);
+    }
+    if (bs > LORA_MAX_LAUNCH_ITEMS || be > LORA_MAX_LAUNCH_ITEMS) return LORA_ERR_UNSUPPORTED;
+  }
+  return LORA_OK;
+}
+
 lora_status_t run(const KArgs& K, int dtype, bool do_shrink, bool do_expand, hipStream_t stream) {
-  const DeviceInfo* d = nullptr;
-  if (lora_status_t st = device_info(&d)) return st;
-  const int di = dtype == LORA_DTYPE_BF16 ? 1 : 0;
+  if (K.T > LORA_MAX_TOKENS) return LORA_ERR_UNSUPPORTED;
+  // upper bounds of the launch's item totals (MBGMM + MBGMV per slice or
+  // column block); the kernels index items with 32-bit ints
   int64_t bs = 0, be = 0;
   for (int p = 0; p < K.np; ++p) {
     bs += (int64_t)K.p[p].nq * (21LL * K.T + 2);
     be += (int64_t)K.p[p].njs * (6LL * K.T + 2);
   }
+  if ((do_shrink && bs > LORA_MAX_LAUNCH_ITEMS) || (do_expand && be > LORA_MAX_LAUNCH_ITEMS))
+    return LORA_ERR_UNSUPPORTED;
+  const DeviceInfo* d = nullptr;
+  if (lora_status_t st = device_info(&d)) return st;
+  const int di = dtype == LORA_DTYPE_BF16 ? 1 : 0;
   // items are per wave: kWaves items per work-group
   if (do_shrink && launch_shrink(K, dtype, grid_for(d->cus * d->occ_shrink[di], ceil_div64(bs, kWaves)), stream) !=
                        hipSuccess)
@@ -272,6 +293,7 @@ size_t lora_workspace_size(int32_t T, int32_t num_adapters, int32_t n_projs, int
 lora_status_t lora_build_segments(const int32_t* ids, int32_t T, const lora_adapters_t* adapters,
                                   const lora_segments_t* segs, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0 || (T > 0 && !ids)) return LORA_ERR_INVALID_ARG;
+  if (T > LORA_MAX_TOKENS) return LORA_ERR_UNSUPPORTED;
   if (lora_status_t st = check_adapters(adapters)) return st;
   if (lora_status_t st = check_segs(segs)) return st;
   if (T > segs->T || adapters->num_adapters > segs->num_adapters) return LORA_ERR_WORKSPACE;
@@ -296,6 +318,7 @@ static lora_status_t run_split(const lora_proj_t* projs, int32_t n_projs, const 
     if (lora_status_t st = check_proj(&projs[i])) return st;
     if (!v[i]) return LORA_ERR_INVALID_ARG;
   }
+  if (lora_status_t st = check_limits(projs, n_projs, segs->T, pool->dtype)) return st;
   for (int base = 0; base < n_projs; base += kProjsPerLaunch) {
     KArgs K;
     memset(&K, 0, sizeof K);
@@ -330,6 +353,7 @@ lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_
                          size_t ws_bytes, void* stream) {
   if (T < 0 || n_projs < 0 || (n_projs > 0 && !projs)) return LORA_ERR_INVALID_ARG;
   if (T > 0 && !ids && !segs) return LORA_ERR_INVALID_ARG;
+  if (T > LORA_MAX_TOKENS) return LORA_ERR_UNSUPPORTED;
   if (lora_status_t st = check_adapters(adapters)) return st;
   if (lora_status_t st = check_pool(pool)) return st;
   if (segs) {
@@ -341,6 +365,7 @@ lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_
     if (lora_status_t st = check_proj(&projs[i])) return st;
     max_d_in = std::max(max_d_in, projs[i].d_in);
   }
+  if (lora_status_t st = check_limits(projs, n_projs, T, pool->dtype)) return st;
   if (!ws) return LORA_ERR_INVALID_ARG;
   if (ws_bytes < lora_workspace_size(T, adapters->num_adapters, n_projs, max_d_in)) return LORA_ERR_WORKSPACE;
   if (!aligned16(ws)) return LORA_ERR_ALIGNMENT;

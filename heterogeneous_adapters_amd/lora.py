@@ -20,6 +20,8 @@ from .build import LIB_PATH
 LORA_DTYPE_F32, LORA_DTYPE_BF16 = 0, 1
 LORA_MAX_RANK = 128
 LORA_MAX_ADAPTERS = 1 << 20
+LORA_MAX_TOKENS = (1 << 24) - 1
+LORA_MAX_LAUNCH_ITEMS = 1 << 30
 LORA_KSLICE = 512
 COUNT_S, COUNT_INVALID, COUNT_T_VALID, COUNT_V_TOTAL, COUNT_FLAGS = 0, 1, 2, 3, 8
 N_COUNTS = 16

@@ -59,7 +59,7 @@ typedef int32_t lora_status_t;
 #define LORA_ERR_PAGE_RANGE (-3)  /* page id outside the pool (validator) */
 #define LORA_ERR_WORKSPACE (-4)   /* workspace or segment buffer too small */
 #define LORA_ERR_HIP (-5)         /* a HIP runtime call or kernel launch failed */
-#define LORA_ERR_UNSUPPORTED (-6) /* unknown dtype, page geometry, too many projections */
+#define LORA_ERR_UNSUPPORTED (-6) /* unknown dtype, page geometry, batch past the size limits */
 #define LORA_ERR_ALIGNMENT (-7)   /* pointer or leading dimension not 16-byte aligned */
 #define LORA_ERR_POOL_FULL (-8)   /* too few evictable pages in the pool (lora_pool.h) */
 
@@ -70,6 +70,16 @@ typedef int32_t lora_status_t;
 #define LORA_MAX_RANK 128
 #define LORA_KSLICE 512      /* input columns per shrink partial sum */
 #define LORA_MAX_ADAPTERS (1 << 20)
+/* Size limits of one call (32-bit indices inside the kernels): T tokens with
+ * T * LORA_MAX_RANK < 2^31, and per launch group of up to 16 projections at
+ * most LORA_MAX_LAUNCH_ITEMS work items, bounded on the host by
+ *   sum over the group of ceil(d_in/512) * (21 T + 2)          (shrink)
+ *   sum over the group of ceil(d_out/cols) * (6 T + 2)         (expand)
+ * with cols = 512 (bf16) or 256 (fp32).  Past either limit a call returns
+ * LORA_ERR_UNSUPPORTED before any device work; split the batch or pass fewer
+ * projections per call. */
+#define LORA_MAX_TOKENS ((1 << 24) - 1)
+#define LORA_MAX_LAUNCH_ITEMS (1 << 30)
 
 /* Adapter set: one rank and one alpha per adapter, shared by every layer and
  * projection (each sequence's adapter has its own rank r_i, [MLSP]

@@ -36,7 +36,8 @@ def test_library_exports_every_declared_function():
 def test_binding_constants_match_header():
     txt = open(HEADERS[0]).read()
     defs = dict(re.findall(r"^#define (LORA_[A-Z_0-9]+) \(?([^/\n]*?)\)?\s*(?:/\*.*)?$", txt, flags=re.M))
-    for name in ("LORA_MAX_RANK", "LORA_MAX_ADAPTERS", "LORA_KSLICE", "LORA_DTYPE_F32", "LORA_DTYPE_BF16"):
+    for name in ("LORA_MAX_RANK", "LORA_MAX_ADAPTERS", "LORA_KSLICE", "LORA_DTYPE_F32", "LORA_DTYPE_BF16",
+                 "LORA_MAX_TOKENS", "LORA_MAX_LAUNCH_ITEMS"):
         assert eval(defs[name].strip()) == getattr(lora, name), name
     # an adapter count past the limit is refused before any device work
     b = _Buf()
@@ -150,6 +151,51 @@ def test_other_rejections():
     s2 = lora.lora_segments_t()
     assert L.lora_segments_init(ctypes.c_void_p(b.p(4)), 1 << 14, 8, 4, r(s2)) == -7
     assert L.lora_segments_init(ctypes.c_void_p(b.p()), 16, 8, 4, r(s2)) == -4
+
+
+def test_size_limits_refused_before_device_work():
+    """Past LORA_MAX_TOKENS, or past LORA_MAX_LAUNCH_ITEMS in any launch group,
+    every entry point returns UNSUPPORTED while validating its arguments (the
+    descriptors point at host memory: nothing is dereferenced or launched)."""
+    b = _Buf()
+    L = lora.lib()
+    r = ctypes.byref
+    v = ctypes.c_void_p(b.p())
+    vs = (ctypes.c_void_p * 16)(*([b.p()] * 16))
+    ad = lora.lora_adapters_t(b.p(), b.p(64), 4)
+    pool = lora.lora_pool_t(b.p(), 4, 512, lora.LORA_DTYPE_BF16)
+
+    def proj(d_in, d_out):
+        return lora.lora_proj_t(b.p(), d_in, b.p(), d_out, b.p(), d_out, d_in, d_out, b.p(), b.p(), b.p(), b.p())
+
+    def segs(T):
+        return lora.lora_segments_t(T, 4, *([b.p()] * 6))
+
+    big = lora.LORA_MAX_TOKENS + 1
+    one = (lora.lora_proj_t * 1)(proj(4096, 4096))
+    assert L.lora_build_segments(v, big, r(ad), r(segs(big)), v, 1 << 40, None) == -6
+    assert L.lora_apply(v, None, big, one, 1, r(ad), r(pool), v, 1 << 40, None) == -6
+    assert L.lora_shrink(one, 1, r(ad), r(segs(big)), r(pool), vs, big * 128, None) == -6
+    assert L.lora_expand(one, 1, r(ad), r(segs(big)), r(pool), vs, 0, big * 128, None) == -6
+    # 1M tokens: one 4096 x 4096 projection fits (the call goes on to the
+    # workspace check); 16 projections of 4096 -> 11008 exceed the expand's
+    # item limit, 16 of 11008 -> 4096 the shrink's
+    T = 1 << 20
+    assert L.lora_apply(v, None, T, one, 1, r(ad), r(pool), v, 64, None) == -4
+    up = (lora.lora_proj_t * 16)(*[proj(4096, 11008)] * 16)
+    down = (lora.lora_proj_t * 16)(*[proj(11008, 4096)] * 16)
+    assert 16 * 22 * (6 * T + 2) > lora.LORA_MAX_LAUNCH_ITEMS
+    assert 16 * 22 * (21 * T + 2) > lora.LORA_MAX_LAUNCH_ITEMS
+    for arr in (up, down):
+        assert L.lora_apply(v, None, T, arr, 16, r(ad), r(pool), v, 1 << 40, None) == -6
+    assert L.lora_expand(up, 16, r(ad), r(segs(T)), r(pool), vs, 0, T * 128, None) == -6
+    assert L.lora_shrink(down, 16, r(ad), r(segs(T)), r(pool), vs, T * 128, None) == -6
+    # the second group of a 17-projection call is over the limit: refused
+    # before the first group (or the segment build) is enqueued
+    mix = (lora.lora_proj_t * 17)(*([proj(512, 512)] * 16 + [proj(11008, 4096)]))
+    T2 = 2_800_000
+    assert 22 * (21 * T2 + 2) > lora.LORA_MAX_LAUNCH_ITEMS >= 16 * 1 * (21 * T2 + 2)
+    assert L.lora_apply(v, None, T2, mix, 17, r(ad), r(pool), v, 1 << 40, None) == -6
 
 
 def test_validate_tables():
