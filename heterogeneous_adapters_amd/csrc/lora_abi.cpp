@@ -263,12 +263,13 @@ const char* lora_status_string(lora_status_t s) {
 int32_t lora_v_slices(int32_t d_in) { return d_in <= 0 ? 0 : ceil_div_i(d_in, LORA_KSLICE); }
 
 size_t lora_segments_size(int32_t T, int32_t num_adapters) {
-  if (T < 0 || num_adapters < 1) return 0;
+  if (T < 0 || T > LORA_MAX_TOKENS || num_adapters < 1 || num_adapters > LORA_MAX_ADAPTERS) return 0;
   return seg_sizes(T, num_adapters).total;
 }
 
 lora_status_t lora_segments_init(void* buf, size_t bytes, int32_t T, int32_t num_adapters, lora_segments_t* out) {
   if (!buf || !out || T < 0 || num_adapters < 1 || num_adapters > LORA_MAX_ADAPTERS) return LORA_ERR_INVALID_ARG;
+  if (T > LORA_MAX_TOKENS) return LORA_ERR_UNSUPPORTED;
   if (!aligned16(buf)) return LORA_ERR_ALIGNMENT;
   const SegSizes z = seg_sizes(T, num_adapters);
   if (bytes < z.total) return LORA_ERR_WORKSPACE;
@@ -285,7 +286,9 @@ lora_status_t lora_segments_init(void* buf, size_t bytes, int32_t T, int32_t num
 }
 
 size_t lora_workspace_size(int32_t T, int32_t num_adapters, int32_t n_projs, int32_t max_d_in) {
-  if (T < 0 || num_adapters < 1 || n_projs < 0 || max_d_in < 0) return 0;
+  if (T < 0 || T > LORA_MAX_TOKENS || num_adapters < 1 || num_adapters > LORA_MAX_ADAPTERS || n_projs < 0 ||
+      max_d_in < 0)
+    return 0;
   return seg_sizes(T, num_adapters).total + hist_bytes(T, num_adapters) +
          (size_t)std::min(n_projs, kProjsPerLaunch) * v_bytes_per_proj(T, max_d_in);
 }

@@ -175,15 +175,16 @@ typedef struct {
 
 /* Bytes of the device buffer that holds segments for T tokens and
  * num_adapters adapters. */
-size_t lora_segments_size(int32_t T, int32_t num_adapters);
+size_t lora_segments_size(int32_t T, int32_t num_adapters);  /* 0 outside the limits */
 
 /* Fill *out with pointers carved from `buf` (device, `bytes` long, 16-byte
- * aligned).  Enqueues nothing.  Errors: INVALID_ARG, WORKSPACE. */
+ * aligned).  Enqueues nothing.  Errors: INVALID_ARG, ALIGNMENT, WORKSPACE,
+ * UNSUPPORTED (T > LORA_MAX_TOKENS). */
 lora_status_t lora_segments_init(void* buf, size_t bytes, int32_t T, int32_t num_adapters,
                                  lora_segments_t* out);
 
 /* Workspace bytes for lora_build_segments and lora_apply with n_projs
- * projections whose largest input width is max_d_in. */
+ * projections whose largest input width is max_d_in (0 outside the limits). */
 size_t lora_workspace_size(int32_t T, int32_t num_adapters, int32_t n_projs, int32_t max_d_in);
 
 /* Number of shrink partial slices for an input width: ceil(d_in / 512). */
@@ -193,7 +194,8 @@ int32_t lora_v_slices(int32_t d_in);
  * deterministic stable counting sort; [MLSP] SGMV grouping).  ids: device
  * [T].  segs: laid out by lora_segments_init with capacity >= (T, N).  The
  * result depends only on ids and ranks; build once per batch and reuse for
- * every layer and projection.  Errors: INVALID_ARG, WORKSPACE, HIP. */
+ * every layer and projection.  Errors: INVALID_ARG, WORKSPACE, UNSUPPORTED,
+ * HIP. */
 lora_status_t lora_build_segments(const int32_t* ids, int32_t T, const lora_adapters_t* adapters,
                                   const lora_segments_t* segs, void* ws, size_t ws_bytes,
                                   void* stream);

@@ -172,6 +172,11 @@ def test_size_limits_refused_before_device_work():
         return lora.lora_segments_t(T, 4, *([b.p()] * 6))
 
     big = lora.LORA_MAX_TOKENS + 1
+    assert L.lora_segments_size(big, 4) == 0 and L.lora_workspace_size(big, 4, 1, 4096) == 0
+    assert L.lora_segments_size(lora.LORA_MAX_TOKENS, 4) > 0
+    assert L.lora_segments_size(8, lora.LORA_MAX_ADAPTERS + 1) == 0
+    s = lora.lora_segments_t()
+    assert L.lora_segments_init(ctypes.c_void_p(b.p()), 1 << 14, big, 4, r(s)) == -6
     one = (lora.lora_proj_t * 1)(proj(4096, 4096))
     assert L.lora_build_segments(v, big, r(ad), r(segs(big)), v, 1 << 40, None) == -6
     assert L.lora_apply(v, None, big, one, 1, r(ad), r(pool), v, 1 << 40, None) == -6
