@@ -187,6 +187,12 @@ PARITY_CASES = {
                                projs=(("a", 32776, 16392),))),
     "wide_dims_f32": (2, dict(T=120, N=6, ranks_override=[1, 16, 33, 64, 128, 8], page_width=128,
                               dtype="f32", projs=(("a", 20488, 12296),))),
+    # the narrowest projections the ABI accepts (8 columns: one 16-byte bf16
+    # row, a lone ragged slice / column block), MBGMV and MBGMM segments
+    "min_dims_bf16": (2, dict(T=300, N=7, ranks_override=[1, 4, 24, 40, 17, 128, 8], page_width=64,
+                              projs=(("a", 8, 8), ("b", 8, 1032), ("c", 1032, 8)))),
+    "min_dims_f32": (2, dict(T=300, N=7, ranks_override=[1, 4, 24, 40, 17, 128, 8], page_width=256,
+                             dtype="f32", projs=(("a", 8, 8), ("b", 8, 1032), ("c", 1032, 8)))),
     # continuous batching: prefill chunks (MBGMM) beside decode tokens (MBGMV)
     "mixed": (5, dict(nchunks=3, chunk_lo=40, chunk_hi=120, ndecode=300, N=50, page_width=512,
                       projs=(("a", 1024, 1536),))),
@@ -349,6 +355,18 @@ def test_wide_f32_against_float64_definition():
     err_oracle = rowwise_rel(W.as_f64(oracle_Y(w, 0), w.dtype), Y64)
     print(f"  vs float64 definition: HIP {err_gpu:.3e}, oracle {err_oracle:.3e}", flush=True)
     assert err_gpu < TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_alpha_returns_base_exactly(dtype):
+    """alpha = 0 scales every adapter's update by zero, so Y = Y_base bit for
+    bit on both paths (the weights are finite)."""
+    w = W.make_workload(2, dict(T=200, N=12, ranks_override=[8, 64, 128, 1, 24, 16] * 2, page_width=256,
+                                dtype=dtype, alpha_override=[0.0] * 12, projs=(("a", 1032, 744),)), keep_dense=False)
+    seg = oracle.segments(w.ids, w.ranks)
+    assert max(np.diff(seg["seg_indptr"])) >= 16 and min(np.diff(seg["seg_indptr"])) < 16
+    Ys, _ = gpu_apply(w)
+    assert np.array_equal(Ys[0], w.Y_base[0])
 
 
 def test_empty_batch():
