@@ -358,6 +358,42 @@ def test_wide_f32_against_float64_definition():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strided_rows_match_contiguous(dtype):
+    """Projections whose rows are column slices of wider tensors: X inside
+    padded rows (ldx = d_in + 24), Y_base and Y slices of one fused q/k/v
+    output (ldy = 3 d_out, plus 8 pad columns for Y).  Y is bit-identical to
+    the run on contiguous rows, in and out of place, and no column outside
+    the slices is written."""
+    d_in, d_out = 1032, 520
+    w = W.make_workload(2, dict(T=300, N=9, ranks_override=[8, 16, 64, 24, 1, 32, 128, 40, 8], page_width=256,
+                                dtype=dtype, projs=(("q", d_in, d_out), ("k", d_in, d_out), ("v", d_in, d_out))),
+                        keep_dense=False)
+    Yref, _ = gpu_apply(w)
+    for in_place in (False, True):
+        b = batch.to_device(w)
+        T, dt = w.T, b.X[0].dtype
+        Xw = [torch.zeros(T, d_in + 24, dtype=dt, device="cuda") for _ in range(3)]
+        Ybw = torch.empty(T, 3 * d_out, dtype=dt, device="cuda")
+        Yw = torch.full((T, 3 * d_out + 8), 5.0, dtype=dt, device="cuda")
+        for p in range(3):
+            Xw[p][:, 8:8 + d_in] = b.X[p]
+            Ybw[:, p * d_out:(p + 1) * d_out] = b.Y_base[p]
+        out = Ybw if in_place else Yw
+        projs = [lora.Proj(Xw[p][:, 8:8 + d_in], Ybw[:, p * d_out:(p + 1) * d_out],
+                           out[:, p * d_out:(p + 1) * d_out], *b.tables[p]) for p in range(3)]
+        assert projs[0].c.ldx == d_in + 24 and projs[0].c.ldyb == 3 * d_out
+        assert projs[0].c.ldy == (3 * d_out if in_place else 3 * d_out + 8)
+        segs = lora.Segments(T, w.N)
+        lora.lora_apply(b.ids, segs, T, projs, b.adapters, b.pool, lora.workspace(T, w.N, 3, d_in))
+        torch.cuda.synchronize()
+        for p in range(3):
+            got = batch.device_to_host(out[:, p * d_out:(p + 1) * d_out])
+            assert np.array_equal(got, Yref[p]), (in_place, p)
+        if not in_place:
+            assert bool((Yw[:, 3 * d_out:].float() == 5.0).all())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_alpha_returns_base_exactly(dtype):
     """alpha = 0 scales every adapter's update by zero, so Y = Y_base bit for
     bit on both paths (the weights are finite)."""
