@@ -394,6 +394,40 @@ def test_strided_rows_match_contiguous(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_page_ids_outside_the_pool_read_as_zero(dtype):
+    """A page id outside the pool (here num_pages + 3 in an A table and -1 in
+    a B table, for the hottest adapter (MBGMM path) and for the one with the
+    fewest tokens (MBGMV path)) is read as a page of zeros and sets LORA_FLAG_PAGE_RANGE; no
+    access leaves the pool.  Expected Y: the oracle on the same tables with
+    those ids pointing at an appended all-zero page."""
+    import dataclasses
+    w = W.make_workload(2, dict(T=300, N=9, ranks_override=[8, 16, 64, 24, 40, 32, 128, 17, 8], page_width=256,
+                                dtype=dtype, projs=(("a", 1032, 744),)), keep_dense=False)
+    seg = oracle.segments(w.ids, w.ranks)
+    cnt = np.diff(seg["seg_indptr"])
+    hot = int(seg["seg_adapter"][np.argmax(cnt)])
+    cold = int(seg["seg_adapter"][np.argmin(cnt)])
+    assert cnt.max() >= 16 > cnt.min() and hot != cold
+    t = w.tables[0]
+    bad, zero = dataclasses.replace(t), dataclasses.replace(t)
+    for f in ("a_pages", "b_pages"):
+        setattr(bad, f, getattr(t, f).copy())
+        setattr(zero, f, getattr(t, f).copy())
+    for a, k in ((hot, 1), (cold, 0)):
+        ia, ib = int(t.a_indptr[a]) + k, int(t.b_indptr[a + 1]) - 1 - k
+        bad.a_pages[ia], bad.b_pages[ib] = w.num_pages + 3, -1
+        zero.a_pages[ia] = zero.b_pages[ib] = w.num_pages
+    pool0 = np.concatenate([w.pool, np.zeros((1, w.pool.shape[1]), w.pool.dtype)])
+    want = oracle.apply(w.X[0], w.Y_base[0], w.ids, w.ranks, w.alpha, zero, pool0, w.page_width, w.dtype)
+    plain = oracle_Y(w, 0)
+    touched = (w.ids == hot) | (w.ids == cold)
+    assert not np.array_equal(want[touched], plain[touched])  # the zeroed pages matter
+    Ys, segs = gpu_apply(dataclasses.replace(w, tables=[bad]))
+    assert segs["flags"] & 1
+    assert rowwise_rel(W.as_f64(Ys[0], w.dtype), W.as_f64(want, w.dtype)) < TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_alpha_returns_base_exactly(dtype):
     """alpha = 0 scales every adapter's update by zero, so Y = Y_base bit for
     bit on both paths (the weights are finite)."""
