@@ -428,6 +428,23 @@ def test_page_ids_outside_the_pool_read_as_zero(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_invalid_ranks_leave_base_rows(dtype):
+    """Adapters whose rank lies outside [1, 128] (0, 129, -4, 200) are
+    counted invalid: their tokens' rows equal Y_base bit for bit, their page
+    tables are never read, and the other tokens match the oracle."""
+    import dataclasses
+    w = W.make_workload(2, dict(T=300, N=6, ranks_override=[8, 8, 8, 16, 8, 64], page_width=256, dtype=dtype,
+                                projs=(("a", 1032, 744),)), keep_dense=False)
+    w = dataclasses.replace(w, ranks=np.array([8, 0, 129, 16, -4, 200], np.int32))
+    Ys, segs = gpu_apply(w)
+    check_segments(segs, oracle.segments(w.ids, w.ranks))
+    bad = np.isin(w.ids, [1, 2, 4, 5])
+    assert bad.any() and segs["n_invalid"] == int(bad.sum())
+    assert np.array_equal(Ys[0][bad], w.Y_base[0][bad])
+    assert rowwise_rel(W.as_f64(Ys[0], w.dtype), W.as_f64(oracle_Y(w, 0), w.dtype)) < TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_alpha_returns_base_exactly(dtype):
     """alpha = 0 scales every adapter's update by zero, so Y = Y_base bit for
     bit on both paths (the weights are finite)."""
