@@ -32,7 +32,9 @@ MUTANTS = [
     ("bf16 ties away from zero", "(rest == 0x8000u && (keep & 1u))", "(rest == 0x8000u)"),
     ("segments in descending adapter id", "for (int32_t a = 0; a < N; ++a) {\n    int32_t cnt = 0;",
      "for (int32_t a = N - 1; a >= 0; --a) {\n    int32_t cnt = 0;"),
-    ("v offsets without the rank", "v += (int64_t)cnt * rank[a];", "v += (int64_t)cnt;"),
+    # V_total (which sizes v) stays right, the segment offsets come out low,
+    # so every write lands at or below its true position
+    ("v offsets short by the token count", "v_indptr[S + 1] = (int32_t)v;", "v_indptr[S + 1] = (int32_t)(v - cnt);"),
     ("base-only tokens counted invalid", "if (ids[t] != -1) ++n_invalid;", "++n_invalid;"),
 ]
 
