@@ -129,6 +129,15 @@ def groups_for(n_layers, names, mode):
     return out
 
 
+PARITY_TOL = 1e-2  # bf16: row-wise infinity-norm relative error against the oracle
+
+
+def fail(msg: str) -> None:
+    """End the run without a headline (non-zero exit)."""
+    print(f"bench.py: FAILED: {msg}", file=sys.stderr, flush=True)
+    sys.exit(3)
+
+
 def log(msg: str) -> None:
     """Progress on stderr (stdout carries only the JSON line)."""
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -402,7 +411,7 @@ def main():
     call_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in evs])  # [steps][calls]
     seg = segs.arrays()
     if seg["flags"] != 0:
-        raise RuntimeError(f"device flags {seg['flags']}")
+        fail(f"device flags {seg['flags']} after the timed steps")
 
     log("eager steps timed; per-kernel leg")
     # per-kernel leg: the same groups through lora_shrink / lora_expand (the
@@ -481,6 +490,37 @@ def main():
                  "replays_checked_bit_exact": checked}
         del cg
 
+    log("sampled parity of every projection")
+    # Parity gate, part 1: every one of the 224 projections on sampled tokens
+    # (random ones, the hottest adapter's, singletons), each computed by the
+    # oracle token by token from the pages those tokens use.  Part 2 is the
+    # whole-layer comparison of the CPU-baseline leg.  A failure of either (or
+    # a device flag) ends the run without a headline.
+    import oracle
+    rng = np.random.default_rng(0)
+    cnt_ids = np.bincount(dw.ids[dw.ids >= 0], minlength=N)
+    hot = np.nonzero(dw.ids == cnt_ids.argmax())[0]
+    single = np.nonzero((dw.ids >= 0) & (cnt_ids[np.maximum(dw.ids, 0)] == 1))[0]
+    sample = np.unique(np.concatenate([rng.choice(T, 16, replace=False), hot[:8], single[:8]]))
+    sub_ids = dw.ids[sample]
+    parity_sampled = 0.0
+    nl_all = W.CONFIGS[4]["layers"]
+    for l in range(nl_all):
+        idx = list(range(l * 7, l * 7 + 7))
+        hpool, htabs = host_subset(dw.pool, [dw.tables[i] for i in idx], np.unique(sub_ids[sub_ids >= 0]))
+        for j, i in enumerate(idx):
+            ref = W.as_f64(oracle.apply(tensor_bits(dw.X[i])[sample], tensor_bits(dw.Y_base[i])[sample], sub_ids,
+                                        dw.ranks, dw.alpha, htabs[j], hpool, dw.page_width, "bf16"), "bf16")
+            got = W.as_f64(tensor_bits(Y[i])[sample], "bf16")
+            err = float((np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max()) \
+                if np.isfinite(got).all() else float("inf")
+            parity_sampled = max(parity_sampled, err)
+        del hpool, htabs
+    parity = {"tolerance": PARITY_TOL, "sampled_tokens": int(len(sample)), "sampled_projections": len(dw.tables),
+              "sampled_max_rowwise_rel_err": float(f"{parity_sampled:.3e}")}
+    if parity_sampled >= PARITY_TOL:
+        fail(f"parity: sampled max row-wise relative error {parity_sampled:.3e} >= {PARITY_TOL}")
+
     eager_gbs = step_bytes / (ms_step * 1e-3) / 1e9
     head_ms = graph["ms_per_step"] if graph else ms_step
     gbs = step_bytes / (head_ms * 1e-3) / 1e9
@@ -549,6 +589,10 @@ def main():
                "sample": f"{layers} of {nl} layers x 7 projections, all {T} tokens "
                          f"({done_bytes / 1e9:.2f} GB algorithmic, {spent:.1f} s)",
                "parity_max_rowwise_rel_err": float(f"{worst:.3e}")}
+        parity["whole_layers"] = layers
+        parity["whole_layer_max_rowwise_rel_err"] = float(f"{worst:.3e}")
+        if worst >= PARITY_TOL:
+            fail(f"parity: whole-layer max row-wise relative error {worst:.3e} >= {PARITY_TOL}")
         # the small workloads on all threads and on one (best of 3; configs 2
         # and 3 on one thread: a single run), over the same algorithmic bytes
         per_cfg = {}
@@ -818,6 +862,7 @@ def main():
             "gbs": round(float(np.sum(call_bytes) / (mean_call_ms.sum() * 1e-3) / 1e9), 1)},
             "split_matches_apply": bool(split_same)}),
         "cpu_baseline": cpu,
+        "parity": parity,
         "prefill": prefill,
         "configs": configs,
         "shared_activation": shared,

@@ -12,11 +12,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-# LORA_LIB_PATH selects another build of the library (tuning experiments)
-LIB_PATH = os.environ.get("LORA_LIB_PATH", os.path.join(HERE, "liblora.so"))
+LIB_PATH = os.path.join(HERE, "liblora.so")
 SOURCES = [os.path.join(CSRC, "lora_kernels.hip"), os.path.join(CSRC, "lora_abi.cpp"),
            os.path.join(CSRC, "lora_pool.cpp")]
-ARCH = os.environ.get("LORA_OFFLOAD_ARCH", "gfx950")
+ARCH = "gfx950"
 
 
 def torch_lib_dir() -> str:

@@ -166,8 +166,12 @@ KProj make_kproj(const lora_proj_t& p, float* v, int nv, int dtype) {
   return k;
 }
 
-void fill_common(KArgs& K, const lora_segments_t* s, const lora_pool_t* pool, int64_t v_stride) {
+// T: the call's token count (lora_apply: the segments must have been built
+// for exactly T tokens), or -1 for the split entry points (any built T up to
+// the buffer's capacity).
+void fill_common(KArgs& K, const lora_segments_t* s, const lora_pool_t* pool, int64_t v_stride, int32_t T) {
   const PlanPtrs pp = plan_ptrs(s);
+  const PlanLayout L = plan_layout(s->T, s->num_adapters);
   K.perm = s->perm;
   K.seg_desc = reinterpret_cast<const int4*>(pp.seg_desc);
   K.shr_item_m = pp.shr_m;
@@ -179,7 +183,13 @@ void fill_common(KArgs& K, const lora_segments_t* s, const lora_pool_t* pool, in
   K.v_stride = v_stride;
   K.num_pages = pool->num_pages;
   K.pw_log2 = log2_exact(pool->page_width);
-  K.T = s->T;
+  K.T = T >= 0 ? T : s->T;
+  K.t_exact = T >= 0;
+  K.s_cap = (int32_t)L.s_cap;
+  K.cap_sm = (int32_t)L.cap_shrink_mfma;
+  K.cap_sv = (int32_t)L.cap_shrink_valu;
+  K.cap_em = (int32_t)L.cap_expand_mfma;
+  K.cap_ev = (int32_t)L.cap_expand_valu;
 }
 
 // Projections of one launch that read the same activations (q/k/v, gate/up
@@ -302,9 +312,9 @@ lora_status_t lora_build_segments(const int32_t* ids, int32_t T, const lora_adap
   if (T > segs->T || adapters->num_adapters > segs->num_adapters) return LORA_ERR_WORKSPACE;
   if (!ws) return LORA_ERR_INVALID_ARG;
   if (ws_bytes < hist_bytes(T, adapters->num_adapters)) return LORA_ERR_WORKSPACE;
-  lora_segments_t s = *segs;
-  s.T = T;
-  return build_into(ids, T, adapters, &s, static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream));
+  // the plan keeps the layout of the buffer's capacity (segs->T,
+  // segs->num_adapters) whatever T is; the built T is recorded in counts[]
+  return build_into(ids, T, adapters, segs, static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream));
 }
 
 // Shared body of lora_shrink / lora_expand: groups of up to kProjsPerLaunch
@@ -325,7 +335,7 @@ static lora_status_t run_split(const lora_proj_t* projs, int32_t n_projs, const 
   for (int base = 0; base < n_projs; base += kProjsPerLaunch) {
     KArgs K;
     memset(&K, 0, sizeof K);
-    fill_common(K, segs, pool, v_stride);
+    fill_common(K, segs, pool, v_stride, -1);
     K.np = std::min(kProjsPerLaunch, n_projs - base);
     for (int i = 0; i < K.np; ++i) {
       const lora_proj_t& p = projs[base + i];
@@ -361,7 +371,7 @@ lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_
   if (lora_status_t st = check_pool(pool)) return st;
   if (segs) {
     if (lora_status_t st = check_segs(segs)) return st;
-    if (segs->T != T || adapters->num_adapters > segs->num_adapters) return LORA_ERR_INVALID_ARG;
+    if (T > segs->T || adapters->num_adapters > segs->num_adapters) return LORA_ERR_INVALID_ARG;
   }
   int32_t max_d_in = 0;
   for (int i = 0; i < n_projs; ++i) {
@@ -395,7 +405,7 @@ lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_
   for (int base = 0; base < n_projs; base += kProjsPerLaunch) {
     KArgs K;
     memset(&K, 0, sizeof K);
-    fill_common(K, S, pool, v_stride);
+    fill_common(K, S, pool, v_stride, T);
     K.np = std::min(kProjsPerLaunch, n_projs - base);
     for (int i = 0; i < K.np; ++i) {
       float* v = reinterpret_cast<float*>(vbase + (size_t)i * vpp);

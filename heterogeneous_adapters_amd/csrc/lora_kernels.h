@@ -39,7 +39,11 @@ struct KArgs {
   int64_t v_stride;
   int32_t num_pages;
   int32_t pw_log2;
-  int32_t T;
+  int32_t T;        // tokens of the call (t_exact) or the segment buffer's token capacity
+  int32_t t_exact;  // the segments must have been built for exactly T tokens (else for at most T)
+  // capacities of the segment buffer's plan (segments, items per table);
+  // counts beyond them mean the buffer was not built as laid out
+  int32_t s_cap, cap_sm, cap_sv, cap_em, cap_ev;
   int32_t np;
   int32_t xshare;  // every projection of the launch reads the same X (same pointer, ldx, d_in)
 };

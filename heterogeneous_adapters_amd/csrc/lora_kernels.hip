@@ -317,6 +317,33 @@ __device__ __forceinline__ const KArgs& kernel_args() {
 __device__ const KArgs& kernel_args();
 #endif
 
+// The segment buffer's counters, read (scalar loads) before any plan entry.
+// A buffer that was never built (check word), built for another token count
+// than the call's, or whose totals exceed the capacity the plan was laid out
+// for, is not walked: the launch computes nothing and raises
+// LORA_FLAG_SEGMENTS, so such a buffer never leads to an access outside it.
+struct PlanCounts {
+  int S, T, t_valid, shr_m, shr_v, exp_m, exp_v;
+  bool ok;
+};
+__device__ __forceinline__ PlanCounts read_counts(const KArgs& K) {
+  PlanCounts c;
+  c.S = cld(K.counts + kCountS);
+  c.T = cld(K.counts + kCountT);
+  c.t_valid = cld(K.counts + kCountTValid);
+  c.shr_m = cld(K.counts + kCountShrinkMfma);
+  c.shr_v = cld(K.counts + kCountShrinkValu);
+  c.exp_m = cld(K.counts + kCountExpandMfma);
+  c.exp_v = cld(K.counts + kCountExpandValu);
+  const int chk = cld(K.counts + kCountCheck);
+  c.ok = chk == segments_check_word(c.T) && c.T >= 0 && (K.t_exact ? c.T == K.T : c.T <= K.T) &&
+         c.S >= 0 && c.S <= min(c.T, K.s_cap) && c.t_valid >= 0 && c.t_valid <= c.T && c.shr_m >= 0 &&
+         c.shr_m <= K.cap_sm && c.shr_v >= 0 && c.shr_v <= K.cap_sv && c.exp_m >= 0 && c.exp_m <= K.cap_em &&
+         c.exp_v >= 0 && c.exp_v <= K.cap_ev;
+  if (!c.ok && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&K.counts[kCountFlags], LORA_FLAG_SEGMENTS);
+  return c;
+}
+
 // ================================================================ shrink
 // MBGMV item (one wave): (segment, rank group g, <= 2 tokens, 512-column
 // slice q).  Each lane streams one 16-byte vector (8 bf16 / 4 fp32 columns)
@@ -572,9 +599,9 @@ constexpr int kShrinkMfmaRounds = 3;
 template <class E, bool WIDE>
 __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArgs) {
   const KArgs& K = kernel_args();
-  const int S = cld(K.counts + kCountS);
-  if (S <= 0) return;
-  const int Um = cld(K.counts + kCountShrinkMfma), Uv = cld(K.counts + kCountShrinkValu);
+  const PlanCounts pc = read_counts(K);
+  if (!pc.ok || pc.S <= 0) return;
+  const int Um = pc.shr_m, Uv = pc.shr_v;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   // MBGMM items first, then MBGMV items; each path walks its own item list,
   // so the two register footprints never share a loop body.  The wave's
@@ -1339,12 +1366,13 @@ __device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int 
 // Rows of tokens without an adapter: Y = Y_base (only when Y is not Y_base),
 // kCopyTokens rows x one column block per item.
 template <class E>
-__device__ __forceinline__ void expand_copy(const KArgs& K, const KProj& P, int jb, int chunk, int t_valid, int lane) {
+__device__ __forceinline__ void expand_copy(const KArgs& K, const KProj& P, int jb, int chunk, int t_valid, int nT,
+                                            int lane) {
   typedef typename E::T T;
   constexpr int CPL = 4 / (int)sizeof(T);
   constexpr int SUBW = 64 * CPL;
   const int t_beg = t_valid + chunk * kCopyTokens;
-  const int t_end = min(K.T, t_beg + kCopyTokens);
+  const int t_end = min(nT, t_beg + kCopyTokens);
   const T* Yb = reinterpret_cast<const T*>(P.Yb);
   T* Y = reinterpret_cast<T*>(P.Y);
   for (int i = t_beg; i < t_end; ++i) {
@@ -1366,11 +1394,12 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
   // per-wave rows (MBGMV staging, MBGMM output tiles) and the block's staged
   // v tile of an MBGMM item
   __shared__ __attribute__((aligned(16))) float vs_all[kWaves + 1][kExpandRowFloats];
-  const int S = cld(K.counts + kCountS);
-  const int t_valid = cld(K.counts + kCountTValid);
-  const int Um = S > 0 ? cld(K.counts + kCountExpandMfma) : 0;
-  const int Uv = S > 0 ? cld(K.counts + kCountExpandValu) : 0;
-  const int ncopy = ceil_div_i(K.T - t_valid, kCopyTokens);
+  const PlanCounts pc = read_counts(K);
+  if (!pc.ok) return;
+  const int t_valid = pc.t_valid;
+  const int Um = pc.S > 0 ? pc.exp_m : 0;
+  const int Uv = pc.S > 0 ? pc.exp_v : 0;
+  const int ncopy = ceil_div_i(pc.T - t_valid, kCopyTokens);
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   float* vs = vs_all[wave];
   // MBGMM items first (whole-block items), then MBGMV items and the copies of
@@ -1425,7 +1454,7 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
     const bool more = ni < it.end;
     ValuItem nxt;
     if (cur.copy) {
-      expand_copy<E>(K, K.p[cur.p], cur.jb, cur.local, t_valid, lane);
+      expand_copy<E>(K, K.p[cur.p], cur.jb, cur.local, t_valid, pc.T, lane);
       if (more) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy);
     } else {
       expand_valu_body<E, WIDE>(K, K.p[cur.p], cur, vs, lane, [&]() {
@@ -1614,6 +1643,8 @@ __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N,
     out.counts[kCountExpandMfma] = carry[5];
     out.counts[kCountExpandValu] = carry[6];
     for (int i = kCountFlags; i < kNumCounts; ++i) out.counts[i] = 0;
+    out.counts[kCountT] = T;
+    out.counts[kCountCheck] = segments_check_word(T);
   }
 }
 

@@ -44,10 +44,7 @@ constexpr int kMfmaExpandTokens = 16;     // tokens per MBGMM expand item (one t
 constexpr int kMfmaShrinkTokensShort = 32, kMfmaShrinkTokensLong = 64, kMfmaLongSegment = 512;
 constexpr int kProjsPerLaunch = 16;       // projection descriptors per launch
 constexpr int kSegChunk = 1024;           // tokens per segment-builder block
-#ifndef LORA_MFMA_MIN_TOKENS
-#define LORA_MFMA_MIN_TOKENS 16
-#endif
-constexpr int kMfmaMinTokens = LORA_MFMA_MIN_TOKENS;  // segment length that switches to MFMA
+constexpr int kMfmaMinTokens = 16;       // segment length that switches to MFMA (one full tile)
 
 // Output columns of an MBGMV expand column block: 4 sub-blocks of 64 lanes x
 // (2 bf16 | 1 fp32) columns, i.e. 64 bytes of B per lane, sub-block and rank
@@ -84,7 +81,12 @@ LORA_HD inline int expand_items_mfma(int n) { return is_mfma_segment(n) ? ceil_d
 constexpr int kCountS = 0, kCountInvalid = 1, kCountTValid = 2, kCountVTotal = 3;
 constexpr int kCountShrinkMfma = 4, kCountShrinkValu = 5, kCountExpandMfma = 6, kCountExpandValu = 7;
 constexpr int kCountFlags = 8;
+// the token count the segments were built for, and a check word derived
+// from it: a compute kernel that finds the pair inconsistent (a buffer never
+// built, or garbage) or built for another batch size computes nothing
+constexpr int kCountT = 9, kCountCheck = 10;
 constexpr int kNumCounts = 16;
+LORA_HD inline int segments_check_word(int T) { return (int)(0x4C6F5261u ^ (unsigned)T); }
 
 // The internal plan area: per-segment descriptors (2 x int4: {adapter,
 // rank, first token, tokens}, {v offset, first shrink item, first expand
@@ -96,21 +98,28 @@ constexpr int kNumCounts = 16;
 constexpr int kValuItemInts = 8;
 struct PlanLayout {
   long long seg_desc, shrink_mfma, shrink_valu, expand_mfma, expand_valu, total;
+  // capacities: segments, and items of each table
+  long long s_cap, cap_shrink_mfma, cap_shrink_valu, cap_expand_mfma, cap_expand_valu;
 };
 LORA_HD inline long long align64(long long x) { return (x + 63) / 64 * 64; }
 LORA_HD inline PlanLayout plan_layout(int T, int N) {
   const long long t = T > 0 ? T : 0;
   const long long smax = (T < N ? t : (N > 0 ? N : 0));
   PlanLayout L;
-  L.seg_desc = 0;
-  L.shrink_mfma = align64(8 * (smax > 0 ? smax : 1));
+  L.s_cap = smax;
   // MBGMM shrink items <= 8*(T/16 + S) <= 9T; MBGMV <= 8*(T/2 + S) <= 12T
-  L.shrink_valu = L.shrink_mfma + align64(9 * t + 1);
-  L.expand_mfma = L.shrink_valu + align64(kValuItemInts * (12 * t + 1));
+  L.cap_shrink_mfma = 9 * t + 1;
+  L.cap_shrink_valu = 12 * t + 1;
   // MBGMM expand items <= T/16 + S <= 2T; MBGMV <= 4*(T/K + S) <= (4/K + 4)T
   // for chunks of K = kValuExpandTokens tokens
-  L.expand_valu = L.expand_mfma + align64(2 * t + 1);
-  L.total = L.expand_valu + align64(kValuItemInts * ((4 / kValuExpandTokens + 4) * t + 1));
+  L.cap_expand_mfma = 2 * t + 1;
+  L.cap_expand_valu = (4 / kValuExpandTokens + 4) * t + 1;
+  L.seg_desc = 0;
+  L.shrink_mfma = align64(8 * (smax > 0 ? smax : 1));
+  L.shrink_valu = L.shrink_mfma + align64(L.cap_shrink_mfma);
+  L.expand_mfma = L.shrink_valu + align64(kValuItemInts * L.cap_shrink_valu);
+  L.expand_valu = L.expand_mfma + align64(L.cap_expand_mfma);
+  L.total = L.expand_valu + align64(kValuItemInts * L.cap_expand_valu);
   return L;
 }
 

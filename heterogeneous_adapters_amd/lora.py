@@ -23,7 +23,8 @@ LORA_MAX_ADAPTERS = 1 << 20
 LORA_MAX_TOKENS = (1 << 24) - 1
 LORA_MAX_LAUNCH_ITEMS = 1 << 30
 LORA_KSLICE = 512
-COUNT_S, COUNT_INVALID, COUNT_T_VALID, COUNT_V_TOTAL, COUNT_FLAGS = 0, 1, 2, 3, 8
+COUNT_S, COUNT_INVALID, COUNT_T_VALID, COUNT_V_TOTAL, COUNT_FLAGS, COUNT_T = 0, 1, 2, 3, 8, 9
+FLAG_PAGE_RANGE, FLAG_SEGMENTS = 1, 2
 N_COUNTS = 16
 
 _vp = ctypes.c_void_p

@@ -23,37 +23,33 @@ import torch
 from . import lora
 
 
-class ManagedPool:
-    """Device pool of ``capacity`` pages caching the adapters of a host tier.
+class PoolState:
+    """Host side of a managed pool: which adapters are resident (the native
+    cache), the host copy of every projection's page tables, the adapters a
+    batch in flight pins, and whether the next upload must wait for the work
+    already enqueued on the compute stream.
 
-    indptrs: per projection, (a_indptr, b_indptr) int32 arrays over the N
-    adapters (slot counts per adapter, fixed by rank and shape).
-    host_tier: pinned CPU tensor (total pages, 16*page_width) holding every
-    adapter's image; adapter a's image is rows offsets[a]:offsets[a+1].
-    """
+    That wait is needed whenever pages that enqueued work may still read have
+    become free since the last wait: an eviction, or the release of the
+    adapters a failed batch had admitted (their pages may be an evicted
+    adapter's).  The flag is sticky until an upload waits, so a batch that
+    reuses such pages without evicting anything itself still orders its
+    uploads after that work."""
 
-    def __init__(self, indptrs: Sequence[tuple], host_tier: torch.Tensor, page_width: int, capacity: int,
-                 device="cuda"):
+    def __init__(self, indptrs: Sequence[tuple], capacity: int):
         self.indptrs = [(np.asarray(a, np.int64), np.asarray(b, np.int64)) for a, b in indptrs]
         N = len(self.indptrs[0][0]) - 1
         counts = np.zeros(N, np.int64)
         for a_ip, b_ip in self.indptrs:
             counts += np.diff(a_ip) + np.diff(b_ip)
         self.offsets = np.concatenate([[0], np.cumsum(counts)])
-        if host_tier.dim() != 2 or host_tier.shape[0] != self.offsets[-1] or host_tier.device.type != "cpu":
-            raise ValueError("host tier must hold every adapter's pages on the host")
-        self.N, self.host_tier, self.page_width = N, host_tier, page_width
-        self.base = torch.empty((capacity, host_tier.shape[1]), dtype=host_tier.dtype, device=device)
-        self.pool = lora.Pool(self.base, page_width)
+        self.N = N
         self.cache = lora.PageCache(capacity)
         # page tables; slots of non-resident adapters hold page 0 (never read)
         self.host_pages = [(np.zeros(a[-1], np.int32), np.zeros(b[-1], np.int32)) for a, b in self.indptrs]
-        i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(device)
-        self.tables = [(i32(a_ip), i32(a_pg), i32(b_ip), i32(b_pg))
-                       for (a_ip, b_ip), (a_pg, b_pg) in zip(self.indptrs, self.host_pages)]
-        self.upload_stream = torch.cuda.Stream(device=device)
-        self.pinned = set()  # adapters pinned by ensure() and not yet unpinned
-        self.hits = self.misses = self.evictions = self.pages_uploaded = 0
+        self.pinned = set()  # adapters pinned by admit() and not yet unpinned
+        self.fence_pending = False  # freed pages may still be read by enqueued work
+        self.hits = self.misses = self.evictions = 0
 
     def n_pages(self, a: int) -> int:
         return int(self.offsets[a + 1] - self.offsets[a])
@@ -66,21 +62,23 @@ class ManagedPool:
             b_pg[b_ip[a]:b_ip[a + 1]] = pages[k + na:k + na + nb]
             k += na + nb
 
-    def ensure(self, adapters: Iterable[int], compute_stream: Optional[torch.cuda.Stream] = None) -> List[int]:
-        """Make ``adapters`` resident and pinned, upload the misses, rewrite the
-        page tables, and make ``compute_stream`` (default: current) wait for
-        the uploads.  Returns the adapters that missed.  If a miss evicted an
-        adapter, the uploads first wait for the work already on
-        ``compute_stream`` (it may still read the evicted pages)."""
-        compute_stream = compute_stream or torch.cuda.current_stream()
+    def admit(self, adapters: Iterable[int]):
+        """Make ``adapters`` resident and pinned and rewrite the host tables.
+        Returns (missed adapters, [(adapter, pages)] to upload, whether those
+        uploads must first wait for the enqueued compute work).  A batch that
+        does not fit raises lora.LoraError and leaves nothing of it pinned or
+        admitted."""
         want = [int(a) for a in dict.fromkeys(int(x) for x in adapters)]
         for a in want:
             if not 0 <= a < self.N:
                 raise ValueError(f"adapter {a} outside 0..{self.N - 1}")
-        missed, plan, evicted_any, newly_pinned = [], [], False, []
+        missed, plan, newly_pinned = [], [], []
         try:
             for a in want:
                 hit, pages, ev = self.cache.admit(a, self.n_pages(a))
+                if len(ev):
+                    self.fence_pending = True
+                    self.evictions += len(ev)
                 if not hit:
                     plan.append((a, pages))
                 # pin at once so that a later admission of this batch cannot evict it
@@ -88,8 +86,6 @@ class ManagedPool:
                 if a not in self.pinned:
                     self.pinned.add(a)
                     newly_pinned.append(a)
-                evicted_any |= len(ev) > 0
-                self.evictions += len(ev)
                 if hit:
                     self.hits += 1
                 else:
@@ -98,15 +94,79 @@ class ManagedPool:
                 self._write_tables(a, pages)
         except lora.LoraError:
             # the batch does not fit: nothing of it stays pinned, and adapters
-            # admitted by this call (pages assigned, nothing uploaded) leave
+            # admitted by this call (pages assigned, nothing uploaded) leave;
+            # their pages may have been an evicted adapter's
             for a in newly_pinned:
                 self.pinned.discard(a)
                 self.cache.set_pinned(a, False)
             for a, _ in plan:
                 self.cache.release(a)
             raise
+        fence = bool(plan) and self.fence_pending
+        if fence:
+            self.fence_pending = False
+        return missed, plan, fence
+
+    def unpin(self, adapters: Iterable[int]) -> None:
+        for a in dict.fromkeys(int(x) for x in adapters):
+            self.cache.set_pinned(a, False)
+            self.pinned.discard(a)
+
+
+class ManagedPool:
+    """Device pool of ``capacity`` pages caching the adapters of a host tier.
+
+    indptrs: per projection, (a_indptr, b_indptr) int32 arrays over the N
+    adapters (slot counts per adapter, fixed by rank and shape).
+    host_tier: pinned CPU tensor (total pages, 16*page_width) holding every
+    adapter's image; adapter a's image is rows offsets[a]:offsets[a+1].
+    """
+
+    def __init__(self, indptrs: Sequence[tuple], host_tier: torch.Tensor, page_width: int, capacity: int,
+                 device="cuda"):
+        self.state = PoolState(indptrs, capacity)
+        st = self.state
+        self.indptrs, self.offsets, self.N, self.cache = st.indptrs, st.offsets, st.N, st.cache
+        if host_tier.dim() != 2 or host_tier.shape[0] != self.offsets[-1] or host_tier.device.type != "cpu":
+            raise ValueError("host tier must hold every adapter's pages on the host")
+        self.host_tier, self.page_width = host_tier, page_width
+        self.base = torch.empty((capacity, host_tier.shape[1]), dtype=host_tier.dtype, device=device)
+        self.pool = lora.Pool(self.base, page_width)
+        i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(device)
+        self.tables = [(i32(a_ip), i32(a_pg), i32(b_ip), i32(b_pg))
+                       for (a_ip, b_ip), (a_pg, b_pg) in zip(self.indptrs, st.host_pages)]
+        self.upload_stream = torch.cuda.Stream(device=device)
+        self.pages_uploaded = 0
+
+    @property
+    def pinned(self):
+        return self.state.pinned
+
+    @property
+    def hits(self):
+        return self.state.hits
+
+    @property
+    def misses(self):
+        return self.state.misses
+
+    @property
+    def evictions(self):
+        return self.state.evictions
+
+    def n_pages(self, a: int) -> int:
+        return self.state.n_pages(a)
+
+    def ensure(self, adapters: Iterable[int], compute_stream: Optional[torch.cuda.Stream] = None) -> List[int]:
+        """Make ``adapters`` resident and pinned, upload the misses, rewrite the
+        page tables, and make ``compute_stream`` (default: current) wait for
+        the uploads.  Returns the adapters that missed.  When pages freed since
+        the last such wait are reused (PoolState), the uploads first wait for
+        the work already on ``compute_stream``: it may still read them."""
+        compute_stream = compute_stream or torch.cuda.current_stream()
+        missed, plan, fence = self.state.admit(adapters)
         if plan:
-            if evicted_any:
+            if fence:
                 self.upload_stream.wait_stream(compute_stream)
             for a, pages in plan:
                 lora.lora_upload_pages(self.pool, self.host_tier[self.offsets[a]:self.offsets[a + 1]], pages,
@@ -116,7 +176,7 @@ class ManagedPool:
         # tables: small, copied on the compute stream after it has passed the
         # work that read the old ones
         with torch.cuda.stream(compute_stream):
-            for (_, a_pg_d, _, b_pg_d), (a_pg, b_pg) in zip(self.tables, self.host_pages):
+            for (_, a_pg_d, _, b_pg_d), (a_pg, b_pg) in zip(self.tables, self.state.host_pages):
                 a_pg_d.copy_(torch.from_numpy(a_pg))
                 b_pg_d.copy_(torch.from_numpy(b_pg))
         return missed
@@ -124,9 +184,7 @@ class ManagedPool:
     def unpin(self, adapters: Iterable[int]) -> None:
         """The batch that used ``adapters`` has been enqueued; they may be
         evicted by later admissions (which then order their uploads after it)."""
-        for a in dict.fromkeys(int(x) for x in adapters):
-            self.cache.set_pinned(a, False)
-            self.pinned.discard(a)
+        self.state.unpin(adapters)
 
     def proj(self, p: int, X: torch.Tensor, Y_base: torch.Tensor, Y: torch.Tensor) -> lora.Proj:
         a_ip, a_pg, b_ip, b_pg = self.tables[p]

@@ -148,9 +148,11 @@ typedef struct {
  *   seg_adapter[S_max]    adapter of segment s
  *   v_indptr[S_max+1]     offset of segment s in the ragged rank-r
  *                         intermediate v: v[v_indptr[s] + i*r + k]
- *   plan                  the work plan the kernels walk (internal layout)
- *   counts[16]            {S, n_invalid, T_valid, V_total, then internal
- *                         work-plan totals and device error flags}
+ *   plan                  the work plan the kernels walk (internal layout,
+ *                         sized for the capacity (T, num_adapters))
+ *   counts[16]            {S, n_invalid, T_valid, V_total, internal
+ *                         work-plan totals, device error flags (index 8),
+ *                         the built token count (9), a check word (10)}
  * A token is valid when 0 <= ids[t] < num_adapters and its adapter's rank is
  * in [1, 128].  ids[t] == -1 marks a base-model token ([MLSA] "What vLLM
  * actually gives you": base-model requests share the server); other invalid
@@ -171,7 +173,13 @@ typedef struct {
 #define LORA_COUNT_T_VALID 2
 #define LORA_COUNT_V_TOTAL 3
 #define LORA_COUNT_FLAGS 8
+#define LORA_COUNT_T 9       /* the token count the segments were built for */
 #define LORA_FLAG_PAGE_RANGE 1 /* a page id outside the pool was skipped (read as 0) */
+/* The segment buffer was not walked: never built, built for another token
+ * count than the call's T (lora_apply) or for more than its capacity, or its
+ * counters exceed the capacity it was laid out for.  The launch wrote
+ * nothing. */
+#define LORA_FLAG_SEGMENTS 2
 
 /* Bytes of the device buffer that holds segments for T tokens and
  * num_adapters adapters. */
@@ -191,11 +199,15 @@ size_t lora_workspace_size(int32_t T, int32_t num_adapters, int32_t n_projs, int
 int32_t lora_v_slices(int32_t d_in);
 
 /* Group the batch's tokens by adapter and build the work plan (a
- * deterministic stable counting sort; [MLSP] SGMV grouping).  ids: device
- * [T].  segs: laid out by lora_segments_init with capacity >= (T, N).  The
+ * deterministic stable counting sort; [MLSP] "Segmented Gather Matrix-Vector
+ * Multiplication (SGMV)": requests grouped by their adapter).  ids: device
+ * [T].  segs: laid out by lora_segments_init with a capacity of at least
+ * (T, adapters->num_adapters); a buffer laid out for a larger batch serves
+ * any smaller one (the built T is recorded in counts[LORA_COUNT_T]).  The
  * result depends only on ids and ranks; build once per batch and reuse for
- * every layer and projection.  Errors: INVALID_ARG, WORKSPACE, UNSUPPORTED,
- * HIP. */
+ * every layer and projection.  ws: device, >= lora_workspace_size(T, N, 0, 0)
+ * bytes.  Errors: INVALID_ARG, WORKSPACE (capacity or workspace too small),
+ * UNSUPPORTED, HIP. */
 lora_status_t lora_build_segments(const int32_t* ids, int32_t T, const lora_adapters_t* adapters,
                                   const lora_segments_t* segs, void* ws, size_t ws_bytes,
                                   void* stream);
@@ -222,8 +234,14 @@ lora_status_t lora_expand(const lora_proj_t* projs, int32_t n_projs, const lora_
                           const lora_segments_t* segs, const lora_pool_t* pool, const float* const* v,
                           int32_t v_slices, int64_t v_stride, void* stream);
 
-/* The fused adapter branch for n_projs projections of one batch: shrink then
- * expand, two kernel launches per group of up to 16 projections.
+/* The whole adapter branch for n_projs projections of one batch: for every
+ * token, Y = Y_base + (alpha/r) (X A) B, the adapted-layer equation of
+ * [MLSP] "The Mathematical Anatomy of Heterogeneous Batches", computed as
+ * the gather / shrink / expand sequence of [MLSP] "Segmented Gather
+ * Matrix-Vector Multiplication (SGMV)" over segments of tokens that share an
+ * adapter, with weights read through the page tables ([MLSP] "Unified Paging
+ * Architecture").  Two kernel launches (shrink, expand) per group of up to
+ * 16 projections.
  *   ids != NULL, segs != NULL : build segments into *segs, then apply
  *   ids != NULL, segs == NULL : build segments inside the workspace
  *   ids == NULL, segs != NULL : reuse prebuilt segments (built by
@@ -232,7 +250,10 @@ lora_status_t lora_expand(const lora_proj_t* projs, int32_t n_projs, const lora_
  * always built (into the workspace when segs is NULL), all counts zero, and
  * nothing else is written.  Descriptor pointers must still
  * be valid (non-null, aligned).
- * projs: host array of n_projs descriptors.  T must equal the segments' T.
+ * projs: host array of n_projs descriptors.  T: the batch's tokens, at most
+ * the capacity segs->T.  Prebuilt segments must have been built for exactly
+ * T tokens; if they were not (or were never built) the kernels compute
+ * nothing and set LORA_FLAG_SEGMENTS in segs->counts[LORA_COUNT_FLAGS].
  * ws: device workspace of lora_workspace_size(T, N, n_projs, max d_in) bytes.
  * Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED, WORKSPACE, HIP. */
 lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_t T,

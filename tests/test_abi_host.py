@@ -132,9 +132,12 @@ def test_other_rejections():
     assert L.lora_shrink(r(proj), 1, r(ad), r(seg), r(pool), (ctypes.c_void_p * 1)(None), 8 * 128, None) == -1
     assert L.lora_shrink(r(proj), -1, r(ad), r(seg), r(pool), vs, 8 * 128, None) == -1
     arr = (lora.lora_proj_t * 1)(proj)
-    # neither ids nor segments; T mismatch; workspace too small
+    # neither ids nor segments; T above the segment buffer's capacity;
+    # workspace too small (T below the capacity is a valid call: a buffer laid
+    # out for a larger batch serves a smaller one)
     assert L.lora_apply(None, None, 8, arr, 1, r(ad), r(pool), v, 1 << 30, None) == -1
-    assert L.lora_apply(None, r(seg), 7, arr, 1, r(ad), r(pool), v, 1 << 30, None) == -1
+    assert L.lora_apply(None, r(seg), 9, arr, 1, r(ad), r(pool), v, 1 << 30, None) == -1
+    assert L.lora_apply(v, r(seg), 9, arr, 1, r(ad), r(pool), v, 1 << 30, None) == -1
     assert L.lora_apply(None, r(seg), 8, arr, 1, r(ad), r(pool), v, 64, None) == -4
     # adapters without rank array; too many adapters for the segment buffer
     bad = lora.lora_adapters_t(None, b.p(), 4)
@@ -227,3 +230,81 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(lora, "_lib", None)
     with pytest.raises(ImportError):
         lora.lib()
+
+
+PLAN_CHECK = r"""
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+#include <algorithm>
+#include "lora_plan.h"
+using namespace lora;
+// Item totals of the tables for one batch, from the same per-segment item
+// functions the segment builder uses.
+static int check(int T, int N, const std::vector<int>& ids, const std::vector<int>& rank) {
+  std::vector<int> cnt(N, 0);
+  for (int t = 0; t < T; ++t) if (ids[t] >= 0 && ids[t] < N && rank[ids[t]] >= 1 && rank[ids[t]] <= 128) cnt[ids[t]]++;
+  long long S = 0, sm = 0, sv = 0, em = 0, ev = 0;
+  for (int a = 0; a < N; ++a) {
+    if (!cnt[a]) continue;
+    const int n = cnt[a], r = rank[a];
+    ++S; sm += shrink_items_mfma(n, r); sv += shrink_items_valu(n, r);
+    em += expand_items_mfma(n); ev += expand_items_valu(n, r);
+  }
+  const PlanLayout L = plan_layout(T, N);
+  if (S > L.s_cap || sm > L.cap_shrink_mfma || sv > L.cap_shrink_valu || em > L.cap_expand_mfma ||
+      ev > L.cap_expand_valu) {
+    printf("FAIL T=%d N=%d S=%lld sm=%lld sv=%lld em=%lld ev=%lld\n", T, N, S, sm, sv, em, ev);
+    return 1;
+  }
+  // the tables fit their regions, in order, inside the plan
+  if (!(L.shrink_mfma >= 8 * L.s_cap && L.shrink_valu - L.shrink_mfma >= L.cap_shrink_mfma &&
+        L.expand_mfma - L.shrink_valu >= kValuItemInts * L.cap_shrink_valu &&
+        L.expand_valu - L.expand_mfma >= L.cap_expand_mfma &&
+        L.total - L.expand_valu >= kValuItemInts * L.cap_expand_valu)) {
+    printf("FAIL layout T=%d N=%d\n", T, N);
+    return 1;
+  }
+  return 0;
+}
+int main() {
+  srand(12345);
+  int bad = 0;
+  const int rk[] = {1, 8, 15, 16, 17, 31, 32, 33, 64, 100, 127, 128};
+  for (int T : {1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1000, 1024, 4099}) {
+    for (int N : {1, 2, 7, 64, 1000, 5000}) {
+      for (int mode = 0; mode < 6; ++mode) {
+        std::vector<int> rank(N), ids(T);
+        for (int a = 0; a < N; ++a) rank[a] = mode == 0 ? 128 : mode == 1 ? 1 : rk[rand() % 12];
+        for (int t = 0; t < T; ++t) {
+          if (mode == 0 || mode == 1) ids[t] = t % N;           // as many segments as possible
+          else if (mode == 2) ids[t] = 0;                        // one segment
+          else if (mode == 3) ids[t] = (t / 16) % N;             // segments of 16 (MBGMM)
+          else if (mode == 4) ids[t] = (t / 15) % N;             // segments of 15 (MBGMV)
+          else ids[t] = rand() % (N + 2) - 1;                    // random, with base-only tokens
+        }
+        bad += check(T, N, ids, rank);
+      }
+    }
+  }
+  printf(bad ? "FAILED\n" : "OK\n");
+  return bad != 0;
+}
+"""
+
+
+def test_plan_capacities_bound_every_item_table(tmp_path):
+    """The capacities the compute kernels check the segment buffer's counters
+    against (plan_layout) bound the item totals of every batch the builder can
+    produce, and the tables they size fit their regions of the plan.  Checked
+    by compiling the plan header with the host compiler and counting items with
+    the same per-segment functions the builder uses."""
+    import subprocess
+    src = tmp_path / "plan_check.cpp"
+    src.write_text(PLAN_CHECK)
+    exe = tmp_path / "plan_check"
+    inc = os.path.join(ROOT, "heterogeneous_adapters_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O1", f"-I{inc}", str(src), "-o", str(exe)], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert res.returncode == 0 and res.stdout.strip().endswith("OK"), res.stdout
+

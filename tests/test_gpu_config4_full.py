@@ -2,8 +2,8 @@
 projections, 1024 tokens, 1000 adapters in a ~160 GiB paged pool), run in the
 launch configuration the benchmark times (segments built once, then q/k/v,
 o, gate/up and down per layer).  Segments are compared in full; Y on sampled
-tokens of sampled projections, each computed by the oracle token by token
-from the pages those tokens use."""
+tokens of all 224 projections, each computed by the oracle token by token
+from the pages those tokens use, and on every token of one whole layer."""
 import gc
 
 import numpy as np
@@ -48,20 +48,37 @@ def test_config4_full_size_sampled_parity():
     hot = np.nonzero(dw.ids == np.bincount(dw.ids).argmax())[0]
     counts = np.bincount(dw.ids, minlength=N)
     single = np.nonzero(counts[dw.ids] == 1)[0]
-    sample = np.unique(np.concatenate([rng.choice(T, 40, replace=False), hot[:24], single[:16]]))
+    sample = np.unique(np.concatenate([rng.choice(T, 24, replace=False), hot[:12], single[:12]]))
     sub_ids = dw.ids[sample]
-    for p in (0, 4, 6, 7 * 15 + 2, 7 * 31 + 5, 7 * 31 + 6):
-        print(f"config 4: projection {p} on {len(sample)} sampled tokens", flush=True)
-        hp, ht = host_subset(dw.pool, [dw.tables[p]], np.unique(sub_ids))
-        Xs = tensor_bits(dw.X[p])[sample]
-        Ybs = tensor_bits(dw.Y_base[p])[sample]
-        ref = W.as_f64(oracle.apply(Xs, Ybs, sub_ids, dw.ranks, dw.alpha, ht[0], hp, dw.page_width, "bf16"),
-                       "bf16")
-        got = W.as_f64(tensor_bits(Y[p])[sample], "bf16")
-        assert np.isfinite(got).all()
+    worst = 0.0
+    for l in range(32):
+        idx = list(range(7 * l, 7 * l + 7))
+        hp, ht = host_subset(dw.pool, [dw.tables[p] for p in idx], np.unique(sub_ids))
+        for j, p in enumerate(idx):
+            Xs = tensor_bits(dw.X[p])[sample]
+            Ybs = tensor_bits(dw.Y_base[p])[sample]
+            ref = W.as_f64(oracle.apply(Xs, Ybs, sub_ids, dw.ranks, dw.alpha, ht[j], hp, dw.page_width, "bf16"),
+                           "bf16")
+            got = W.as_f64(tensor_bits(Y[p])[sample], "bf16")
+            assert np.isfinite(got).all(), p
+            err = float((np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max())
+            worst = max(worst, err)
+            assert err < 1e-2, (p, err)
+        print(f"config 4: layer {l}: 7 projections on {len(sample)} sampled tokens, worst so far {worst:.3e}",
+              flush=True)
+    # every token of one whole layer (the oracle on all 1024 rows)
+    l = 17
+    idx = list(range(7 * l, 7 * l + 7))
+    valid = dw.ids[(dw.ids >= 0) & (dw.ids < N)]
+    hp, ht = host_subset(dw.pool, [dw.tables[p] for p in idx], np.unique(valid))
+    for j, p in enumerate(idx):
+        ref = W.as_f64(oracle.apply(tensor_bits(dw.X[p]), tensor_bits(dw.Y_base[p]), dw.ids, dw.ranks, dw.alpha,
+                                    ht[j], hp, dw.page_width, "bf16"), "bf16")
+        got = W.as_f64(tensor_bits(Y[p]), "bf16")
+        assert np.isfinite(got).all(), p
         err = float((np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max())
-        print(f"  rowwise rel err {err:.3e}", flush=True)
-        assert err < 1e-2
+        print(f"config 4: layer {l} projection {j}: all {T} tokens, rowwise rel err {err:.3e}", flush=True)
+        assert err < 1e-2, (p, err)
     del projs, Y, pool, dw, tabs
     gc.collect()
     torch.cuda.empty_cache()

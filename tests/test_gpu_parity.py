@@ -590,3 +590,75 @@ def test_shared_activation_group_matches_separate_inputs():
     for p in range(3):
         ref = oracle.apply(Xh, w.Y_base[p], w.ids, w.ranks, w.alpha, w.tables[p], w.pool, w.page_width, w.dtype)
         assert rowwise_rel(W.as_f64(ys["shared"][p], w.dtype), W.as_f64(ref, w.dtype)) < TOL["bf16"]
+
+
+def test_segment_buffer_larger_than_the_batch():
+    """A segment buffer laid out for a larger batch (capacity T + 37 tokens,
+    N + 5 adapters) serves the batch through every entry point, bit-identical
+    to a buffer of the batch's own size.  Prebuilt segments reused with
+    another token count, and a buffer that was never built, are not walked:
+    nothing is written and LORA_FLAG_SEGMENTS is raised."""
+    w = W.make_workload(2, dict(T=300, N=9, ranks_override=[8, 16, 64, 24, 1, 32, 128, 40, 8], page_width=512,
+                                projs=(("a", 1024, 1536), ("b", 1536, 1024))), keep_dense=False)
+    Yref, segref = gpu_apply(w)
+    b = batch.to_device(w)
+    projs = [b.proj(p) for p in range(w.n_projs)]
+    Tc, Nc = w.T + 37, w.N + 5
+    big = lora.Segments(Tc, Nc)
+    ws = lora.workspace(Tc, Nc, w.n_projs, 1536)
+
+    def fetch():
+        torch.cuda.synchronize()
+        return [batch.device_to_host(b.Y[p]) for p in range(w.n_projs)]
+
+    def check_big():
+        got = big.arrays()
+        assert got["flags"] == 0
+        assert np.array_equal(got["perm"][:w.T], segref["perm"])
+        for k in ("seg_indptr", "seg_adapter", "v_indptr", "S", "T_valid", "V_total", "n_invalid"):
+            assert np.array_equal(got[k], segref[k]), k
+        assert int(big.counts()[lora.COUNT_T]) == w.T
+
+    # prebuilt into the larger buffer, then applied
+    lora.lora_build_segments(b.ids, b.adapters, big, ws)
+    lora.lora_apply(None, big, w.T, projs, b.adapters, b.pool, ws)
+    Y = fetch()
+    check_big()
+    for p in range(w.n_projs):
+        assert np.array_equal(Y[p], Yref[p]), p
+    # built inside lora_apply into the larger buffer
+    for y in b.Y:
+        y.fill_(7.0)
+    lora.lora_apply(b.ids, big, w.T, projs, b.adapters, b.pool, ws)
+    Y = fetch()
+    check_big()
+    for p in range(w.n_projs):
+        assert np.array_equal(Y[p], Yref[p]), p
+    # the split entry points on the larger buffer (v strided by its capacity)
+    for y in b.Y:
+        y.fill_(7.0)
+    stride = Tc * lora.LORA_MAX_RANK
+    vs = [torch.empty(lora.lora_v_slices(t.d_in) * stride, dtype=torch.float32, device="cuda") for t in w.tables]
+    lora.lora_shrink(projs, b.adapters, big, b.pool, vs, stride)
+    lora.lora_expand(projs, b.adapters, big, b.pool, vs, 0, stride)
+    Y = fetch()
+    for p in range(w.n_projs):
+        assert np.array_equal(Y[p], Yref[p]), p
+    # reused with another token count: nothing computed, flag raised
+    for y in b.Y:
+        y.fill_(7.0)
+    lora.lora_apply(None, big, w.T - 1, projs, b.adapters, b.pool, ws)
+    Y = fetch()
+    assert int(big.counts()[lora.COUNT_FLAGS]) & lora.FLAG_SEGMENTS
+    for p in range(w.n_projs):
+        assert bool((b.Y[p].float() == 7.0).all()), p
+    # a buffer never built (zeroed counters): nothing computed, flag raised
+    fresh = lora.Segments(w.T, w.N)
+    fresh.buf.zero_()
+    lora.lora_apply(None, fresh, w.T, projs, b.adapters, b.pool, ws)
+    lora.lora_shrink(projs, b.adapters, fresh, b.pool, vs, stride)
+    lora.lora_expand(projs, b.adapters, fresh, b.pool, vs, 0, stride)
+    torch.cuda.synchronize()
+    assert int(fresh.counts()[lora.COUNT_FLAGS]) & lora.FLAG_SEGMENTS
+    for p in range(w.n_projs):
+        assert bool((b.Y[p].float() == 7.0).all()), p

@@ -250,3 +250,51 @@ def test_upload_rejects_bad_arguments_before_any_copy():
     assert L.lora_upload_pages(ctypes.byref(pool), src, None, 2, None) == INVALID_ARG
     assert L.lora_upload_pages(ctypes.byref(pool), src, ids, -1, None) == INVALID_ARG
     assert L.lora_upload_pages(ctypes.byref(pool), None, None, 0, None) == 0
+
+
+def _state(n_adapters=8, pages_each=3, capacity=6):
+    from heterogeneous_adapters_amd.pool import PoolState
+    ip = np.arange(n_adapters + 1, dtype=np.int64)          # one A slot per adapter
+    ipb = np.arange(n_adapters + 1, dtype=np.int64) * (pages_each - 1)  # the rest B slots
+    return PoolState([(ip, ipb)], capacity)
+
+
+def test_upload_order_after_a_failed_batch():
+    """A batch that does not fit evicts resident adapters before it fails; its
+    rollback frees the pages it had taken, which the evicted adapters' work,
+    already enqueued, may still read.  The next batch that takes those pages
+    without evicting anything itself must still order its uploads after that
+    work (the decision ManagedPool.ensure acts on)."""
+    st = _state()
+    for a in (0, 1):
+        missed, plan, fence = st.admit([a])
+        assert missed == [a] and len(plan) == 1 and not fence
+        st.unpin([a])
+    assert st.cache.free_pages == 0
+    with pytest.raises(lora.LoraError):
+        st.admit([2, 3, 4])        # evicts 0 and 1, then 4 does not fit
+    assert st.pinned == set() and st.cache.num_resident == 0 and st.cache.free_pages == 6
+    missed, plan, fence = st.admit([5])
+    assert missed == [5] and fence, "pages of evicted adapters reused without waiting for their readers"
+    st.unpin([5])
+    # the wait covered every page freed so far: the next miss into free pages needs none
+    missed, plan, fence = st.admit([6])
+    assert missed == [6] and not fence
+    # a batch of hits uploads nothing and keeps a pending wait for the next upload
+    st.unpin([6])
+    with pytest.raises(lora.LoraError):
+        st.admit([6, 1, 2])        # 6 hits, 1 evicts 5, then 2 does not fit
+    assert st.fence_pending
+    missed, plan, fence = st.admit([6])
+    assert missed == [] and plan == [] and not fence and st.fence_pending
+    st.unpin([6])
+    missed, plan, fence = st.admit([0])
+    assert missed == [0] and fence and not st.fence_pending
+
+
+def test_upload_order_evictions_in_a_successful_batch():
+    st = _state()
+    st.admit([0]); st.unpin([0])
+    st.admit([1]); st.unpin([1])
+    missed, plan, fence = st.admit([2])   # evicts 0
+    assert missed == [2] and fence
