@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "liblora.so")
 SOURCES = [os.path.join(CSRC, "lora_kernels.hip"), os.path.join(CSRC, "lora_abi.cpp"),
-           os.path.join(CSRC, "lora_pool.cpp")]
+           os.path.join(CSRC, "lora_pool.cpp"), os.path.join(CSRC, "lora_noalloc.hip")]
 ARCH = "gfx950"
 
 

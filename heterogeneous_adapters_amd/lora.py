@@ -56,7 +56,8 @@ EXPORTS = ("lora_status_string", "lora_v_slices", "lora_segments_size", "lora_se
            "lora_workspace_size", "lora_build_segments", "lora_shrink", "lora_expand", "lora_apply",
            "lora_validate_tables", "lora_cache_create", "lora_cache_destroy", "lora_cache_free_pages",
            "lora_cache_num_resident", "lora_cache_admit", "lora_cache_set_pinned", "lora_cache_release",
-           "lora_cache_lookup", "lora_upload_pages")
+           "lora_cache_lookup", "lora_upload_pages", "lora_apply_noalloc")
+LORA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class LoraError(RuntimeError):
@@ -90,6 +91,8 @@ def lib():
                                   P(lora_pool_t), P(_vp), _i32, _i64, _vp]
         L.lora_apply.argtypes = [_vp, P(lora_segments_t), _i32, P(lora_proj_t), _i32, P(lora_adapters_t),
                                  P(lora_pool_t), _vp, ctypes.c_size_t, _vp]
+        L.lora_apply_noalloc.argtypes = [_vp, P(lora_segments_t), _i32, P(lora_proj_t), _i32,
+                                         P(lora_adapters_t), P(lora_pool_t), _vp]
         L.lora_validate_tables.argtypes = [_i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
         L.lora_cache_create.argtypes = [_i32, P(_vp)]
         L.lora_cache_destroy.argtypes = [_vp]
@@ -104,7 +107,7 @@ def lib():
         L.lora_cache_lookup.argtypes = [_vp, _i64, _vp, _i32, P(_i32)]
         L.lora_upload_pages.argtypes = [P(lora_pool_t), _vp, _vp, _i32, _vp]
         for name in ("lora_segments_init", "lora_build_segments", "lora_shrink", "lora_expand",
-                     "lora_apply", "lora_validate_tables", "lora_cache_create", "lora_cache_admit",
+                     "lora_apply", "lora_apply_noalloc", "lora_validate_tables", "lora_cache_create", "lora_cache_admit",
                      "lora_cache_set_pinned", "lora_cache_release", "lora_cache_lookup", "lora_upload_pages"):
             getattr(L, name).restype = _i32
         _lib = L
@@ -272,6 +275,15 @@ def lora_apply(ids: Optional[torch.Tensor], segs: Optional[Segments], T: int, pr
     _check("lora_apply", lib().lora_apply(
         _ptr(ids), ctypes.byref(segs.c) if segs is not None else None, T, arr, len(projs),
         ctypes.byref(adapters.c), ctypes.byref(pool.c), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def lora_apply_noalloc(ids: Optional[torch.Tensor], segs: Optional[Segments], T: int, projs: Sequence[Proj],
+                       adapters: Adapters, pool: Pool, stream=None) -> None:
+    """lora_apply on the library's own fixed device array (no workspace)."""
+    arr = (lora_proj_t * max(len(projs), 1))(*[p.c for p in projs])
+    _check("lora_apply_noalloc", lib().lora_apply_noalloc(
+        _ptr(ids), ctypes.byref(segs.c) if segs is not None else None, T, arr, len(projs),
+        ctypes.byref(adapters.c), ctypes.byref(pool.c), _stream(stream)))
 
 
 def lora_validate_tables(rank, d_in: int, d_out: int, page_width: int, num_pages: int,

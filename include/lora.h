@@ -261,6 +261,27 @@ lora_status_t lora_apply(const int32_t* ids, const lora_segments_t* segs, int32_
                          const lora_adapters_t* adapters, const lora_pool_t* pool, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* lora_apply without a workspace argument, for callers that cannot allocate
+ * device memory when they call (code under HIP graph capture, serving loops
+ * that must not allocate, harnesses that forbid it).  The workspace is a
+ * fixed array of LORA_NOALLOC_SCRATCH_BYTES owned by the library: one copy
+ * per GPU, allocated when the library's code is loaded on that GPU and held
+ * until the process ends.  Arguments, segment handling and results are those
+ * of lora_apply; nothing is allocated by the call.
+ * Every call on one GPU uses that GPU's array, and the array keeps the last
+ * call's contents (nothing in it has to start at zero): calls that may
+ * overlap on one GPU (different streams, or different host threads without
+ * ordering) race on it and must not be issued.
+ * Errors: those of lora_apply, and WORKSPACE when lora_workspace_size(T, N,
+ * n_projs, max d_in) exceeds LORA_NOALLOC_SCRATCH_BYTES (a decode batch fits:
+ * 1024 tokens over 1000 adapters with three 4096-wide or one 11008-wide
+ * projection per call need 12.7 MiB and 11.7 MiB). */
+#define LORA_NOALLOC_SCRATCH_BYTES (64u << 20)
+lora_status_t lora_apply_noalloc(const int32_t* ids, const lora_segments_t* segs, int32_t T,
+                                 const lora_proj_t* projs, int32_t n_projs,
+                                 const lora_adapters_t* adapters, const lora_pool_t* pool,
+                                 void* stream);
+
 /* Host-side check of page tables (all arguments host copies): every adapter
  * owns exactly ceil(r/16)*ceil(d/PW) slots and every page id lies in
  * [0, num_pages) ([MLSA] "Trade-offs, Gotchas": validate shape and rank

@@ -308,3 +308,25 @@ def test_plan_capacities_bound_every_item_table(tmp_path):
     res = subprocess.run([str(exe)], capture_output=True, text=True)
     assert res.returncode == 0 and res.stdout.strip().endswith("OK"), res.stdout
 
+
+def test_noalloc_refuses_batches_beyond_its_array():
+    """lora_apply_noalloc sizes the call before anything else: a batch whose
+    workspace exceeds the library's fixed array is refused with WORKSPACE
+    (the descriptors point at host memory: nothing is dereferenced)."""
+    b = _Buf()
+    L = lora.lib()
+    r = ctypes.byref
+    v = ctypes.c_void_p(b.p())
+    ad = lora.lora_adapters_t(b.p(), b.p(64), 16)
+    pool = lora.lora_pool_t(b.p(), 4, 4096, lora.LORA_DTYPE_BF16)
+    one = (lora.lora_proj_t * 1)(lora.lora_proj_t(b.p(), 4096, b.p(), 4096, b.p(), 4096, 4096, 4096,
+                                                  b.p(), b.p(), b.p(), b.p()))
+    T = 38781  # a prefill batch: 8 slices x T x 128 x 4 bytes of partial sums
+    assert L.lora_workspace_size(T, 16, 1, 4096) > lora.LORA_NOALLOC_SCRATCH_BYTES
+    assert L.lora_apply_noalloc(v, None, T, one, 1, r(ad), r(pool), None) == -4
+    assert L.lora_apply_noalloc(v, None, -1, one, 1, r(ad), r(pool), None) == -1
+    assert L.lora_apply_noalloc(v, None, 8, None, 1, r(ad), r(pool), None) == -1
+    assert L.lora_apply_noalloc(v, None, 8, one, 1, None, r(pool), None) == -1
+    txt = open(HEADERS[0]).read()
+    assert re.search(r"#define LORA_NOALLOC_SCRATCH_BYTES \(64u << 20\)", txt)
+    assert lora.LORA_NOALLOC_SCRATCH_BYTES == 64 << 20
