@@ -48,12 +48,12 @@ SegSizes seg_sizes(int32_t T, int32_t N) {
 
 // Pointers of the plan area of a segment buffer laid out for (T, N).
 struct PlanPtrs {
-  int32_t *seg_desc, *shr_m, *shr_v, *exp_m, *exp_v;
+  int32_t *seg_desc, *shr_m, *shr_v, *exp_m, *exp_v, *sync;
 };
 PlanPtrs plan_ptrs(const lora_segments_t* s) {
   const PlanLayout L = plan_layout(s->T, s->num_adapters);
   return PlanPtrs{s->plan + L.seg_desc, s->plan + L.shrink_mfma, s->plan + L.shrink_valu, s->plan + L.expand_mfma,
-                  s->plan + L.expand_valu};
+                  s->plan + L.expand_valu, s->plan + L.sync};
 }
 
 size_t hist_bytes(int32_t T, int32_t N) {
@@ -110,6 +110,7 @@ struct DeviceInfo {
   int cus = 0;
   int occ_shrink[2] = {0, 0};
   int occ_expand[2] = {0, 0};
+  int occ_apply[2] = {0, 0};
 };
 constexpr int kMaxDevices = 64;
 DeviceInfo g_dev[kMaxDevices];
@@ -121,14 +122,16 @@ lora_status_t device_info(const DeviceInfo** out) {
   if (!d.ready.load(std::memory_order_acquire)) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return LORA_ERR_HIP;
-    int s0 = 0, e0 = 0, s1 = 0, e1 = 0;
-    if (occupancy(LORA_DTYPE_F32, &s0, &e0) != hipSuccess) return LORA_ERR_HIP;
-    if (occupancy(LORA_DTYPE_BF16, &s1, &e1) != hipSuccess) return LORA_ERR_HIP;
+    int s0 = 0, e0 = 0, a0 = 0, s1 = 0, e1 = 0, a1 = 0;
+    if (occupancy(LORA_DTYPE_F32, &s0, &e0, &a0) != hipSuccess) return LORA_ERR_HIP;
+    if (occupancy(LORA_DTYPE_BF16, &s1, &e1, &a1) != hipSuccess) return LORA_ERR_HIP;
     d.cus = std::max(cus, 1);
     d.occ_shrink[0] = std::max(s0, 1);
     d.occ_expand[0] = std::max(e0, 1);
+    d.occ_apply[0] = std::max(a0, 1);
     d.occ_shrink[1] = std::max(s1, 1);
     d.occ_expand[1] = std::max(e1, 1);
+    d.occ_apply[1] = std::max(a1, 1);
     d.ready.store(1, std::memory_order_release);
   }
   *out = &d;
@@ -136,6 +139,18 @@ lora_status_t device_info(const DeviceInfo** out) {
 }
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Bound of the apply kernel's phase wait (lora_set_wait_limit): ns > 0 a
+// bound, 0 the default, < 0 a forced give-up after |ns|.
+constexpr int64_t kDefaultWaitNs = 50'000'000;
+std::atomic<int64_t> g_wait_ns{0};
+
+void wait_params(KArgs& K) {
+  const int64_t ns = g_wait_ns.load(std::memory_order_relaxed);
+  const int64_t bound = ns == 0 ? kDefaultWaitNs : (ns > 0 ? ns : -ns);
+  K.wait_ticks = std::max<int64_t>(bound / 10, 1);  // s_memrealtime counts at 100 MHz
+  K.wait_bias = ns < 0 ? 1 : 0;
+}
 
 int grid_for(int resident, int64_t bound) {
   int64_t g = std::min<int64_t>(resident, std::max<int64_t>(bound, 1));
@@ -190,6 +205,8 @@ void fill_common(KArgs& K, const lora_segments_t* s, const lora_pool_t* pool, in
   K.cap_sv = (int32_t)L.cap_shrink_valu;
   K.cap_em = (int32_t)L.cap_expand_mfma;
   K.cap_ev = (int32_t)L.cap_expand_valu;
+  K.sync = pp.sync;
+  wait_params(K);
 }
 
 // Projections of one launch that read the same activations (q/k/v, gate/up
@@ -231,6 +248,11 @@ lora_status_t run(const KArgs& K, int dtype, bool do_shrink, bool do_expand, hip
   const DeviceInfo* d = nullptr;
   if (lora_status_t st = device_info(&d)) return st;
   const int di = dtype == LORA_DTYPE_BF16 ? 1 : 0;
+  if (do_shrink && do_expand)  // one launch; its grid is resident at once
+    return launch_apply(K, dtype, grid_for(d->cus * d->occ_apply[di], ceil_div64(std::max(bs, be), kWaves)),
+                        stream) == hipSuccess
+               ? LORA_OK
+               : LORA_ERR_HIP;
   // items are per wave: kWaves items per work-group
   if (do_shrink && launch_shrink(K, dtype, grid_for(d->cus * d->occ_shrink[di], ceil_div64(bs, kWaves)), stream) !=
                        hipSuccess)
@@ -244,8 +266,8 @@ lora_status_t run(const KArgs& K, int dtype, bool do_shrink, bool do_expand, hip
 lora_status_t build_into(const int32_t* ids, int32_t T, const lora_adapters_t* ad, const lora_segments_t* segs,
                          int32_t* hist, hipStream_t stream) {
   const PlanPtrs pp = plan_ptrs(segs);
-  SegOut o{segs->perm, segs->seg_indptr, segs->seg_adapter, segs->v_indptr, pp.seg_desc,
-           pp.shr_m,   pp.shr_v,         pp.exp_m,          pp.exp_v,       segs->counts};
+  SegOut o{segs->perm, segs->seg_indptr, segs->seg_adapter, segs->v_indptr, pp.seg_desc, pp.shr_m,
+           pp.shr_v,   pp.exp_m,         pp.exp_v,          segs->counts,   pp.sync};
   return launch_build_segments(ids, T, ad->num_adapters, ad->rank, ad->alpha, hist, o, stream) == hipSuccess
              ? LORA_OK
              : LORA_ERR_HIP;
@@ -269,6 +291,8 @@ const char* lora_status_string(lora_status_t s) {
     default: return "unknown status";
   }
 }
+
+void lora_set_wait_limit(int64_t ns) { g_wait_ns.store(ns, std::memory_order_relaxed); }
 
 int32_t lora_v_slices(int32_t d_in) { return d_in <= 0 ? 0 : ceil_div_i(d_in, LORA_KSLICE); }
 

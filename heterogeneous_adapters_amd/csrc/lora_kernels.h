@@ -46,6 +46,12 @@ struct KArgs {
   int32_t s_cap, cap_sm, cap_sv, cap_em, cap_ev;
   int32_t np;
   int32_t xshare;  // every projection of the launch reads the same X (same pointer, ldx, d_in)
+  // the apply kernel's phase barrier: the segment buffer's sync area, the
+  // bound of the wait in 100 MHz ticks, and an offset added to the wait's
+  // target (> 0 only to force the give-up path in tests)
+  int32_t* sync;
+  int64_t wait_ticks;
+  int32_t wait_bias;
 };
 
 struct SegOut {
@@ -59,12 +65,14 @@ struct SegOut {
   int32_t* exp_item_m;
   int32_t* exp_item_v;
   int32_t* counts;
+  int32_t* sync;
 };
 
 hipError_t launch_build_segments(const int32_t* ids, int T, int N, const int32_t* rank, const float* alpha,
                                  int32_t* hist, const SegOut& out, hipStream_t stream);
 hipError_t launch_shrink(const KArgs& K, int dtype, int grid, hipStream_t stream);
 hipError_t launch_expand(const KArgs& K, int dtype, int grid, hipStream_t stream);
-hipError_t occupancy(int dtype, int* shrink_blocks, int* expand_blocks);
+hipError_t launch_apply(const KArgs& K, int dtype, int grid, hipStream_t stream);
+hipError_t occupancy(int dtype, int* shrink_blocks, int* expand_blocks, int* apply_blocks);
 
 }  // namespace lora

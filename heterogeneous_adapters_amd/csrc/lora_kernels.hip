@@ -96,6 +96,22 @@ __device__ int4 cld4(const int4* p);
 #endif
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// The rank-r partial sums v: plain loads and stores between two launches;
+// in the single-launch apply kernel (CO) agent-scope atomic accesses, since
+// a partial written by a wave on one XCD is read by waves on others while
+// the kernel runs.  On gfx950 these are ordinary loads and stores with the
+// sc1 bit (coherent at agent scope, write-through) -- no cache maintenance.
+template <bool CO>
+__device__ __forceinline__ float vld(const float* p) {
+  if constexpr (CO) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool CO>
+__device__ __forceinline__ void vst(float* p, float x) {
+  if constexpr (CO) __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = x;
+}
+
 // 8-wide bf16 dot product accumulated in fp32 (v_dot2_f32_bf16).
 __device__ __forceinline__ float dot16(uint4 w, uint4 x, float acc, Bf16) {
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, x.x), acc, false);
@@ -240,63 +256,6 @@ __device__ __forceinline__ float wave_reduce_scatter32(float (&v)[32], int lane)
   return e + dpp_f<kDppQuadXor1>(e);    // bit 0
 }
 
-// ================================================================ work walk
-// XCD-aware wave walk: the item range [0, total) is cut into 8 contiguous
-// parts, part x served by the waves of the work-groups with blockIdx.x % 8
-// == x (work-groups are dealt to the XCDs round robin), so items that share
-// an adapter slice are read through the same L2.  Every wave walks its own
-// items: no work-group barrier couples the waves.
-struct WaveWalk {
-  int i, end, stride, lo;
-  // `walkers` items are taken per block at a time (kWaves: one per wave; 1:
-  // whole-block items), `w` is this walker's index in the block.
-  __device__ WaveWalk(int total, int w, int walkers = kWaves) {
-    const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
-    const int x = blockIdx.x % nx;
-    lo = (int)(((int64_t)total * x) / nx);
-    end = (int)(((int64_t)total * (x + 1)) / nx);
-    i = lo + (int)(blockIdx.x / nx) * walkers + w;
-    stride = (gridDim.x / nx) * walkers;
-  }
-};
-
-// The MBGMV walk when the first Wm waves of each XCD run the MBGMM items:
-// the other waves take R rounds of the XCD's MBGMV items among themselves (R:
-// the MBGMV items that take as long as one wave's MBGMM items), then every
-// wave takes items in turn.
-struct TwoClassWalk {
-  int i, end, nV, W, ib, ka;  // ka: first-phase items left after the current one (-1: second phase)
-  __device__ TwoClassWalk(int total, int Wm, int R, int wv) {
-    const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
-    const int x = blockIdx.x % nx, G = gridDim.x / nx;
-    const int w = (int)(blockIdx.x / nx) * kWaves + wv;  // walker index inside the XCD
-    const int lo = (int)(((int64_t)total * x) / nx);
-    end = (int)(((int64_t)total * (x + 1)) / nx);
-    W = G * kWaves;
-    Wm = min(Wm, W);
-    nV = W - Wm;
-    ib = lo + R * nV + w;
-    if (w >= Wm && R > 0) {
-      i = lo + (w - Wm);
-      ka = R - 1;
-    } else {
-      i = ib;
-      ka = -1;
-    }
-  }
-  __device__ int next() {
-    if (ka > 0) {
-      --ka;
-      return i + nV;
-    }
-    if (ka == 0) {
-      ka = -1;
-      return ib;
-    }
-    return i + W;
-  }
-};
-
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -304,6 +263,7 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 
 // The kernels take one by-value KArgs argument, which sits at offset 0 of the
 // kernel-argument segment.  They read it through the segment pointer, so a
@@ -343,6 +303,46 @@ __device__ __forceinline__ PlanCounts read_counts(const KArgs& K) {
   if (!c.ok && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&K.counts[kCountFlags], LORA_FLAG_SEGMENTS);
   return c;
 }
+
+// The expand side of the apply kernel's phase barrier.  Every wave waits,
+// once, before it first reads v: the counter of XCDs whose work-groups have
+// all written their shrink partial sums must reach its target.  The wait is
+// bounded (s_memrealtime, a 100 MHz clock); past the bound the wave gives
+// up, raises LORA_FLAG_SYNC and goes on (the call's Y is then invalid).  In
+// the two-launch kernels `done` is null and nothing is waited for.
+struct PhaseWait {
+  const int* done;
+  int target;
+  long long ticks;
+  bool passed;
+  __device__ bool ready() const { return passed; }
+  __device__ void wait(const KArgs& K) {
+    if (passed) return;
+    passed = true;
+    if (!done) return;
+    const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
+    for (;;) {
+      const int v = uniform(__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (v >= target) return;
+      if ((long long)__builtin_amdgcn_s_memrealtime() - t0 > ticks) {
+        if ((threadIdx.x & 63) == 0) atomicOr(&K.counts[kCountFlags], LORA_FLAG_SYNC);
+        return;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+  }
+};
+
+// The MBGMV item sequence of one wave: first() gives its first item (-1:
+// none), issue() / resolve() the next one (-1: none left).
+struct StaticWalk {
+  TwoClassWalk tw;
+  int pend;
+  __device__ StaticWalk(int total, int Wm, int R, int wave) : tw(total, Wm, R, wave, gridDim.x, blockIdx.x) {}
+  __device__ int first() { return tw.i < tw.end ? tw.i : -1; }
+  __device__ void issue() { pend = tw.next(); tw.i = pend; }
+  __device__ int resolve() { return pend < tw.end ? pend : -1; }
+};
 
 // ================================================================ shrink
 // MBGMV item (one wave): (segment, rank group g, <= 2 tokens, 512-column
@@ -406,7 +406,7 @@ __device__ __forceinline__ ShrinkItem fetch_shrink_item(const KArgs& K, int i, i
 // 64 lanes are reduced across the wave.  All loads are issued before the
 // first product, so an item costs one memory round trip; the next item's
 // metadata is fetched while they are in flight.
-template <class E, bool WIDE, class Prefetch>
+template <class E, bool WIDE, bool CO, class Prefetch>
 __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, const ShrinkItem& item, int lane,
                                             Prefetch&& prefetch) {
   typedef typename E::T T;
@@ -487,7 +487,7 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, cons
   const int vi = lane >> 1;
   const int rr = vi / NV, tt = vi % NV;
   if ((lane & 1) == 0 && rr < rows && tt < nt)
-    P.v[(int64_t)q * K.v_stride + d1.x + (int64_t)(tb + tt) * r + g * 16 + rr] = sum;
+    vst<CO>(P.v + (int64_t)q * K.v_stride + d1.x + (int64_t)(tb + tt) * r + g * 16 + rr, sum);
 }
 
 // MBGMM item (one wave): (segment, 16*NTT-token tile, rank group g, slice q):
@@ -498,7 +498,7 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, cons
 // MFMAs (2*NTT memory round trips per item).  The rank groups of a token tile
 // are consecutive items, so the tile's activations are re-read from the L2
 // that holds them.
-template <class E, bool WIDE, int NTT>
+template <class E, bool WIDE, int NTT, bool CO>
 __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int q, int4 d0, int4 d1, int local,
                                             int lane) {
   typedef typename E::T T;
@@ -586,49 +586,27 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
       float* dst = P.v + (int64_t)q * K.v_stride + d1.x + (int64_t)(tb + s * 16 + li) * r + k0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (k0 + i < r) dst[i] = acc[s][i];
+        if (k0 + i < r) vst<CO>(dst + i, acc[s][i]);
     }
   }
 }
 
-// MBGMV rounds one MBGMM shrink item is worth (measured: 2 and 4 were slower)
-constexpr int kShrinkMfmaRounds = 3;
-
 // WIDE: pages hold at least one whole 512-column slice, so every page
 // lookup of an item is wave-uniform; chosen by the host from the page width.
-template <class E, bool WIDE>
-__global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArgs) {
-  const KArgs& K = kernel_args();
-  const PlanCounts pc = read_counts(K);
-  if (!pc.ok || pc.S <= 0) return;
-  const int Um = pc.shr_m, Uv = pc.shr_v;
-  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  // MBGMM items first, then MBGMV items; each path walks its own item list,
-  // so the two register footprints never share a loop body.  The wave's
-  // first MBGMV item's metadata is requested before the MBGMM pass.
-  int total_v = 0;
-  for (int p = 0; p < K.np; ++p) total_v += K.p[p].nq * Uv;
-  int total = 0;
-  for (int p = 0; p < K.np; ++p) total += K.p[p].nq * Um;
-  // The MBGMM items go to the first waves of each XCD's walk.  When they are
-  // a small share of the items (under one in eight: a decode batch's hot
-  // adapters, whose segments are short enough for 32-token items), those
-  // waves skip the first rounds of MBGMV items: a 32-token MBGMM item is four
-  // rounds of loads against one for an MBGMV item.
-  int Wm = 0, R = 0;
-  if (total > 0 && 8 * (int64_t)total < total_v) {
-    WaveWalk im(total, wave);
-    const int m = im.end - im.lo;
-    Wm = min(m, im.stride);
-    R = kShrinkMfmaRounds * ceil_div_i(m, im.stride);
-  }
-  TwoClassWalk iv(total_v, Wm, R, wave);
+// The shrink items of one wave: its MBGMM items (the static XCD-aware walk),
+// then its MBGMV items in the order `walk` gives them.
+template <class E, bool WIDE, bool CO, class Walk>
+__device__ __forceinline__ void shrink_items(const KArgs& K, Walk walk, int total, int Um, int Uv, int wave,
+                                             int lane) {
+  const int grid = gridDim.x, block = blockIdx.x;
+  // The wave's first MBGMV item's metadata is requested before the MBGMM pass.
   ShrinkItem cur;
-  if (iv.i < iv.end) cur = fetch_shrink_item<WIDE>(K, iv.i, Uv);
+  const int i0 = walk.first();
+  if (i0 >= 0) cur = fetch_shrink_item<WIDE>(K, i0, Uv);
   // Item order: projection-major, or -- when every projection of the launch
   // reads the same X -- projection-minor, so the siblings' items for one
   // (slice, item) run side by side and their X rows come from L2.
-  for (WaveWalk it(total, wave); it.i < it.end; it.i += it.stride) {
+  for (WaveWalk it(total, wave, kWaves, grid, block); it.i < it.end; it.i += it.stride) {
     int p, q, u;
     if (K.xshare) {
       p = it.i % K.np;
@@ -645,22 +623,48 @@ __global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArg
     const int s = cld(K.shr_item_m + u);
     const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
     if (shrink_tile_tokens(d0.w) == kMfmaShrinkTokensLong)
-      shrink_mfma<E, WIDE, kMfmaShrinkTokensLong / 16>(K, K.p[p], q, d0, d1, u - d1.y, lane);
+      shrink_mfma<E, WIDE, kMfmaShrinkTokensLong / 16, CO>(K, K.p[p], q, d0, d1, u - d1.y, lane);
     else
-      shrink_mfma<E, WIDE, kMfmaShrinkTokensShort / 16>(K, K.p[p], q, d0, d1, u - d1.y, lane);
+      shrink_mfma<E, WIDE, kMfmaShrinkTokensShort / 16, CO>(K, K.p[p], q, d0, d1, u - d1.y, lane);
   }
-  if (iv.i >= iv.end) return;
+  if (i0 < 0) return;
   for (;;) {
-    const int ni = iv.next();
-    const bool more = ni < iv.end;
+    walk.issue();
+    int ni = -1;
     ShrinkItem nxt;
-    shrink_valu<E, WIDE>(K, K.p[cur.p], cur, lane, [&]() {
-      if (more) nxt = fetch_shrink_item<WIDE>(K, ni, Uv);
+    shrink_valu<E, WIDE, CO>(K, K.p[cur.p], cur, lane, [&]() {
+      ni = walk.resolve();
+      if (ni >= 0) nxt = fetch_shrink_item<WIDE>(K, ni, Uv);
     });
-    if (!more) break;
+    if (ni < 0) break;
     cur = nxt;
-    iv.i = ni;
   }
+}
+
+template <class E, bool WIDE, bool CO>
+__device__ __forceinline__ void shrink_phase(const KArgs& K, const PlanCounts& pc) {
+  if (pc.S <= 0) return;
+  const int Um = pc.shr_m, Uv = pc.shr_v;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // MBGMM items first, then MBGMV items; each path walks its own item list,
+  // so the two register footprints never share a loop body.  The wave's
+  // first MBGMV item's metadata is requested before the MBGMM pass.
+  int total_v = 0;
+  for (int p = 0; p < K.np; ++p) total_v += K.p[p].nq * Uv;
+  int total = 0;
+  for (int p = 0; p < K.np; ++p) total += K.p[p].nq * Um;
+  const int grid = gridDim.x, block = blockIdx.x;
+  int Wm, R;
+  shrink_walk_split(total, total_v, wave, grid, block, Wm, R);
+  shrink_items<E, WIDE, CO>(K, StaticWalk(total_v, Wm, R, wave), total, Um, Uv, wave, lane);
+}
+
+template <class E, bool WIDE>
+__global__ __launch_bounds__(kThreads, E::kShrinkBlocks) void shrink_kernel(KArgs) {
+  const KArgs& K = kernel_args();
+  const PlanCounts pc = read_counts(K);
+  if (!pc.ok) return;
+  shrink_phase<E, WIDE, false>(K, pc);
 }
 
 // ================================================================ expand
@@ -677,7 +681,7 @@ struct RowStage {
   float x[SF][M];
 };
 
-template <int NT, int M, int SF>
+template <int NT, int M, int SF, bool CO>
 __device__ __forceinline__ void row_load(const KArgs& K, const KProj& P, const float* src, int q, int e0, int ne,
                                          int tid, RowStage<M, SF>& st) {
 #pragma unroll
@@ -685,7 +689,7 @@ __device__ __forceinline__ void row_load(const KArgs& K, const KProj& P, const f
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const int e = e0 + tid + NT * m;
-      st.x[j][m] = (q + j < P.nv && e < ne) ? src[(int64_t)(q + j) * K.v_stride + e] : 0.0f;
+      st.x[j][m] = (q + j < P.nv && e < ne) ? vld<CO>(src + (int64_t)(q + j) * K.v_stride + e) : 0.0f;
     }
 }
 
@@ -710,14 +714,14 @@ __device__ __forceinline__ void row_store(const RowStage<M, SF>& st, int e0, int
   }
 }
 
-template <int NT, int M, int SF>
+template <int NT, int M, int SF, bool CO>
 __device__ __forceinline__ void stage_v_pass(const KArgs& K, const KProj& P, const float* src, int e0, int ne,
                                              int r, int rs, float* vs, int tid) {
   RowStage<M, SF> st;
 #pragma unroll
   for (int m = 0; m < M; ++m) st.acc[m] = 0.0f;
   for (int q = 0; q < P.nv; q += SF) {
-    row_load<NT, M, SF>(K, P, src, q, e0, ne, tid, st);
+    row_load<NT, M, SF, CO>(K, P, src, q, e0, ne, tid, st);
     row_add<M, SF>(st);
   }
   row_store<NT, M, SF>(st, e0, ne, r, rs, vs, tid);
@@ -733,22 +737,23 @@ __device__ __forceinline__ void stage_v_pad(int r, int nt, float* vs, int tid) {
   }
 }
 
-template <int NT>
+template <int NT, bool CO>
 __device__ __forceinline__ void stage_v_rows(const KArgs& K, const KProj& P, int voff, int r, int tb, int nt,
                                              float* vs, int tid) {
   const int rs = rank_groups(r) * 16;
   const int ne = nt * r;
   const float* src = P.v + voff + (int64_t)tb * r;
-  if (ne <= 2 * NT) stage_v_pass<NT, 2, 8>(K, P, src, 0, ne, r, rs, vs, tid);
+  if (ne <= 2 * NT) stage_v_pass<NT, 2, 8, CO>(K, P, src, 0, ne, r, rs, vs, tid);
   else
-    for (int e0 = 0; e0 < ne; e0 += NT * 8) stage_v_pass<NT, 8, 2>(K, P, src, e0, ne, r, rs, vs, tid);
+    for (int e0 = 0; e0 < ne; e0 += NT * 8) stage_v_pass<NT, 8, 2, CO>(K, P, src, e0, ne, r, rs, vs, tid);
   stage_v_pad<NT>(r, nt, vs, tid);
 }
 
 // one wave stages its own rows
+template <bool CO>
 __device__ __forceinline__ void stage_v(const KArgs& K, const KProj& P, int voff, int r, int tb, int nt,
                                         float* vs, int lane) {
-  stage_v_rows<64>(K, P, voff, r, tb, nt, vs, lane);
+  stage_v_rows<64, CO>(K, P, voff, r, tb, nt, vs, lane);
   wave_sync();
 }
 
@@ -783,7 +788,7 @@ __device__ __forceinline__ void split_setup(SplitStage<M>& st, int p0, int np, i
   }
 }
 
-template <int M>
+template <int M, bool CO>
 __device__ __forceinline__ void split_load(const KArgs& K, const KProj& P, const float* src, int q, int r,
                                            SplitStage<M>& st) {
 #pragma unroll
@@ -792,8 +797,8 @@ __device__ __forceinline__ void split_load(const KArgs& K, const KProj& P, const
     for (int m = 0; m < M; ++m) {
       const float* a = src + (int64_t)(q + j) * K.v_stride + st.e[m];
       const bool ok = q + j < P.nv;
-      st.x[j][m][0] = ok && st.kk[m] < r ? a[0] : 0.0f;
-      st.x[j][m][1] = ok && st.kk[m] + 1 < r ? a[1] : 0.0f;
+      st.x[j][m][0] = ok && st.kk[m] < r ? vld<CO>(a) : 0.0f;
+      st.x[j][m][1] = ok && st.kk[m] + 1 < r ? vld<CO>(a + 1) : 0.0f;
     }
 }
 
@@ -815,28 +820,29 @@ __device__ __forceinline__ void split_store(const SplitStage<M>& st, uint32_t* v
     if (st.kk[m] < LORA_MAX_RANK) vs[st.dst[m]] = pack_bf2(st.acc[m][0], st.acc[m][1]);
 }
 
-template <int M>
+template <int M, bool CO>
 __device__ __forceinline__ void stage_v_split_pass(const KArgs& K, const KProj& P, const float* src, int p0,
                                                    int np, int r, int G, uint32_t* vs, int lane) {
   SplitStage<M> st;
   split_setup<M>(st, p0, np, r, G, lane);
   for (int q = 0; q < P.nv; q += SplitStage<M>::SF) {
-    split_load<M>(K, P, src, q, r, st);
+    split_load<M, CO>(K, P, src, q, r, st);
     split_add<M>(st);
   }
   split_store<M>(st, vs);
 }
 
+template <bool CO>
 __device__ __forceinline__ void stage_v_split(const KArgs& K, const KProj& P, int voff, int r, int n, uint32_t* vs,
                                               int lane) {
   const int G = rank_groups(r);
   const int np = n * G * 8;
   const float* src = P.v + voff;
   const int mm = ceil_div_i(np, 64);
-  if (mm <= 1) stage_v_split_pass<1>(K, P, src, 0, np, r, G, vs, lane);
-  else if (mm <= 2) stage_v_split_pass<2>(K, P, src, 0, np, r, G, vs, lane);
+  if (mm <= 1) stage_v_split_pass<1, CO>(K, P, src, 0, np, r, G, vs, lane);
+  else if (mm <= 2) stage_v_split_pass<2, CO>(K, P, src, 0, np, r, G, vs, lane);
   else
-    for (int p0 = 0; p0 < np; p0 += 64 * 4) stage_v_split_pass<4>(K, P, src, p0, np, r, G, vs, lane);
+    for (int p0 = 0; p0 < np; p0 += 64 * 4) stage_v_split_pass<4, CO>(K, P, src, p0, np, r, G, vs, lane);
   wave_sync();
 }
 
@@ -927,9 +933,9 @@ __device__ __forceinline__ uint32_t pack_cols(const float (&y)[1]) { return __fl
 // the chunk.  Pair i is (sub-block i % nsub, group g0 + i / nsub).  v of the
 // chunk's tokens is staged once; the tokens are then produced one at a time
 // from the B registers.
-template <class E, bool ONE_PAGE, class Prefetch>
+template <class E, bool ONE_PAGE, bool CO, class Prefetch>
 __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P, const ValuItem& item, float* vs,
-                                                 int lane, Prefetch&& prefetch) {
+                                                 int lane, PhaseWait& sw, bool fresh, Prefetch&& prefetch) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
   constexpr int CPL = 4 / (int)sizeof(T);
@@ -1021,10 +1027,12 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
   [[maybe_unused]] SplitStage<1> st1;
   [[maybe_unused]] const float* vsrc = P.v + d1.x + tb * r;
   [[maybe_unused]] const bool early = EPV == 8 && n * G * 8 <= 64;
+  // apply kernel: v is final only once the phase barrier has been passed
+  // (fresh); an early round issued before that is issued again after the wait
   if constexpr (EPV == 8) {
     if (early) {
       split_setup<1>(st1, 0, n * G * 8, r, G, lane);
-      split_load<1>(K, P, vsrc, 0, r, st1);
+      split_load<1, CO>(K, P, vsrc, 0, r, st1);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -1034,20 +1042,22 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
   __builtin_amdgcn_sched_barrier(0);
   prefetch();
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (CO) sw.wait(K);
   if constexpr (EPV == 8) {
     if (early) {
+      if (!fresh) split_load<1, CO>(K, P, vsrc, 0, r, st1);
       split_add<1>(st1);
       for (int q = SplitStage<1>::SF; q < P.nv; q += SplitStage<1>::SF) {
-        split_load<1>(K, P, vsrc, q, r, st1);
+        split_load<1, CO>(K, P, vsrc, q, r, st1);
         split_add<1>(st1);
       }
       split_store<1>(st1, reinterpret_cast<uint32_t*>(vs));
       wave_sync();
     } else {
-      stage_v_split(K, P, d1.x + tb * r, r, n, reinterpret_cast<uint32_t*>(vs), lane);
+      stage_v_split<CO>(K, P, d1.x + tb * r, r, n, reinterpret_cast<uint32_t*>(vs), lane);
     }
   } else {
-    stage_v(K, P, d1.x, r, tb, n, vs, lane);
+    stage_v<CO>(K, P, d1.x, r, tb, n, vs, lane);
   }
   for (int t = 0; t < n; ++t) {
     uint32_t (&yb)[NP] = ybt[0];  // token t's row; the rows move up one slot per token
@@ -1170,7 +1180,7 @@ constexpr int kExpandRowFloats = kMfmaExpandTokens * (LORA_MAX_RANK + 4);
 // ranks of an output column contiguously, so each lane's operand is one
 // 16-byte load, and a lane's four C values are four adjacent columns of one
 // token (one 8- or 16-byte Y access).
-template <class E, int NKS, bool WIDE>
+template <class E, int NKS, bool WIDE, bool CO>
 __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P, int j0, int jend, int wc, int a,
                                                  int r, int t0, int nt, float scale, float* vs, float* cw, int voff,
                                                  int tb, int lane) {
@@ -1255,7 +1265,7 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
   RowStage<2, 8> st0;
   if (early) {
     st0.acc[0] = st0.acc[1] = 0.0f;
-    row_load<kThreads, 2, 8>(K, P, vsrc, 0, 0, ne, threadIdx.x, st0);
+    row_load<kThreads, 2, 8, CO>(K, P, vsrc, 0, 0, ne, threadIdx.x, st0);
   }
   __builtin_amdgcn_sched_barrier(0);
   if (active) load_part(0, bcur, ycur, okcur);
@@ -1263,13 +1273,13 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
   if (early) {
     row_add<2, 8>(st0);
     for (int q = 8; q < P.nv; q += 8) {
-      row_load<kThreads, 2, 8>(K, P, vsrc, q, 0, ne, threadIdx.x, st0);
+      row_load<kThreads, 2, 8, CO>(K, P, vsrc, q, 0, ne, threadIdx.x, st0);
       row_add<2, 8>(st0);
     }
     row_store<kThreads, 2, 8>(st0, 0, ne, r, rs, vs, threadIdx.x);
     stage_v_pad<kThreads>(r, nt, vs, threadIdx.x);
   } else {
-    stage_v_rows<kThreads>(K, P, voff, r, tb, nt, vs, threadIdx.x);
+    stage_v_rows<kThreads, CO>(K, P, voff, r, tb, nt, vs, threadIdx.x);
   }
   __syncthreads();
   uint4 vv[NKS];
@@ -1340,7 +1350,7 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
 // MBGMM expand item (one block): (segment, 16-token tile, 4*wc columns).  The
 // block stages v of the tile once into shared LDS rows; wave w then produces
 // columns [w*wc, (w+1)*wc) of the item.
-template <class E, bool WIDE>
+template <class E, bool WIDE, bool CO>
 __device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int jb, int wc, int4 d0, int4 d1,
                                             int local, float* vs, float* cw, int wave, int lane) {
   constexpr int KSTEP = 4 * E::kEpv;
@@ -1356,10 +1366,10 @@ __device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int 
   // every rank; the choice is the same for the whole block (one segment)
   const int nks = ceil_div_i(r, KSTEP);
   if (WIDE && nks <= MAXKS / 4)  // bf16: one K step (r <= 32), so twice the columns per part
-    expand_mfma_body<E, MAXKS / 4, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
+    expand_mfma_body<E, MAXKS / 4, WIDE, CO>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
   else if (nks <= MAXKS / 2)
-    expand_mfma_body<E, MAXKS / 2, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
-  else expand_mfma_body<E, MAXKS, WIDE>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
+    expand_mfma_body<E, MAXKS / 2, WIDE, CO>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
+  else expand_mfma_body<E, MAXKS, WIDE, CO>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
   __syncthreads();  // the rows are restaged by the block's next item
 }
 
@@ -1388,14 +1398,40 @@ __device__ __forceinline__ void expand_copy(const KArgs& K, const KProj& P, int 
 // WIDE: pages hold at least one whole MBGMV column block (expand_cols), so
 // every page lookup of an item is wave-uniform; chosen by the host from the
 // page width (the other instantiation looks pages up per lane).
-template <class E, bool WIDE>
-__global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArgs) {
-  const KArgs& K = kernel_args();
-  // per-wave rows (MBGMV staging, MBGMM output tiles) and the block's staged
-  // v tile of an MBGMM item
-  __shared__ __attribute__((aligned(16))) float vs_all[kWaves + 1][kExpandRowFloats];
-  const PlanCounts pc = read_counts(K);
-  if (!pc.ok) return;
+// The MBGMV expand items and copies of rows without an adapter of one wave,
+// in the order `walk` gives them.
+template <class E, bool WIDE, bool CO, class Walk>
+__device__ __forceinline__ void expand_valu_items(const KArgs& K, Walk walk, const PlanCounts& pc, int Uv, int ncopy,
+                                                  float* vs, int lane, PhaseWait& sw) {
+  const int i0 = walk.first();
+  if (i0 < 0) return;
+  ValuItem cur = fetch_valu_item<E>(K, i0, Uv, ncopy);
+  for (;;) {
+    walk.issue();
+    int ni = -1;
+    ValuItem nxt;
+    if (cur.copy) {
+      expand_copy<E>(K, K.p[cur.p], cur.jb, cur.local, pc.t_valid, pc.T, lane);
+      ni = walk.resolve();
+      if (ni >= 0) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy);
+    } else {
+      const bool fresh = !CO || sw.ready();
+      expand_valu_body<E, WIDE, CO>(K, K.p[cur.p], cur, vs, lane, sw, fresh, [&]() {
+        ni = walk.resolve();
+        if (ni >= 0) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy);
+      });
+      wave_sync();
+    }
+    if (ni < 0) break;
+    cur = nxt;
+  }
+}
+
+// vs_all: per-wave LDS rows (MBGMV staging, MBGMM output tiles) and, in row
+// kWaves, the block's staged v tile of an MBGMM item.
+template <class E, bool WIDE, bool CO>
+__device__ __forceinline__ void expand_phase(const KArgs& K, const PlanCounts& pc,
+                                             float (*vs_all)[kExpandRowFloats], PhaseWait& sw) {
   const int t_valid = pc.t_valid;
   const int Um = pc.S > 0 ? pc.exp_m : 0;
   const int Uv = pc.S > 0 ? pc.exp_v : 0;
@@ -1404,34 +1440,23 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
   float* vs = vs_all[wave];
   // MBGMM items first (whole-block items), then MBGMV items and the copies of
   // rows without an adapter (one wave each); each path walks its own item
-  // list.  The columns per wave of an MBGMM item (128..512, at most the page
-  // width) shrink until the items cover the grid once, so a few hot segments
-  // still spread over every compute unit; wide items stage a token tile's v
-  // once for more columns.  (Covering the grid twice over, with narrower
+  // list.  (Covering the grid twice over with MBGMM items, with narrower
   // items, left each block two or three items in a row, each one memory
   // round trip.)
-  int Gm = 0, R = 0;  // MBGMM blocks per XCD; first MBGMV rounds the other blocks take alone
+  const int grid = gridDim.x, block = blockIdx.x;
   int total_v = 0;
   for (int p = 0; p < K.np; ++p) total_v += K.p[p].njs * (Uv + (K.p[p].Y != K.p[p].Yb ? ncopy : 0));
+  int total = 0, wc = 0;
+  if (Um > 0) wc = expand_mfma_cols(K.np, [&](int p) { return K.p[p].d_out; }, K.pw_log2, Um, grid, total);
+  const ExpandSplit es = expand_walk_split(total, total_v, grid, block);
   if (Um > 0) {
-    int wc = min(512, 1 << K.pw_log2), total = 0;
-    for (;; wc >>= 1) {
-      total = 0;
-      for (int p = 0; p < K.np; ++p) total += ceil_div_i(K.p[p].d_out, kWaves * wc) * Um;
-      if (wc <= 128 || total >= (int)gridDim.x) break;
+    // apply kernel: the block's MBGMM items read v from their start (the
+    // tile's staging overlaps its first B loads), so their waves wait for
+    // the phase barrier before the first one
+    if constexpr (CO) {
+      if (es.first < es.end_m) sw.wait(K);
     }
-    // When the MBGMM items are a small share of the launch's items (a decode
-    // batch with a few hot adapters: under one in eight), they go to the
-    // first third of each XCD's blocks (one per CU), so the other waves start
-    // streaming MBGMV weights at once and the MBGMM items' round trips overlap
-    // them; otherwise (prefill, mixed batches) to every block.
-    const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
-    const int x = blockIdx.x % nx, beta = blockIdx.x / nx, G = gridDim.x / nx;
-    const int lo_m = (int)(((int64_t)total * x) / nx), end_m = (int)(((int64_t)total * (x + 1)) / nx);
-    const int m = end_m - lo_m;
-    Gm = m <= 0 ? 0 : 8 * (int64_t)total >= total_v ? G : min(max(G / 3, 1), m);
-    R = Gm > 0 ? ceil_div_i(6 * m, 10 * Gm) : 0;  // an MBGMM item took ~0.6 MBGMV item times
-    for (int i = beta < Gm ? lo_m + beta : end_m; i < end_m; i += Gm) {
+    for (int i = es.first; i < es.end_m; i += es.step) {
       int rem = i, p = 0;
       int nb = ceil_div_i(K.p[0].d_out, kWaves * wc);
       while (rem >= nb * Um) {
@@ -1443,29 +1468,68 @@ __global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArg
       const int u = rem - jb * Um;
       const int s = cld(K.exp_item_m + u);
       const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
-      expand_mfma<E, WIDE>(K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[kWaves], vs_all[wave], wave, lane);
+      expand_mfma<E, WIDE, CO>(K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[kWaves], vs_all[wave], wave, lane);
     }
   }
-  TwoClassWalk it(total_v, Gm * kWaves, R, wave);
-  if (it.i >= it.end) return;
-  ValuItem cur = fetch_valu_item<E>(K, it.i, Uv, ncopy);
-  for (;;) {
-    const int ni = it.next();
-    const bool more = ni < it.end;
-    ValuItem nxt;
-    if (cur.copy) {
-      expand_copy<E>(K, K.p[cur.p], cur.jb, cur.local, t_valid, pc.T, lane);
-      if (more) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy);
-    } else {
-      expand_valu_body<E, WIDE>(K, K.p[cur.p], cur, vs, lane, [&]() {
-        if (more) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy);
-      });
-      wave_sync();
-    }
-    if (!more) break;
-    cur = nxt;
-    it.i = ni;
+  expand_valu_items<E, WIDE, CO>(K, StaticWalk(total_v, es.Gm * kWaves, es.R, wave), pc, Uv, ncopy, vs, lane, sw);
+}
+
+template <class E, bool WIDE>
+__global__ __launch_bounds__(kThreads, E::kExpandBlocks) void expand_kernel(KArgs) {
+  const KArgs& K = kernel_args();
+  __shared__ __attribute__((aligned(16))) float vs_all[kWaves + 1][kExpandRowFloats];
+  const PlanCounts pc = read_counts(K);
+  if (!pc.ok) return;
+  PhaseWait sw{nullptr, 0, 0, true};
+  expand_phase<E, WIDE, false>(K, pc, vs_all, sw);
+}
+
+// ================================================================ apply
+// The whole branch for a launch group in one launch ([MLSP] "Custom CUDA
+// Kernels: SGMV and MBGMV": fused operations rather than a launch per step).
+// Every wave runs its shrink items (partial sums of v written with
+// agent-coherent stores), arrives at the phase barrier, then runs its expand
+// items; before its first read of v it waits until every work-group of the
+// grid has arrived.  The waves of a work-group arrive through an LDS counter,
+// the last one through a per-XCD counter, the last work-group of an XCD
+// through the count of finished XCDs (the waited-on counter), and the very
+// last arrival flips the epoch.  Items, their order and their arithmetic are
+// those of shrink_kernel followed by expand_kernel, so Y is bit-identical.
+// The grid is sized from this kernel's occupancy so that it is resident at
+// once; a wave that still finds the barrier closed after the bound gives up
+// (LORA_FLAG_SYNC).
+template <class E, bool WS, bool WE>
+__global__ __launch_bounds__(kThreads, E::kExpandBlocks) void apply_kernel(KArgs) {
+  const KArgs& K = kernel_args();
+  __shared__ __attribute__((aligned(16))) float vs_all[kWaves + 1][kExpandRowFloats];
+  __shared__ int arrived;
+  const PlanCounts pc = read_counts(K);
+  if (!pc.ok) return;
+  // with no adapter rows (only copies of Y_base) there is nothing to wait for
+  const bool sync = pc.S > 0;
+  const int epoch = sync ? uniform(__hip_atomic_load(K.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) : 0;
+  int* bank = K.sync + sync_bank(epoch & 1);
+  if (sync) {  // the other bank, for the next launch: two words of each of its lines
+    int* other = K.sync + sync_bank((epoch & 1) ^ 1);
+    for (int l = blockIdx.x * kThreads + threadIdx.x; l < 2 * kSyncBankLines; l += gridDim.x * kThreads)
+      __hip_atomic_store(other + (l >> 1) * kSyncLine + (l & 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (threadIdx.x == 0) arrived = 0;
+  __syncthreads();
+  shrink_phase<E, WS, true>(K, pc);
+  // Arrival.  The partial sums were written through to the coherence point
+  // (agent-scope stores); waiting for every outstanding access of the wave
+  // makes them complete before the wave is counted.
+  __builtin_amdgcn_s_waitcnt(0);
+  const int nx = xcd_count(gridDim.x);
+  if (sync && (threadIdx.x & 63) == 0 && atomicAdd(&arrived, 1) == kWaves - 1) {
+    if (__hip_atomic_fetch_add(bank + (blockIdx.x % nx) * kSyncLine, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            (int)gridDim.x / nx - 1 &&
+        __hip_atomic_fetch_add(bank + 8 * kSyncLine, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nx - 1)
+      __hip_atomic_store(K.sync, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  PhaseWait sw{bank + 8 * kSyncLine, nx + K.wait_bias, K.wait_ticks, !sync};
+  expand_phase<E, WE, true>(K, pc, vs_all, sw);
 }
 
 // ================================================================ segments
@@ -1646,6 +1710,8 @@ __global__ __launch_bounds__(kSegScanThreads) void seg_scan_kernel(int T, int N,
     out.counts[kCountT] = T;
     out.counts[kCountCheck] = segments_check_word(T);
   }
+  // the apply kernel's phase-barrier counters start from zero for this batch
+  for (int i = threadIdx.x; i < kSyncInts; i += kSegScanThreads) out.sync[i] = 0;
 }
 
 // Stable scatter: each block sorts its chunk's (adapter, position) keys in
@@ -1743,15 +1809,39 @@ hipError_t launch_expand(const KArgs& K, int dtype, int grid, hipStream_t stream
   return launch_err();
 }
 
-hipError_t occupancy(int dtype, int* shrink_blocks, int* expand_blocks) {
+hipError_t launch_apply(const KArgs& K, int dtype, int grid, hipStream_t stream) {
+  const bool bf16 = dtype == LORA_DTYPE_BF16;
+  const bool ws = (1 << K.pw_log2) >= kKSlice, we = (1 << K.pw_log2) >= expand_cols(bf16);
+  if (bf16) {  // both page-width thresholds are 512 columns
+    if (ws) apply_kernel<Bf16, true, true><<<grid, kThreads, 0, stream>>>(K);
+    else apply_kernel<Bf16, false, false><<<grid, kThreads, 0, stream>>>(K);
+  } else {
+    if (ws) apply_kernel<F32, true, true><<<grid, kThreads, 0, stream>>>(K);
+    else if (we) apply_kernel<F32, false, true><<<grid, kThreads, 0, stream>>>(K);
+    else apply_kernel<F32, false, false><<<grid, kThreads, 0, stream>>>(K);
+  }
+  return launch_err();
+}
+
+// Work-groups per CU of each kernel.  The apply kernel's grid must be
+// resident at once, so its count is the minimum over its instantiations.
+hipError_t occupancy(int dtype, int* shrink_blocks, int* expand_blocks, int* apply_blocks) {
   hipError_t e;
+  int a0 = 0, a1 = 0, a2 = 0;
   if (dtype == LORA_DTYPE_BF16) {
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(shrink_blocks, shrink_kernel<Bf16, true>, kThreads, 0);
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(expand_blocks, expand_kernel<Bf16, true>, kThreads, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a0, apply_kernel<Bf16, true, true>, kThreads, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a1, apply_kernel<Bf16, false, false>, kThreads, 0);
+    a2 = a1;
   } else {
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(shrink_blocks, shrink_kernel<F32, true>, kThreads, 0);
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(expand_blocks, expand_kernel<F32, true>, kThreads, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a0, apply_kernel<F32, true, true>, kThreads, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a1, apply_kernel<F32, false, true>, kThreads, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a2, apply_kernel<F32, false, false>, kThreads, 0);
   }
+  *apply_blocks = min(a0, min(a1, a2));
   return e;
 }
 

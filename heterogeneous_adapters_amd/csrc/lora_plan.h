@@ -96,8 +96,23 @@ LORA_HD inline int segments_check_word(int T) { return (int)(0x4C6F5261u ^ (unsi
 // short decode items reaches the descriptor in one load, not two.
 // Offsets in int32 units, each a multiple of 64.
 constexpr int kValuItemInts = 8;
+// The phase barrier of the single-launch apply kernel, in the plan (int32
+// units, one 128-byte line per counter, so that atomics on different
+// counters do not share a line):
+//   line 0               epoch E: the launch in progress uses bank E & 1
+//   bank b, lines 0..7   work-groups of XCD x that have written their shrink
+//                        partial sums
+//   bank b, line 8       XCDs all of whose work-groups have
+// A launch zeroes the other bank at its start and flips E when its last
+// work-group arrives, so every launch finds its bank zeroed without any
+// reset between launches; the segment builder zeroes the whole area.
+constexpr int kSyncLine = 32;
+constexpr int kSyncBankLines = 9;
+constexpr int kSyncInts = kSyncLine * (1 + 2 * kSyncBankLines);
+LORA_HD inline int sync_bank(int b) { return kSyncLine * (1 + kSyncBankLines * b); }
+
 struct PlanLayout {
-  long long seg_desc, shrink_mfma, shrink_valu, expand_mfma, expand_valu, total;
+  long long seg_desc, shrink_mfma, shrink_valu, expand_mfma, expand_valu, sync, total;
   // capacities: segments, and items of each table
   long long s_cap, cap_shrink_mfma, cap_shrink_valu, cap_expand_mfma, cap_expand_valu;
 };
@@ -119,8 +134,138 @@ LORA_HD inline PlanLayout plan_layout(int T, int N) {
   L.shrink_valu = L.shrink_mfma + align64(L.cap_shrink_mfma);
   L.expand_mfma = L.shrink_valu + align64(kValuItemInts * L.cap_shrink_valu);
   L.expand_valu = L.expand_mfma + align64(L.cap_expand_mfma);
-  L.total = L.expand_valu + align64(kValuItemInts * L.cap_expand_valu);
+  L.sync = L.expand_valu + align64(kValuItemInts * L.cap_expand_valu);
+  L.total = L.sync + kSyncInts;
   return L;
+}
+
+// ------------------------------------------------------------ work walks
+// The compute kernels are persistent grids (grid work-groups of kWaves
+// waves) whose waves walk the item lists below.  The walks depend only on
+// the grid size, the work-group index and the item totals, and are written
+// for host and device alike, so that a host test can enumerate every wave's
+// items and check that each item is taken exactly once.
+//
+// XCD-aware wave walk: the item range [0, total) is cut into 8 contiguous
+// parts, part x served by the waves of the work-groups with index % 8 == x
+// (work-groups are dealt to the 8 XCDs round robin), so items that share an
+// adapter slice are read through the same L2.  Every wave walks its own
+// items: no work-group barrier couples the waves.
+LORA_HD inline int xcd_count(int grid) { return (grid % 8 == 0) ? 8 : 1; }
+
+struct WaveWalk {
+  int i, end, stride, lo;
+  // `walkers` items are taken per work-group at a time (kWaves: one per wave;
+  // 1: whole-block items), `w` is this walker's index in the work-group.
+  LORA_HD WaveWalk(int total, int w, int walkers, int grid, int block) {
+    const int nx = xcd_count(grid);
+    const int x = block % nx;
+    lo = (int)(((long long)total * x) / nx);
+    end = (int)(((long long)total * (x + 1)) / nx);
+    i = lo + (block / nx) * walkers + w;
+    stride = (grid / nx) * walkers;
+  }
+};
+
+// The MBGMV walk when the first Wm waves of each XCD run the MBGMM items:
+// the other waves take R rounds of the XCD's MBGMV items among themselves (R:
+// the MBGMV items that take as long as one wave's MBGMM items), then every
+// wave takes items in turn.
+struct TwoClassWalk {
+  int i, end, nV, W, ib, ka;  // ka: first-phase items left after the current one (-1: second phase)
+  int lo;                     // start of this XCD's part of the range
+  LORA_HD TwoClassWalk(int total, int Wm, int R, int wv, int grid, int block) {
+    const int nx = xcd_count(grid);
+    const int x = block % nx, G = grid / nx;
+    const int w = (block / nx) * kWaves + wv;  // walker index inside the XCD
+    lo = (int)(((long long)total * x) / nx);
+    end = (int)(((long long)total * (x + 1)) / nx);
+    W = G * kWaves;
+    Wm = Wm < W ? Wm : W;
+    nV = W - Wm;
+    ib = lo + R * nV + w;
+    if (w >= Wm && R > 0) {
+      i = lo + (w - Wm);
+      ka = R - 1;
+    } else {
+      i = ib;
+      ka = -1;
+    }
+  }
+  LORA_HD int next() {
+    if (ka > 0) {
+      --ka;
+      return i + nV;
+    }
+    if (ka == 0) {
+      ka = -1;
+      return ib;
+    }
+    return i + W;
+  }
+};
+
+// MBGMV rounds one MBGMM shrink item is worth (measured: 2 and 4 were slower)
+constexpr int kShrinkMfmaRounds = 3;
+
+// Shrink: the MBGMM items go to the first waves of each XCD's walk.  When
+// they are a small share of the items (under one in eight: a decode batch's
+// hot adapters, whose segments are short enough for 32-token items), those
+// waves skip the first rounds of MBGMV items: a 32-token MBGMM item is four
+// rounds of loads against one for an MBGMV item.  Returns (Wm, R) of the
+// MBGMV walk.
+LORA_HD inline void shrink_walk_split(int total_m, int total_v, int wave, int grid, int block, int& Wm, int& R) {
+  Wm = 0;
+  R = 0;
+  if (total_m > 0 && 8 * (long long)total_m < total_v) {
+    WaveWalk im(total_m, wave, kWaves, grid, block);
+    const int m = im.end - im.lo;
+    Wm = m < im.stride ? m : im.stride;
+    R = kShrinkMfmaRounds * ceil_div_i(m, im.stride);
+  }
+}
+
+// Expand: the MBGMM items are whole-block items.  When they are a small share
+// of the launch's items (a decode batch with a few hot adapters: under one in
+// eight), they go to the first third of each XCD's work-groups (one per CU),
+// so the other waves start streaming MBGMV weights at once and the MBGMM
+// items' round trips overlap them; otherwise (prefill, mixed batches) to
+// every work-group.  This work-group takes MBGMM items first, lo_m + beta,
+// lo_m + beta + Gm, ... below end_m (when beta < Gm); Gm and R parameterise
+// the MBGMV walk (the other work-groups take R first rounds alone).
+struct ExpandSplit {
+  int Gm, R, first, lo_m, end_m, step;
+};
+LORA_HD inline ExpandSplit expand_walk_split(int total_m, int total_v, int grid, int block) {
+  ExpandSplit e{0, 0, 0, 0, 0, 1};
+  if (total_m <= 0) return e;
+  const int nx = xcd_count(grid);
+  const int x = block % nx, beta = block / nx, G = grid / nx;
+  const int lo_m = (int)(((long long)total_m * x) / nx);
+  e.lo_m = lo_m;
+  e.end_m = (int)(((long long)total_m * (x + 1)) / nx);
+  const int m = e.end_m - lo_m;
+  const int third = G / 3 > 1 ? G / 3 : 1;
+  e.Gm = m <= 0 ? 0 : 8 * (long long)total_m >= total_v ? G : (third < m ? third : m);
+  e.R = e.Gm > 0 ? ceil_div_i(6 * m, 10 * e.Gm) : 0;  // an MBGMM item took ~0.6 MBGMV item times
+  e.first = beta < e.Gm ? lo_m + beta : e.end_m;
+  e.step = e.Gm > 0 ? e.Gm : 1;
+  return e;
+}
+
+// Columns per wave of an MBGMM expand item (128..512, at most the page
+// width), halved until the items cover the grid once, so a few hot segments
+// still spread over every compute unit; wide items stage a token tile's v
+// once for more columns.  d_out(p) gives projection p's output width.
+template <class DOut>
+LORA_HD inline int expand_mfma_cols(int np, DOut d_out, int pw_log2, int Um, int grid, int& total) {
+  int wc = (1 << pw_log2) < 512 ? (1 << pw_log2) : 512;
+  for (;; wc >>= 1) {
+    total = 0;
+    for (int p = 0; p < np; ++p) total += ceil_div_i(d_out(p), kWaves * wc) * Um;
+    if (wc <= 128 || total >= grid) break;
+  }
+  return wc;
 }
 
 }  // namespace lora

@@ -24,7 +24,7 @@ LORA_MAX_TOKENS = (1 << 24) - 1
 LORA_MAX_LAUNCH_ITEMS = 1 << 30
 LORA_KSLICE = 512
 COUNT_S, COUNT_INVALID, COUNT_T_VALID, COUNT_V_TOTAL, COUNT_FLAGS, COUNT_T = 0, 1, 2, 3, 8, 9
-FLAG_PAGE_RANGE, FLAG_SEGMENTS = 1, 2
+FLAG_PAGE_RANGE, FLAG_SEGMENTS, FLAG_SYNC = 1, 2, 4
 N_COUNTS = 16
 
 _vp = ctypes.c_void_p
@@ -56,7 +56,7 @@ EXPORTS = ("lora_status_string", "lora_v_slices", "lora_segments_size", "lora_se
            "lora_workspace_size", "lora_build_segments", "lora_shrink", "lora_expand", "lora_apply",
            "lora_validate_tables", "lora_cache_create", "lora_cache_destroy", "lora_cache_free_pages",
            "lora_cache_num_resident", "lora_cache_admit", "lora_cache_set_pinned", "lora_cache_release",
-           "lora_cache_lookup", "lora_upload_pages", "lora_apply_noalloc")
+           "lora_cache_lookup", "lora_upload_pages", "lora_apply_noalloc", "lora_set_wait_limit")
 LORA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -94,6 +94,8 @@ def lib():
         L.lora_apply_noalloc.argtypes = [_vp, P(lora_segments_t), _i32, P(lora_proj_t), _i32,
                                          P(lora_adapters_t), P(lora_pool_t), _vp]
         L.lora_validate_tables.argtypes = [_i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
+        L.lora_set_wait_limit.argtypes = [_i64]
+        L.lora_set_wait_limit.restype = None
         L.lora_cache_create.argtypes = [_i32, P(_vp)]
         L.lora_cache_destroy.argtypes = [_vp]
         L.lora_cache_destroy.restype = None
@@ -284,6 +286,11 @@ def lora_apply_noalloc(ids: Optional[torch.Tensor], segs: Optional[Segments], T:
     _check("lora_apply_noalloc", lib().lora_apply_noalloc(
         _ptr(ids), ctypes.byref(segs.c) if segs is not None else None, T, arr, len(projs),
         ctypes.byref(adapters.c), ctypes.byref(pool.c), _stream(stream)))
+
+
+def lora_set_wait_limit(ns: int) -> None:
+    """Bound on lora_apply's internal phase wait (0: default; < 0: give up after |ns|, for tests)."""
+    lib().lora_set_wait_limit(int(ns))
 
 
 def lora_validate_tables(rank, d_in: int, d_out: int, page_width: int, num_pages: int,

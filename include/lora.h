@@ -180,6 +180,11 @@ typedef struct {
  * counters exceed the capacity it was laid out for.  The launch wrote
  * nothing. */
 #define LORA_FLAG_SEGMENTS 2
+/* The single-launch kernel of lora_apply gave up waiting for its shrink
+ * phase (its grid could not run all at once: another kernel held compute
+ * units for longer than the wait's bound, lora_set_wait_limit).  Y of that
+ * call is invalid; the segment buffer stays usable for later calls. */
+#define LORA_FLAG_SYNC 4
 
 /* Bytes of the device buffer that holds segments for T tokens and
  * num_adapters adapters. */
@@ -240,8 +245,13 @@ lora_status_t lora_expand(const lora_proj_t* projs, int32_t n_projs, const lora_
  * the gather / shrink / expand sequence of [MLSP] "Segmented Gather
  * Matrix-Vector Multiplication (SGMV)" over segments of tokens that share an
  * adapter, with weights read through the page tables ([MLSP] "Unified Paging
- * Architecture").  Two kernel launches (shrink, expand) per group of up to
- * 16 projections.
+ * Architecture").  One kernel launch per group of up to 16 projections (the
+ * fused operations of [MLSP] "Custom CUDA Kernels: SGMV and MBGMV"): its
+ * waves write the shrink partial sums, then wait once for the whole grid's
+ * and run the expand, the same arithmetic as lora_shrink + lora_expand (Y
+ * bit-identical).  The wait's bookkeeping lives in the segment buffer, so
+ * calls that share one segment buffer must not run concurrently (issue them
+ * on one stream).
  *   ids != NULL, segs != NULL : build segments into *segs, then apply
  *   ids != NULL, segs == NULL : build segments inside the workspace
  *   ids == NULL, segs != NULL : reuse prebuilt segments (built by
@@ -281,6 +291,15 @@ lora_status_t lora_apply_noalloc(const int32_t* ids, const lora_segments_t* segs
                                  const lora_proj_t* projs, int32_t n_projs,
                                  const lora_adapters_t* adapters, const lora_pool_t* pool,
                                  void* stream);
+
+/* Bound on the internal wait of lora_apply's single-launch kernel: its
+ * expand phase waits until every work-group of the grid has written its
+ * shrink partial sums, which needs the whole grid resident at once (the grid
+ * is sized from the kernel's occupancy).  Process-wide; for diagnostics and
+ * tests.  ns > 0 sets the bound, 0 restores the default (50 ms), ns < 0
+ * makes every such wait give up after |ns| ns (exercises the give-up path:
+ * LORA_FLAG_SYNC, no hang). */
+void lora_set_wait_limit(int64_t ns);
 
 /* Host-side check of page tables (all arguments host copies): every adapter
  * owns exactly ceil(r/16)*ceil(d/PW) slots and every page id lies in

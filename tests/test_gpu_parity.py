@@ -662,3 +662,48 @@ def test_segment_buffer_larger_than_the_batch():
     assert int(fresh.counts()[lora.COUNT_FLAGS]) & lora.FLAG_SEGMENTS
     for p in range(w.n_projs):
         assert bool((b.Y[p].float() == 7.0).all()), p
+
+
+def test_single_launch_wait_give_up_is_flagged_and_recovers():
+    """The apply kernel's bounded wait between its shrink and expand phases,
+    forced to give up from the host (its target made unreachable): the launch
+    still ends, LORA_FLAG_SYNC is raised, and the next call on the same
+    segment buffer -- whose barrier bookkeeping the forced call advanced as
+    usual -- is bit-identical to the two-launch path."""
+    w = W.make_workload(2, dict(T=200, N=9, ranks_override=[8, 16, 64, 24, 1, 32, 128, 40, 8], page_width=512,
+                                projs=(("a", 1024, 1536), ("b", 1536, 1024))), keep_dense=False)
+    Ysplit, _ = gpu_apply(w, via="split_group")
+    b = batch.to_device(w)
+    projs = [b.proj(p) for p in range(w.n_projs)]
+    segs = lora.Segments(w.T, w.N)
+    ws = lora.workspace(w.T, w.N, w.n_projs, 1536)
+    lora.lora_build_segments(b.ids, b.adapters, segs, ws)
+    try:
+        lora.lora_set_wait_limit(-200_000)  # every wait gives up after 0.2 ms
+        lora.lora_apply(None, segs, w.T, projs, b.adapters, b.pool, ws)
+        torch.cuda.synchronize()
+    finally:
+        lora.lora_set_wait_limit(0)
+    assert int(segs.counts()[lora.COUNT_FLAGS]) & lora.FLAG_SYNC
+    for rep in range(3):
+        for y in b.Y:
+            y.fill_(7.0)
+        lora.lora_apply(None, segs, w.T, projs, b.adapters, b.pool, ws)
+        torch.cuda.synchronize()
+        for p in range(w.n_projs):
+            assert np.array_equal(batch.device_to_host(b.Y[p]), Ysplit[p]), (rep, p)
+    lora.lora_build_segments(b.ids, b.adapters, segs, ws)
+    lora.lora_apply(None, segs, w.T, projs, b.adapters, b.pool, ws)
+    torch.cuda.synchronize()
+    assert segs.arrays()["flags"] == 0
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_single_launch_matches_two_launches(k):
+    """lora_apply (one launch per group) against lora_shrink + lora_expand (two
+    launches, the same items): bit-identical Y on the benchmark configs."""
+    w = W.make_workload(k, keep_dense=False)
+    Ya, _ = gpu_apply(w)
+    Ys, _ = gpu_apply(w, via="split_group")
+    for p in range(w.n_projs):
+        assert np.array_equal(Ya[p], Ys[p]), p
