@@ -15,12 +15,15 @@ method must move: activations once, each distinct adapter's unpadded A and B
 once) with every input already resident in HBM, for the step captured once in
 a HIP graph and replayed (its replays are checked bit for bit against the
 eager step first); the eager step is reported under ``eager``.  ``roofline`` covers the
-dominant kernel (the expand kernel, its wide-page instantiation; both kernels are reported under
-``kernels``): after the timed steps the same groups are run through
-lora_shrink / lora_expand -- the two launches of lora_apply, same grid --
-with HIP events around each launch on the stream the library launches on.
-``traffic`` is the HBM bytes per launch from the committed rocprofv3 counter
-summary, or null when the kernel sources changed since it was taken.
+dominant kernel: at 1024 tokens lora_apply runs each projection group as one
+launch of the apply kernel, timed by HIP events around every call of the
+eager step (on the stream the library launches on); ``roofline.rocprof``
+gives the same kernel's mean duration from the committed rocprofv3 summary.
+After the timed steps the same groups also run through lora_shrink /
+lora_expand (the two-launch path, same items, Y checked bit-identical), whose
+kernels are reported under ``kernels``.  ``traffic`` is the HBM bytes per
+launch from the committed rocprofv3 counter summary, or null when the kernel
+sources changed since it was taken.
 ``cpu_baseline`` is the CPU oracle on a bounded sample of the same step.
 
 ``--summarize-profile DIR`` (no GPU) turns rocprofv3 CSV output (kernel
@@ -44,7 +47,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 KERNEL_SOURCES = ("heterogeneous_adapters_amd/csrc/lora_kernels.hip", "heterogeneous_adapters_amd/csrc/lora_kernels.h",
                   "heterogeneous_adapters_amd/csrc/lora_plan.h", "include/lora.h")
-TRAFFIC_SUMMARY = "profiles/expand_kernel_bf16.llama7b_decode_T1024.hbm_traffic.txt"
+TRAFFIC_SUMMARY = "profiles/lora_kernels.llama7b_decode_T1024.hbm_traffic.txt"
+STATS_SUMMARY = "profiles/lora_kernels.llama7b_decode_T1024.kernel_stats.txt"
+# rocprof kernel names of the decode step's kernels (bf16, wide pages)
+APPLY_KERNEL = "apply_kernel<lora::Bf16, true, true>"
+SHRINK_KERNEL = "shrink_kernel<lora::Bf16, true>"
+EXPAND_KERNEL = "expand_kernel<lora::Bf16, true>"
 CALIB_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
 
 
@@ -63,24 +71,54 @@ def kernel_source_hash(root: str = ROOT) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_hash: str):
-    """HBM bytes per launch of the expand kernel from the committed counter
-    summary; None when absent or taken on other kernel sources."""
-    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+def _read_summary(rel: str, kernel_hash: str):
+    """Key/value lines and table rows of a committed profile summary; None
+    when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
         return None
-    kv = {}
+    kv, rows = {}, []
     with open(path) as f:
         for line in f:
-            if ":" in line and not line.startswith(" "):
+            if line.startswith("  "):
+                rows.append(line.split())
+            elif ":" in line:
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
     if kv.get("kernel_source_hash") != kernel_hash:
         return None
-    try:
-        return int(float(kv["hbm_bytes_per_launch"]))
-    except (KeyError, ValueError):
+    return kv, rows
+
+
+def load_traffic(kernel_hash: str):
+    """HBM bytes per launch of the decode step's kernels (apply, shrink,
+    expand) from the committed counter summary, or None."""
+    got = _read_summary(TRAFFIC_SUMMARY, kernel_hash)
+    if got is None:
         return None
+    out = {}
+    for key in ("apply", "shrink", "expand"):
+        try:
+            out[key] = int(float(got[0][f"{key}_hbm_bytes_per_launch"]))
+        except (KeyError, ValueError):
+            pass
+    return out or None
+
+
+def load_stats(kernel_hash: str):
+    """Mean duration (us) per launch of each lora kernel from the committed
+    rocprofv3 kernel-stats summary, or None."""
+    got = _read_summary(STATS_SUMMARY, kernel_hash)
+    if got is None:
+        return None
+    out = {}
+    for r in got[1]:
+        if len(r) >= 7 and r[0].isdigit():
+            name = " ".join(r[6:])
+            for k in (APPLY_KERNEL, SHRINK_KERNEL, EXPAND_KERNEL):
+                if k in name:
+                    out[k] = float(r[1])
+    return out or None
 
 
 def parse():
@@ -100,7 +138,7 @@ def parse():
     ap.add_argument("--no-stream-ref", action="store_true",
                     help="skip the streaming reference (a plain device copy and read of 1 GiB)")
     ap.add_argument("--no-configs", action="store_true", help="skip the configs 1-2 leg (config 3 still runs)")
-    ap.add_argument("--only", choices=["prefill", "configs"],
+    ap.add_argument("--only", choices=["prefill", "configs", "config1", "config2"],
                     help="run only this leg and print its JSON (for profiling one workload)")
     ap.add_argument("--rotate-bytes", type=float, default=1.0,
                     help="GB of input/pool copies the configs leg rotates over (more than the 256 MB MALL)")
@@ -195,7 +233,7 @@ def summarize_profile(dirs, command):
             if "lora::" in name and ctr in ("MfmaUtil", "MfmaFlopsBF16"):
                 key = "mfma_util_pct" if ctr == "MfmaUtil" else "mfma_bf16_flops_per_dispatch"
                 lines.append(f"{key} {float(np.mean(list(disp.values()))):.4g}  {name[:90]}")
-        for kname, key in (("shrink_kernel<lora::Bf16, true>", "shrink"), ("expand_kernel<lora::Bf16, true>", "expand")):
+        for kname, key in ((APPLY_KERNEL, "apply"), (SHRINK_KERNEL, "shrink"), (EXPAND_KERNEL, "expand")):
             tot, have = 0.0, 0
             for (name, ctr), disp in per.items():
                 if kname in name and ctr in calib:
@@ -205,8 +243,6 @@ def summarize_profile(dirs, command):
                     have += 1
             if have == 2:
                 lines.append(f"{key}_hbm_bytes_per_launch: {tot:.0f}")
-                if key == "expand":
-                    lines.append(f"hbm_bytes_per_launch: {tot:.0f}")
     print("\n".join(lines))
 
 
@@ -268,6 +304,26 @@ def configs_leg(which, steps, rotate_gb):
             ev[i][1].record()
         torch.cuda.synchronize()
         ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        # the two kernels of the two-launch path on the same rotation, each
+        # timed on its own (lora_shrink, then lora_expand of that call's v)
+        stride = max(w.T, 1) * lora.LORA_MAX_RANK
+        vbuf = [torch.empty(lora.lora_v_slices(t.d_in) * stride, dtype=torch.float32, device=b0.pool.base.device)
+                for t in w.tables]
+        ks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+        for i in range(n_calls):
+            c = copies[i % K]
+            ks[i][0].record()
+            lora.lora_shrink(projs[i % K], c.adapters, segs, c.pool, vbuf, stride)
+            ks[i][1].record()
+            lora.lora_expand(projs[i % K], c.adapters, segs, c.pool, vbuf, 0, stride)
+            ks[i][2].record()
+        torch.cuda.synchronize()
+        shr_us = float(np.median([a.elapsed_time(b) for a, b, _ in ks])) * 1e3
+        exp_us = float(np.median([b.elapsed_time(c) for _, b, c in ks])) * 1e3
+        split = [traffic.group_split_bytes(w.ids, w.ranks, [(t.d_in, t.d_out, i)], 2) for i, t in enumerate(w.tables)]
+        sb, eb = sum(x[0] for x in split), sum(x[1] for x in split)
+        del vbuf
         by = sum(traffic.algorithmic_bytes(w.ids, w.ranks, t.d_in, t.d_out, 2) for t in w.tables)
         fl = sum(traffic.algorithmic_flops(w.ids, w.ranks, t.d_in, t.d_out) for t in w.tables)
         tf = fl / (ms * 1e-3) / 1e12
@@ -278,7 +334,11 @@ def configs_leg(which, steps, rotate_gb):
                        "frac_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                        "tflops": round(tf, 2), "frac_bf16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                        "intensity_flop_per_byte": round(fl / by, 2),
-                       "segment_build_us_median": round(float(np.median(seg_ms)) * 1e3, 1)}
+                       "segment_build_us_median": round(float(np.median(seg_ms)) * 1e3, 1),
+                       "two_launch_kernels": {
+                           "shrink_us_median": round(shr_us, 2), "shrink_gbs": round(sb / shr_us / 1e3, 1),
+                           "expand_us_median": round(exp_us, 2), "expand_gbs": round(eb / exp_us / 1e3, 1),
+                           "timing": "hip events around each lora_shrink and lora_expand call, same rotation"}}
         del copies, projs, b0, w
         torch.cuda.empty_cache()
     return out
@@ -339,8 +399,10 @@ def main():
 
     torch.cuda.set_device(0)
     if args.only:
-        which = [3] if args.only == "prefill" else [1, 2, 3]
+        which = {"prefill": [3], "configs": [1, 2, 3], "config1": [1], "config2": [2]}[args.only]
         print(json.dumps({"configs": configs_leg(which, args.prefill_steps, args.rotate_bytes)}), flush=True)
+        if args.calibration_copy:
+            calibration_copy()
         return
     dev = "cuda"
     log("generating the decode-step workload on the device")
@@ -525,32 +587,64 @@ def main():
     head_ms = graph["ms_per_step"] if graph else ms_step
     gbs = step_bytes / (head_ms * 1e-3) / 1e9
     mean_call_ms = call_ms.mean(axis=0)
+    hsh = kernel_source_hash()
+    stats = load_stats(hsh) or {}
+    hbm = load_traffic(hsh) or {}
+
+    def rocprof_part(kname, bytes_per_launch):
+        us = stats.get(kname)
+        if us is None:
+            return None
+        gb = bytes_per_launch / (us * 1e-6) / 1e9
+        return {"source": STATS_SUMMARY, "mean_launch_us": us, "achieved": round(gb, 1),
+                "frac": round(gb / HBM_PEAK_GBS, 4)}
+
     kernels = {}
-    for kname, ms_g, part in (("shrink_kernel<Bf16>", shr_ms, 0), ("expand_kernel<Bf16, true>", exp_ms, 1)):
+    # The step's kernel: at T = 1024 lora_apply runs each group as one launch
+    # of the apply kernel (lora_set_launch_mode, automatic choice); HIP events
+    # around every call of the eager step time it (they include the gap
+    # between launches), the committed rocprofv3 summary gives its duration
+    apply_b = float(np.mean(call_bytes))
+    gb_apply = float(np.sum(call_bytes) / (mean_call_ms.sum() * 1e-3) / 1e9)
+    kernels[APPLY_KERNEL] = {"launches_per_step": len(groups), "mean_launch_us": round(float(mean_call_ms.mean()) * 1e3, 2),
+                             "timing": "hip events around each lora_apply call, eager step",
+                             "algorithmic_bytes_per_launch": int(apply_b), "gbs": round(gb_apply, 1),
+                             "frac_hbm_peak": round(gb_apply / HBM_PEAK_GBS, 4),
+                             "rocprof": rocprof_part(APPLY_KERNEL, apply_b), "hbm_bytes_per_launch": hbm.get("apply")}
+    # the two-launch path's kernels (lora_shrink / lora_expand on the same
+    # groups, the same items; Y checked bit-identical)
+    for kname, ms_g, part, tkey in ((SHRINK_KERNEL, shr_ms, 0, "shrink"), (EXPAND_KERNEL, exp_ms, 1, "expand")):
         kb = [sp[part] for sp in call_split]
         gb = float(np.sum(kb) / (ms_g.sum() * 1e-3) / 1e9)
         kernels[kname] = {"launches_per_step": len(groups), "mean_launch_us": round(float(ms_g.mean()) * 1e3, 2),
+                          "timing": "hip events around each lora_shrink / lora_expand launch",
                           "algorithmic_bytes_per_launch": int(np.mean(kb)), "gbs": round(gb, 1),
-                          "frac_hbm_peak": round(gb / HBM_PEAK_GBS, 4)}
-    # the same two kernels by projection group (q/k/v, o, gate/up, down), as
-    # mean launch time and GB/s over the layers
+                          "frac_hbm_peak": round(gb / HBM_PEAK_GBS, 4),
+                          "rocprof": rocprof_part(kname, float(np.mean(kb))), "hbm_bytes_per_launch": hbm.get(tkey)}
+    # the two kernels by projection group (q/k/v, o, gate/up, down), as
+    # mean launch time and GB/s over the layers, and the single launch
     by_group = {}
     for gi, g in enumerate(groups):
         key = "+".join(names[i % len(names)].replace("_proj", "") for i in g)
-        d = by_group.setdefault(key, {"shrink_us": [], "expand_us": [], "shrink_b": [], "expand_b": []})
+        d = by_group.setdefault(key, {"shrink_us": [], "expand_us": [], "shrink_b": [], "expand_b": [],
+                                      "apply_us": [], "apply_b": []})
         d["shrink_us"].append(shr_ms[gi] * 1e3)
         d["expand_us"].append(exp_ms[gi] * 1e3)
+        d["apply_us"].append(mean_call_ms[gi] * 1e3)
         d["shrink_b"].append(call_split[gi][0])
         d["expand_b"].append(call_split[gi][1])
+        d["apply_b"].append(call_bytes[gi])
     for key, d in by_group.items():
-        su, eu = float(np.mean(d["shrink_us"])), float(np.mean(d["expand_us"]))
-        by_group[key] = {"shrink_us": round(su, 2), "shrink_gbs": round(float(np.mean(d["shrink_b"])) / su / 1e3, 1),
+        su, eu, au = (float(np.mean(d[k])) for k in ("shrink_us", "expand_us", "apply_us"))
+        by_group[key] = {"apply_us": round(au, 2), "apply_gbs": round(float(np.mean(d["apply_b"])) / au / 1e3, 1),
+                         "shrink_us": round(su, 2), "shrink_gbs": round(float(np.mean(d["shrink_b"])) / su / 1e3, 1),
                          "expand_us": round(eu, 2), "expand_gbs": round(float(np.mean(d["expand_b"])) / eu / 1e3, 1)}
     kernels["by_group"] = by_group
-    dom = kernels["expand_kernel<Bf16, true>"]
+    dom = kernels[APPLY_KERNEL]
     roofline = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": dom["frac_hbm_peak"], "traffic": load_traffic(kernel_source_hash()),
-                "kernel": "expand_kernel<Bf16, true>", "mean_launch_us": dom["mean_launch_us"],
+                "frac": dom["frac_hbm_peak"], "traffic": hbm.get("apply"),
+                "kernel": APPLY_KERNEL, "timing": dom["timing"], "mean_launch_us": dom["mean_launch_us"],
+                "rocprof": dom["rocprof"], "traffic_source": TRAFFIC_SUMMARY if hbm.get("apply") else None,
                 "algorithmic_bytes_per_launch": dom["algorithmic_bytes_per_launch"],
                 "launches_per_step": len(groups)}
 
@@ -880,11 +974,18 @@ def main():
         out["stream_reference"] = ref
     print(json.dumps(out), flush=True)
     if args.calibration_copy:
-        a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            torch.neg(a, out=b)
-        torch.cuda.synchronize()
+        calibration_copy()
+
+
+def calibration_copy():
+    """A plain elementwise copy of CALIB_BYTES (read and written), whose
+    FETCH_SIZE / WRITE_SIZE readings calibrate the counters' units."""
+    import torch
+    a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -398,37 +398,36 @@ __device__ __forceinline__ ShrinkItem fetch_shrink_item(const KArgs& K, int i, i
   return it;
 }
 
-// MBGMV item (one wave): (segment, rank group g, <= 2 tokens, 512-column
-// slice q).  Each lane streams one 16-byte vector (8 bf16 / 4 fp32 columns)
-// of each of the group's 16 page rows -- a wave reads 1 KiB contiguous per
-// row -- together with the same columns of the tokens' activation rows (the
-// gathered activations of [MLSP] SGMV), forms partial dot products, and the
-// 64 lanes are reduced across the wave.  All loads are issued before the
-// first product, so an item costs one memory round trip; the next item's
-// metadata is fetched while they are in flight.
-template <class E, bool WIDE, bool CO, class Prefetch>
-__device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, const ShrinkItem& item, int lane,
-                                            Prefetch&& prefetch) {
+// The loads of one MBGMV shrink item, held in registers until its products.
+template <class E>
+struct ShrinkLoads {
+  static constexpr int NVEC = kKSlice / (64 * E::kEpv);  // vectors per lane and row (bf16 1, fp32 2)
+  uint4 x[kValuTokens][NVEC];
+  uint4 w[16][NVEC];
+  bool ok[NVEC];  // lane inside d_in and page inside the pool
+};
+
+// Issue every load of an item.  Every load is unconditional and in bounds:
+// rows past the rank re-read the group's last row, tokens past the item its
+// last token, lanes past d_in the slice's last vector.  Their products are
+// never stored (rows, tokens) or are zeroed before the reduction (lanes), so
+// no load is ever skipped -- a skipped load's zero fill would make the
+// compiler wait for older loads into the same registers.
+template <class E, bool WIDE>
+__device__ __forceinline__ void shrink_valu_issue(const KArgs& K, const KProj& P, const ShrinkItem& item, int lane,
+                                                  ShrinkLoads<E>& L) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
-  constexpr int NVEC = kKSlice / (64 * EPV);  // vectors per lane and row (bf16 1, fp32 2)
+  constexpr int NVEC = ShrinkLoads<E>::NVEC;
   constexpr int NV = kValuTokens;
   const int q = item.q;
-  const int4 d1 = item.d1;
   const int r = item.d0.y;
-  const int g = item.g, tb = item.tb, nt = item.nt;
+  const int g = item.g;
   const int col0 = q * kKSlice;
   const int ncols = min(kKSlice, P.d_in - col0);  // a multiple of 8
   const int pw = 1 << K.pw_log2;
   const int rows = min(16, r - g * 16);
-  const int slot0 = item.slot0;
   const T* X = reinterpret_cast<const T*>(P.X);
-  // Every load is unconditional and in bounds: rows past the rank re-read
-  // the group's last row, tokens past the item its last token, lanes past
-  // d_in the slice's last vector.  Their products are never stored (rows,
-  // tokens) or are zeroed before the reduction (lanes), so no load is ever
-  // skipped -- a skipped load's zero fill would make the compiler wait for
-  // older loads into the same registers.
   int cl[NVEC];
   bool lane_ok[NVEC];
 #pragma unroll
@@ -449,26 +448,33 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, cons
     }
   } else {
 #pragma unroll
-    for (int v = 0; v < NVEC; ++v) pg[v] = page_base<E>(K, P.a_pages[slot0 + ((col0 + cl[v]) >> K.pw_log2)], pok[v]);
+    for (int v = 0; v < NVEC; ++v) pg[v] = page_base<E>(K, P.a_pages[item.slot0 + ((col0 + cl[v]) >> K.pw_log2)], pok[v]);
   }
+#pragma unroll
+  for (int v = 0; v < NVEC; ++v) L.ok[v] = lane_ok[v] && pok[v];
   // X first, then the rows in product order: vector memory returns in issue
   // order, so the products of row rr wait only for X and rows 0..rr
-  uint4 x[NV][NVEC];
 #pragma unroll
   for (int tt = 0; tt < NV; ++tt) {
     const int64_t row = (int64_t)item.xr[tt] * P.ldx + col0;
 #pragma unroll
-    for (int v = 0; v < NVEC; ++v) x[tt][v] = ldg16(X + row + cl[v]);
+    for (int v = 0; v < NVEC; ++v) L.x[tt][v] = ldg16(X + row + cl[v]);
   }
   __builtin_amdgcn_sched_barrier(0);
-  uint4 w[16][NVEC];
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr)
 #pragma unroll
-    for (int v = 0; v < NVEC; ++v) w[rr][v] = ldg16(pg[v] + min(rr, rows - 1) * pw + ((col0 + cl[v]) & (pw - 1)));
-  __builtin_amdgcn_sched_barrier(0);
-  prefetch();
-  __builtin_amdgcn_sched_barrier(0);
+    for (int v = 0; v < NVEC; ++v) L.w[rr][v] = ldg16(pg[v] + min(rr, rows - 1) * pw + ((col0 + cl[v]) & (pw - 1)));
+}
+
+// The products, the wave reduction and the stores of an item's partial sums.
+template <class E, bool CO>
+__device__ __forceinline__ void shrink_valu_finish(const KArgs& K, const KProj& P, const ShrinkItem& item, int lane,
+                                                   const ShrinkLoads<E>& L) {
+  constexpr int NVEC = ShrinkLoads<E>::NVEC;
+  constexpr int NV = kValuTokens;
+  const int r = item.d0.y;
+  const int rows = min(16, r - item.g * 16);
   static_assert(16 * NV == 32, "one 32-value wave reduction per item");
   float acc[32];
 #pragma unroll
@@ -478,61 +484,97 @@ __device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, cons
       float s = 0.0f;
 #pragma unroll
       for (int v = 0; v < NVEC; ++v) {
-        const float d = dot16(w[rr][v], x[tt][v], 0.0f, E());
-        s += (lane_ok[v] && pok[v]) ? d : 0.0f;
+        const float d = dot16(L.w[rr][v], L.x[tt][v], 0.0f, E());
+        s += L.ok[v] ? d : 0.0f;
       }
       acc[rr * NV + tt] = s;
     }
   const float sum = wave_reduce_scatter32(acc, lane);
   const int vi = lane >> 1;
   const int rr = vi / NV, tt = vi % NV;
-  if ((lane & 1) == 0 && rr < rows && tt < nt)
-    vst<CO>(P.v + (int64_t)q * K.v_stride + d1.x + (int64_t)(tb + tt) * r + g * 16 + rr, sum);
+  if ((lane & 1) == 0 && rr < rows && tt < item.nt)
+    vst<CO>(P.v + (int64_t)item.q * K.v_stride + item.d1.x + (int64_t)(item.tb + tt) * r + item.g * 16 + rr, sum);
 }
 
-// MBGMM item (one wave): (segment, 16*NTT-token tile, rank group g, slice q):
-// C[rank][token] += A^T[rank][col] * X^T[col][token] over the slice's 512
-// columns, as NTT 16x16 MFMA tiles that share each A operand (so A, re-read
-// from L2 for every tile of the segment, is read once per 16*NTT tokens),
-// with the operands of 8 / NTT K steps requested before the first of their
-// MFMAs (2*NTT memory round trips per item).  The rank groups of a token tile
-// are consecutive items, so the tile's activations are re-read from the L2
-// that holds them.
-template <class E, bool WIDE, int NTT, bool CO>
+// MBGMV item (one wave): (segment, rank group g, <= 2 tokens, 512-column
+// slice q).  Each lane streams one 16-byte vector (8 bf16 / 4 fp32 columns)
+// of each of the group's 16 page rows -- a wave reads 1 KiB contiguous per
+// row -- together with the same columns of the tokens' activation rows (the
+// gathered activations of [MLSP] SGMV), forms partial dot products, and the
+// 64 lanes are reduced across the wave.  All loads are issued before the
+// first product, so an item costs one memory round trip; the next item's
+// metadata is fetched while they are in flight.
+template <class E, bool WIDE, bool CO, class Prefetch>
+__device__ __forceinline__ void shrink_valu(const KArgs& K, const KProj& P, const ShrinkItem& item, int lane,
+                                            Prefetch&& prefetch) {
+  ShrinkLoads<E> L;
+  shrink_valu_issue<E, WIDE>(K, P, item, lane, L);
+  __builtin_amdgcn_sched_barrier(0);
+  prefetch();
+  __builtin_amdgcn_sched_barrier(0);
+  shrink_valu_finish<E, CO>(K, P, item, lane, L);
+}
+
+// MBGMM item (one wave): (segment, 16*NTT-token tile, GG rank groups from
+// g0, slice q): C[rank][token] += A^T[rank][col] * X^T[col][token] over the
+// slice's 512 columns, as GG x NTT 16x16 MFMA tiles -- each A operand shared
+// by the NTT token tiles (A, re-read from L2 for every tile of a segment, is
+// read once per 16*NTT tokens) and each X operand by the GG rank groups (the
+// tile's activations are read once per GG groups) -- with the operands of
+// SIF K steps requested before the first of their MFMAs.  The items of one
+// token tile (its group sets) are consecutive, so they re-read the tile's
+// activations from the L2 that holds them.
+template <class E, bool WIDE, int NTT, int GG, bool CO>
 __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int q, int4 d0, int4 d1, int local,
                                             int lane) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
   constexpr int STEP = 4 * EPV;
   constexpr int NSTEP = kKSlice / STEP;
-  constexpr int TILE = 16 * NTT;  // tokens per item
-  constexpr int SIF = 8 / NTT;                 // K steps in flight: 8 (A + NTT X) operand pairs
+  constexpr int TILE = 16 * NTT;                          // tokens per item
+  // K steps in flight: 8 (A + NTT X) operand pairs with one group; with
+  // groups sharing X, one step (GG A + NTT X operands) keeps the kernel
+  // within the shrink's register budget
+  constexpr int SIF = GG == 1 ? 8 / NTT : 1;
   static_assert(NSTEP % SIF == 0, "steps in flight divide the slice");
   const int a = d0.x, r = d0.y, t0 = d0.z, n = d0.w;
   const int G = rank_groups(r);
-  const int tt = local / G;
-  const int g = local - tt * G;
+  const int GQ = ceil_div_i(G, GG);  // group sets per token tile
+  const int tt = local / GQ;
+  const int g0 = (local - tt * GQ) * GG;
   const int tb = tt * TILE;
   const int nt = min(TILE, n - tb);
   const int li = lane & 15, qq = lane >> 4;
   const int col0 = q * kKSlice;
   const int ncols = min(kKSlice, P.d_in - col0);  // a multiple of 8
   const int pw = 1 << K.pw_log2;
-  const int slot = cld(P.a_indptr + a) + g * ((P.d_in + pw - 1) >> K.pw_log2);
-  bool ok1 = true;
-  const T* pg1 = WIDE ? page_base<E>(K, cld(P.a_pages + slot + (col0 >> K.pw_log2)), ok1) : nullptr;
+  const int nci = (P.d_in + pw - 1) >> K.pw_log2;
+  const int abase = cld(P.a_indptr + a);
+  // group gi of the item is g0 + gi, or (past the adapter's last group) the
+  // last group again: its loads stay in bounds and its products are skipped
+  int slot[GG];
+  bool ok1[GG];
+  const T* pg1[GG];
+#pragma unroll
+  for (int gi = 0; gi < GG; ++gi) {
+    slot[gi] = abase + min(g0 + gi, G - 1) * nci;
+    ok1[gi] = true;
+    pg1[gi] = WIDE ? page_base<E>(K, cld(P.a_pages + slot[gi] + (col0 >> K.pw_log2)), ok1[gi]) : nullptr;
+  }
   // Operands are loaded row-contiguously -- lane l reads chunk l & 3 of row
   // l >> 2, so a quarter-wave covers 4 rows x 64 contiguous bytes -- and
   // moved to the MFMA layout (lane L holds chunk L >> 4 of row L & 15) with a
   // cross-lane permute.  Loaded in the MFMA layout directly, every
   // quarter-wave would touch 16 rows (16 cache lines per 256 bytes).
-  // Loads are unconditional and in bounds (see shrink_valu): rank rows past
-  // r re-read the group's last row (their outputs are never stored), tokens
-  // past the tile its first token (never stored); K positions past d_in are
-  // zeroed at the product.
+  // Loads are unconditional and in bounds (see shrink_valu_issue): rank rows
+  // past r re-read the group's last row (their outputs are never stored),
+  // tokens past the tile its first token (never stored); K positions past
+  // d_in are zeroed at the product.
   const int lr = lane >> 2, lk = lane & 3;
   const int src = ((lane & 15) * 4 + (lane >> 4)) * 4;  // byte address of the source lane
-  const int lrow = min(lr, r - g * 16 - 1);
+  int lrow[GG];
+#pragma unroll
+  for (int gi = 0; gi < GG; ++gi) lrow[gi] = min(lr, r - min(g0 + gi, G - 1) * 16 - 1);
   const T* X = reinterpret_cast<const T*>(P.X);
   int64_t xrow[NTT];
 #pragma unroll
@@ -541,28 +583,35 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
     return make_uint4(__builtin_amdgcn_ds_bpermute(src, (int)v.x), __builtin_amdgcn_ds_bpermute(src, (int)v.y),
                       __builtin_amdgcn_ds_bpermute(src, (int)v.z), __builtin_amdgcn_ds_bpermute(src, (int)v.w));
   };
-  f4 acc[NTT];
+  f4 acc[GG][NTT];
 #pragma unroll
-  for (int s = 0; s < NTT; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int gi = 0; gi < GG; ++gi)
+#pragma unroll
+    for (int s = 0; s < NTT; ++s) acc[gi][s] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
   for (int st0 = 0; st0 < NSTEP; st0 += SIF) {
-    uint4 av[SIF], xv[SIF][NTT];
-    bool okv[SIF];
+    uint4 av[SIF][GG], xv[SIF][NTT];
+    bool okv[SIF][GG];
 #pragma unroll
     for (int j = 0; j < SIF; ++j) {
       const int cl = (st0 + j) * STEP + lk * EPV;       // this lane's load chunk
       const int col = col0 + min(cl, ncols - EPV);
-      okv[j] = (st0 + j) * STEP + qq * EPV < ncols;     // the chunk it holds after the permute
-      if constexpr (!WIDE) {
-        // the page of the chunk this lane will hold decides its mask; the
-        // page of the chunk it loads, the address
-        bool okh, okl;
-        page_base<E>(K, P.a_pages[slot + ((col0 + min((st0 + j) * STEP + qq * EPV, ncols - EPV)) >> K.pw_log2)], okh);
-        okv[j] = okv[j] && okh;
-        const T* pl = page_base<E>(K, P.a_pages[slot + (col >> K.pw_log2)], okl);
-        av[j] = ldg16(pl + lrow * pw + (col & (pw - 1)));
-      } else {
-        av[j] = ldg16(pg1 + lrow * pw + (col & (pw - 1)));
+      const bool inside = (st0 + j) * STEP + qq * EPV < ncols;  // the chunk it holds after the permute
+#pragma unroll
+      for (int gi = 0; gi < GG; ++gi) {
+        okv[j][gi] = inside;
+        if constexpr (!WIDE) {
+          // the page of the chunk this lane will hold decides its mask; the
+          // page of the chunk it loads, the address
+          bool okh, okl;
+          page_base<E>(K, P.a_pages[slot[gi] + ((col0 + min((st0 + j) * STEP + qq * EPV, ncols - EPV)) >> K.pw_log2)],
+                       okh);
+          okv[j][gi] = okv[j][gi] && okh;
+          const T* pl = page_base<E>(K, P.a_pages[slot[gi] + (col >> K.pw_log2)], okl);
+          av[j][gi] = ldg16(pl + lrow[gi] * pw + (col & (pw - 1)));
+        } else {
+          av[j][gi] = ldg16(pg1[gi] + lrow[gi] * pw + (col & (pw - 1)));
+        }
       }
 #pragma unroll
       for (int s = 0; s < NTT; ++s) xv[j][s] = ldg16(X + xrow[s] + col);
@@ -572,21 +621,32 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
     for (int j = 0; j < SIF; ++j) {
       // permute with every lane active (a permute reads 0 from an inactive
       // lane), then zero the K positions past d_in with a mask
-      const uint4 ap = permute(av[j]);
-      const uint32_t m = (okv[j] && ok1) ? 0xffffffffu : 0u;
-      const uint4 am = make_uint4(ap.x & m, ap.y & m, ap.z & m, ap.w & m);
+      uint4 xp[NTT];
 #pragma unroll
-      for (int s = 0; s < NTT; ++s) mma(acc[s], am, permute(xv[j][s]), E());
+      for (int s = 0; s < NTT; ++s) xp[s] = permute(xv[j][s]);
+#pragma unroll
+      for (int gi = 0; gi < GG; ++gi) {
+        if (GG > 1 && g0 + gi >= G) continue;  // uniform
+        const uint4 ap = permute(av[j][gi]);
+        const uint32_t m = (okv[j][gi] && ok1[gi]) ? 0xffffffffu : 0u;
+        const uint4 am = make_uint4(ap.x & m, ap.y & m, ap.z & m, ap.w & m);
+#pragma unroll
+        for (int s = 0; s < NTT; ++s) mma(acc[gi][s], am, xp[s], E());
+      }
     }
   }
-  const int k0 = g * 16 + qq * 4;
 #pragma unroll
-  for (int s = 0; s < NTT; ++s) {
-    if (s * 16 + li < nt) {
-      float* dst = P.v + (int64_t)q * K.v_stride + d1.x + (int64_t)(tb + s * 16 + li) * r + k0;
+  for (int gi = 0; gi < GG; ++gi) {
+    if (GG > 1 && g0 + gi >= G) continue;
+    const int k0 = (g0 + gi) * 16 + qq * 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (k0 + i < r) vst<CO>(dst + i, acc[s][i]);
+    for (int s = 0; s < NTT; ++s) {
+      if (s * 16 + li < nt) {
+        float* dst = P.v + (int64_t)q * K.v_stride + d1.x + (int64_t)(tb + s * 16 + li) * r + k0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (k0 + i < r) vst<CO>(dst + i, acc[gi][s][i]);
+      }
     }
   }
 }
@@ -623,9 +683,10 @@ __device__ __forceinline__ void shrink_items(const KArgs& K, Walk walk, int tota
     const int s = cld(K.shr_item_m + u);
     const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
     if (shrink_tile_tokens(d0.w) == kMfmaShrinkTokensLong)
-      shrink_mfma<E, WIDE, kMfmaShrinkTokensLong / 16, CO>(K, K.p[p], q, d0, d1, u - d1.y, lane);
+      shrink_mfma<E, WIDE, kMfmaShrinkTokensLong / 16, kMfmaShrinkGroupsLong, CO>(K, K.p[p], q, d0, d1, u - d1.y,
+                                                                                   lane);
     else
-      shrink_mfma<E, WIDE, kMfmaShrinkTokensShort / 16, CO>(K, K.p[p], q, d0, d1, u - d1.y, lane);
+      shrink_mfma<E, WIDE, kMfmaShrinkTokensShort / 16, 1, CO>(K, K.p[p], q, d0, d1, u - d1.y, lane);
   }
   if (i0 < 0) return;
   for (;;) {

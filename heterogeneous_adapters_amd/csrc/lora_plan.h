@@ -42,6 +42,10 @@ constexpr int kMfmaExpandTokens = 16;     // tokens per MBGMM expand item (one t
 // batch's hot adapters and prefill chunks of a mixed batch: items of half
 // the load rounds, twice as many).
 constexpr int kMfmaShrinkTokensShort = 32, kMfmaShrinkTokensLong = 64, kMfmaLongSegment = 512;
+// Rank groups per MBGMM shrink item: the 64-token items of long segments
+// share each activation operand between 2 rank groups (the tile's
+// activations are read from L2 once per 2 groups), the short ones take one.
+constexpr int kMfmaShrinkGroupsLong = 2;
 constexpr int kProjsPerLaunch = 16;       // projection descriptors per launch
 constexpr int kSegChunk = 1024;           // tokens per segment-builder block
 constexpr int kMfmaMinTokens = 16;       // segment length that switches to MFMA (one full tile)
@@ -67,8 +71,10 @@ LORA_HD inline int shrink_tile_tokens(int n) { return n >= kMfmaLongSegment ? kM
 LORA_HD inline int shrink_items_valu(int n, int r) {
   return is_mfma_segment(n) ? 0 : rank_groups(r) * ceil_div_i(n, kValuTokens);
 }
+LORA_HD inline int shrink_item_groups(int n) { return n >= kMfmaLongSegment ? kMfmaShrinkGroupsLong : 1; }
 LORA_HD inline int shrink_items_mfma(int n, int r) {
-  return is_mfma_segment(n) ? rank_groups(r) * ceil_div_i(n, shrink_tile_tokens(n)) : 0;
+  return is_mfma_segment(n) ? ceil_div_i(rank_groups(r), shrink_item_groups(n)) * ceil_div_i(n, shrink_tile_tokens(n))
+                            : 0;
 }
 LORA_HD inline int valu_expand_parts(int r) { return rank_groups(r) == 1 ? 1 : rank_groups(r) == 2 ? 2 : 4; }
 LORA_HD inline int valu_expand_chunks(int n) { return ceil_div_i(n, kValuExpandTokens); }

@@ -56,7 +56,9 @@ EXPORTS = ("lora_status_string", "lora_v_slices", "lora_segments_size", "lora_se
            "lora_workspace_size", "lora_build_segments", "lora_shrink", "lora_expand", "lora_apply",
            "lora_validate_tables", "lora_cache_create", "lora_cache_destroy", "lora_cache_free_pages",
            "lora_cache_num_resident", "lora_cache_admit", "lora_cache_set_pinned", "lora_cache_release",
-           "lora_cache_lookup", "lora_upload_pages", "lora_apply_noalloc", "lora_set_wait_limit")
+           "lora_cache_lookup", "lora_upload_pages", "lora_apply_noalloc", "lora_set_wait_limit",
+           "lora_set_launch_mode")
+LORA_LAUNCH_AUTO, LORA_LAUNCH_SINGLE, LORA_LAUNCH_TWO = 0, 1, 2
 LORA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -96,6 +98,8 @@ def lib():
         L.lora_validate_tables.argtypes = [_i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
         L.lora_set_wait_limit.argtypes = [_i64]
         L.lora_set_wait_limit.restype = None
+        L.lora_set_launch_mode.argtypes = [_i32]
+        L.lora_set_launch_mode.restype = _i32
         L.lora_cache_create.argtypes = [_i32, P(_vp)]
         L.lora_cache_destroy.argtypes = [_vp]
         L.lora_cache_destroy.restype = None
@@ -291,6 +295,11 @@ def lora_apply_noalloc(ids: Optional[torch.Tensor], segs: Optional[Segments], T:
 def lora_set_wait_limit(ns: int) -> None:
     """Bound on lora_apply's internal phase wait (0: default; < 0: give up after |ns|, for tests)."""
     lib().lora_set_wait_limit(int(ns))
+
+
+def lora_set_launch_mode(mode: int) -> None:
+    """LORA_LAUNCH_AUTO / _SINGLE / _TWO for lora_apply (process-wide)."""
+    _check("lora_set_launch_mode", lib().lora_set_launch_mode(int(mode)))
 
 
 def lora_validate_tables(rank, d_in: int, d_out: int, page_width: int, num_pages: int,

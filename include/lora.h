@@ -245,13 +245,14 @@ lora_status_t lora_expand(const lora_proj_t* projs, int32_t n_projs, const lora_
  * the gather / shrink / expand sequence of [MLSP] "Segmented Gather
  * Matrix-Vector Multiplication (SGMV)" over segments of tokens that share an
  * adapter, with weights read through the page tables ([MLSP] "Unified Paging
- * Architecture").  One kernel launch per group of up to 16 projections (the
- * fused operations of [MLSP] "Custom CUDA Kernels: SGMV and MBGMV"): its
- * waves write the shrink partial sums, then wait once for the whole grid's
- * and run the expand, the same arithmetic as lora_shrink + lora_expand (Y
- * bit-identical).  The wait's bookkeeping lives in the segment buffer, so
- * calls that share one segment buffer must not run concurrently (issue them
- * on one stream).
+ * Architecture").  Per group of up to 16 projections either one kernel
+ * launch (the fused operations of [MLSP] "Custom CUDA Kernels: SGMV and
+ * MBGMV": its waves write the shrink partial sums, wait once for the whole
+ * grid's, and run the expand) or the two launches of lora_shrink and
+ * lora_expand -- see lora_set_launch_mode; the arithmetic, and Y, are the
+ * same bit for bit.  The single launch keeps its wait's bookkeeping in the
+ * segment buffer, so calls that share one segment buffer must not run
+ * concurrently (issue them on one stream).
  *   ids != NULL, segs != NULL : build segments into *segs, then apply
  *   ids != NULL, segs == NULL : build segments inside the workspace
  *   ids == NULL, segs != NULL : reuse prebuilt segments (built by
@@ -291,6 +292,19 @@ lora_status_t lora_apply_noalloc(const int32_t* ids, const lora_segments_t* segs
                                  const lora_proj_t* projs, int32_t n_projs,
                                  const lora_adapters_t* adapters, const lora_pool_t* pool,
                                  void* stream);
+
+/* How lora_apply launches a group (process-wide).  LORA_LAUNCH_SINGLE: one
+ * launch (shrink phase, wait, expand phase), which needs its grid resident
+ * at once -- a kernel on another stream holding compute units for longer
+ * than the wait's bound makes the call give up (LORA_FLAG_SYNC).
+ * LORA_LAUNCH_TWO: a shrink launch then an expand launch, no such
+ * requirement (what a caller running other kernels concurrently should
+ * use).  LORA_LAUNCH_AUTO (default): one launch for batches of at most 2048
+ * tokens, two above; both give bit-identical Y.  Errors: INVALID_ARG. */
+#define LORA_LAUNCH_AUTO 0
+#define LORA_LAUNCH_SINGLE 1
+#define LORA_LAUNCH_TWO 2
+lora_status_t lora_set_launch_mode(int32_t mode);
 
 /* Bound on the internal wait of lora_apply's single-launch kernel: its
  * expand phase waits until every work-group of the grid has written its

@@ -330,3 +330,14 @@ def test_noalloc_refuses_batches_beyond_its_array():
     txt = open(HEADERS[0]).read()
     assert re.search(r"#define LORA_NOALLOC_SCRATCH_BYTES \(64u << 20\)", txt)
     assert lora.LORA_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_launch_mode_values():
+    L = lora.lib()
+    for m in (lora.LORA_LAUNCH_AUTO, lora.LORA_LAUNCH_SINGLE, lora.LORA_LAUNCH_TWO):
+        assert L.lora_set_launch_mode(m) == 0
+    assert L.lora_set_launch_mode(3) == -1 and L.lora_set_launch_mode(-1) == -1
+    assert L.lora_set_launch_mode(lora.LORA_LAUNCH_AUTO) == 0
+    txt = open(HEADERS[0]).read()
+    for name, v in (("LORA_LAUNCH_AUTO", 0), ("LORA_LAUNCH_SINGLE", 1), ("LORA_LAUNCH_TWO", 2)):
+        assert re.search(rf"#define {name} {v}\b", txt), name

@@ -14,6 +14,7 @@ import bench
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 EXPAND = "void lora::expand_kernel<lora::Bf16, true>(lora::KArgs)"
 SHRINK = "void lora::shrink_kernel<lora::Bf16, true>(lora::KArgs)"
+APPLY = "void lora::apply_kernel<lora::Bf16, true, true>(lora::KArgs)"
 COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(at::TensorIteratorBase&)>"
 
 
@@ -33,7 +34,7 @@ def test_summary_scales_counters_by_the_calibration_copy(tmp_path, capsys):
     rows = []
     disp = 0
     for name, fetch, write in ((COPY, calib_kib / 2, calib_kib), (EXPAND, 1000.0, 300.0), (EXPAND, 3000.0, 500.0),
-                               (SHRINK, 700.0, 10.0)):
+                               (SHRINK, 700.0, 10.0), (APPLY, 4000.0, 600.0)):
         disp += 1
         rows.append([disp, name, "FETCH_SIZE", fetch])
         rows.append([disp, name, "WRITE_SIZE", write])
@@ -47,8 +48,30 @@ def test_summary_scales_counters_by_the_calibration_copy(tmp_path, capsys):
     assert float(vals["write_size_scale"]) == pytest.approx(1.0)
     assert int(vals["expand_fetch_size_bytes_per_launch"]) == 2000 * 1024 * 2
     assert int(vals["expand_write_size_bytes_per_launch"]) == 400 * 1024
-    assert int(vals["hbm_bytes_per_launch"]) == 2000 * 2048 + 400 * 1024
+    assert int(vals["expand_hbm_bytes_per_launch"]) == 2000 * 2048 + 400 * 1024
     assert int(vals["shrink_hbm_bytes_per_launch"]) == 700 * 2048 + 10 * 1024
+    assert int(vals["apply_hbm_bytes_per_launch"]) == 4000 * 2048 + 600 * 1024
+
+
+def test_committed_summaries_are_read_back(tmp_path, monkeypatch):
+    """The bench reads per-kernel durations and HBM bytes back from summaries
+    written by summarize_profile, and ignores them under another kernel hash."""
+    h = bench.kernel_source_hash()
+    stats = tmp_path / "stats.txt"
+    stats.write_text(f"command: x\nkernel_source_hash: {h}\nkernel stats (...):\n"
+                     f"    calls     avg_us     min_us     max_us   total_ms    pct  name\n"
+                     f"      128      88.50      20.00     150.00     11.328  90.00  {APPLY}\n"
+                     f"      128      30.00      10.00      60.00      3.840  10.00  {SHRINK}\n")
+    traffic = tmp_path / "traffic.txt"
+    traffic.write_text(f"command: x\nkernel_source_hash: {h}\napply_hbm_bytes_per_launch: 350000000\n"
+                       f"expand_hbm_bytes_per_launch: 200000000\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "STATS_SUMMARY", "stats.txt")
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", "traffic.txt")
+    st = bench.load_stats(h)
+    assert st[bench.APPLY_KERNEL] == 88.5 and st[bench.SHRINK_KERNEL] == 30.0
+    assert bench.load_traffic(h) == {"apply": 350000000, "expand": 200000000}
+    assert bench.load_stats("0" * 16) is None and bench.load_traffic("0" * 16) is None
 
 
 def test_summary_of_kernel_stats_and_mfma_counters(tmp_path, capsys):

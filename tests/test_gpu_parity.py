@@ -678,6 +678,7 @@ def test_single_launch_wait_give_up_is_flagged_and_recovers():
     segs = lora.Segments(w.T, w.N)
     ws = lora.workspace(w.T, w.N, w.n_projs, 1536)
     lora.lora_build_segments(b.ids, b.adapters, segs, ws)
+    lora.lora_set_launch_mode(lora.LORA_LAUNCH_SINGLE)
     try:
         lora.lora_set_wait_limit(-200_000)  # every wait gives up after 0.2 ms
         lora.lora_apply(None, segs, w.T, projs, b.adapters, b.pool, ws)
@@ -695,15 +696,25 @@ def test_single_launch_wait_give_up_is_flagged_and_recovers():
     lora.lora_build_segments(b.ids, b.adapters, segs, ws)
     lora.lora_apply(None, segs, w.T, projs, b.adapters, b.pool, ws)
     torch.cuda.synchronize()
+    lora.lora_set_launch_mode(lora.LORA_LAUNCH_AUTO)
     assert segs.arrays()["flags"] == 0
 
 
-@pytest.mark.parametrize("k", [1, 2, 3])
-def test_single_launch_matches_two_launches(k):
-    """lora_apply (one launch per group) against lora_shrink + lora_expand (two
-    launches, the same items): bit-identical Y on the benchmark configs."""
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+@pytest.mark.parametrize("mode", ["single", "two", "auto"])
+def test_launch_modes_match_split_entry_points(k, mode):
+    """lora_apply in each launch mode (one launch per group, two launches, or
+    the automatic choice by batch size) against lora_shrink + lora_expand
+    called directly: bit-identical Y on the benchmark configs (5: the mixed
+    prefill + decode batch)."""
     w = W.make_workload(k, keep_dense=False)
-    Ya, _ = gpu_apply(w)
     Ys, _ = gpu_apply(w, via="split_group")
+    code = {"single": lora.LORA_LAUNCH_SINGLE, "two": lora.LORA_LAUNCH_TWO, "auto": lora.LORA_LAUNCH_AUTO}[mode]
+    try:
+        lora.lora_set_launch_mode(code)
+        Ya, seg = gpu_apply(w)
+    finally:
+        lora.lora_set_launch_mode(lora.LORA_LAUNCH_AUTO)
+    assert seg["flags"] == 0
     for p in range(w.n_projs):
         assert np.array_equal(Ya[p], Ys[p]), p
