@@ -49,6 +49,12 @@ KERNEL_SOURCES = ("heterogeneous_adapters_amd/csrc/lora_kernels.hip", "heterogen
                   "heterogeneous_adapters_amd/csrc/lora_plan.h", "include/lora.h")
 TRAFFIC_SUMMARY = "profiles/lora_kernels.llama7b_decode_T1024.hbm_traffic.txt"
 STATS_SUMMARY = "profiles/lora_kernels.llama7b_decode_T1024.kernel_stats.txt"
+# rocprofv3 summaries of the single-workload runs (bench.py --only configN / prefill)
+CONFIG_SUMMARIES = {
+    2: ("profiles/lora_kernels.hetero_decode_mlp_T512.kernel_stats.txt",
+        "profiles/lora_kernels.hetero_decode_mlp_T512.hbm_traffic.txt"),
+    3: ("profiles/mbgmm_prefill_T38781.kernel_stats.txt", "profiles/mbgmm_prefill_T38781.hbm_traffic.txt"),
+}
 # rocprof kernel names of the decode step's kernels (bf16, wide pages)
 APPLY_KERNEL = "apply_kernel<lora::Bf16, true, true>"
 SHRINK_KERNEL = "shrink_kernel<lora::Bf16, true>"
@@ -90,10 +96,10 @@ def _read_summary(rel: str, kernel_hash: str):
     return kv, rows
 
 
-def load_traffic(kernel_hash: str):
-    """HBM bytes per launch of the decode step's kernels (apply, shrink,
-    expand) from the committed counter summary, or None."""
-    got = _read_summary(TRAFFIC_SUMMARY, kernel_hash)
+def load_traffic(kernel_hash: str, path: str = ""):
+    """HBM bytes per launch of the kernels (apply, shrink, expand) from a
+    committed counter summary (default: the decode step's), or None."""
+    got = _read_summary(path or TRAFFIC_SUMMARY, kernel_hash)
     if got is None:
         return None
     out = {}
@@ -105,10 +111,10 @@ def load_traffic(kernel_hash: str):
     return out or None
 
 
-def load_stats(kernel_hash: str):
-    """Mean duration (us) per launch of each lora kernel from the committed
-    rocprofv3 kernel-stats summary, or None."""
-    got = _read_summary(STATS_SUMMARY, kernel_hash)
+def load_stats(kernel_hash: str, path: str = ""):
+    """Mean duration (us) per launch of each lora kernel from a committed
+    rocprofv3 kernel-stats summary (default: the decode step's), or None."""
+    got = _read_summary(path or STATS_SUMMARY, kernel_hash)
     if got is None:
         return None
     out = {}
@@ -339,8 +345,30 @@ def configs_leg(which, steps, rotate_gb):
                            "shrink_us_median": round(shr_us, 2), "shrink_gbs": round(sb / shr_us / 1e3, 1),
                            "expand_us_median": round(exp_us, 2), "expand_gbs": round(eb / exp_us / 1e3, 1),
                            "timing": "hip events around each lora_shrink and lora_expand call, same rotation"}}
+        if k in CONFIG_SUMMARIES:
+            out[str(k)]["rocprof"] = config_rocprof(k, {"apply": by, "shrink": sb, "expand": eb})
         del copies, projs, b0, w
         torch.cuda.empty_cache()
+    return out
+
+
+def config_rocprof(k, algorithmic):
+    """Per-kernel rocprofv3 figures of config k from its committed summaries
+    (mean launch duration, HBM bytes per launch and their ratio to the
+    algorithmic bytes), when they were taken on the current kernel sources."""
+    hsh = kernel_source_hash()
+    stats_path, traffic_path = CONFIG_SUMMARIES[k]
+    stats = load_stats(hsh, stats_path) or {}
+    hbm = load_traffic(hsh, traffic_path) or {}
+    out = {"stats_source": stats_path if stats else None, "traffic_source": traffic_path if hbm else None}
+    for kname, key in ((APPLY_KERNEL, "apply"), (SHRINK_KERNEL, "shrink"), (EXPAND_KERNEL, "expand")):
+        us, hb = stats.get(kname), hbm.get(key)
+        if us is None and hb is None:
+            continue
+        alg = algorithmic[key]
+        out[key] = {"mean_launch_us": us, "gbs": round(alg / us / 1e3, 1) if us else None,
+                    "algorithmic_bytes_per_launch": int(alg), "hbm_bytes_per_launch": hb,
+                    "hbm_over_algorithmic": round(hb / alg, 3) if hb else None}
     return out
 
 

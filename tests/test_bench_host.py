@@ -74,6 +74,25 @@ def test_committed_summaries_are_read_back(tmp_path, monkeypatch):
     assert bench.load_stats("0" * 16) is None and bench.load_traffic("0" * 16) is None
 
 
+def test_config_summaries_give_traffic_over_algorithmic(tmp_path, monkeypatch):
+    """A single-workload summary pair yields each kernel's mean launch, rate
+    and counter bytes over algorithmic bytes; kernels absent from both are
+    left out, and summaries under another kernel hash are not used."""
+    h = bench.kernel_source_hash()
+    (tmp_path / "s.txt").write_text(f"command: x\nkernel_source_hash: {h}\nkernel stats (...):\n"
+                                    f"    calls     avg_us     min_us     max_us   total_ms    pct  name\n"
+                                    f"       20      50.00      40.00      60.00      1.000  50.00  {SHRINK}\n")
+    (tmp_path / "t.txt").write_text(f"command: x\nkernel_source_hash: {h}\nshrink_hbm_bytes_per_launch: 110000000\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "CONFIG_SUMMARIES", {3: ("s.txt", "t.txt")})
+    got = bench.config_rocprof(3, {"apply": 1.0, "shrink": 100e6, "expand": 1.0})
+    assert set(got) == {"stats_source", "traffic_source", "shrink"}
+    assert got["shrink"] == {"mean_launch_us": 50.0, "gbs": 2000.0, "algorithmic_bytes_per_launch": 100000000,
+                             "hbm_bytes_per_launch": 110000000, "hbm_over_algorithmic": 1.1}
+    (tmp_path / "t.txt").write_text("command: x\nkernel_source_hash: 0000000000000000\n")
+    assert bench.config_rocprof(3, {"apply": 1.0, "shrink": 100e6, "expand": 1.0})["traffic_source"] is None
+
+
 def test_summary_of_kernel_stats_and_mfma_counters(tmp_path, capsys):
     d = tmp_path / "prof"
     d.mkdir()
