@@ -165,12 +165,6 @@ void wait_params(KArgs& K) {
   K.wait_bias = ns < 0 ? 1 : 0;
 }
 
-int grid_for(int resident, int64_t bound) {
-  int64_t g = std::min<int64_t>(resident, std::max<int64_t>(bound, 1));
-  g = (g + 7) / 8 * 8;
-  return (int)std::max<int64_t>(g, 8);
-}
-
 KProj make_kproj(const lora_proj_t& p, float* v, int nv, int dtype) {
   KProj k;
   memset(&k, 0, sizeof k);
@@ -262,15 +256,15 @@ lora_status_t run(const KArgs& K, int dtype, bool do_shrink, bool do_expand, hip
   if (lora_status_t st = device_info(&d)) return st;
   const int di = dtype == LORA_DTYPE_BF16 ? 1 : 0;
   if (do_shrink && do_expand && single_launch(K.T))  // one launch; its grid is resident at once
-    return launch_apply(K, dtype, grid_for(d->cus * d->occ_apply[di], ceil_div64(std::max(bs, be), kWaves)),
+    return launch_apply(K, dtype, launch_grid(d->cus * d->occ_apply[di], ceil_div64(std::max(bs, be), kWaves)),
                         stream) == hipSuccess
                ? LORA_OK
                : LORA_ERR_HIP;
   // items are per wave: kWaves items per work-group
-  if (do_shrink && launch_shrink(K, dtype, grid_for(d->cus * d->occ_shrink[di], ceil_div64(bs, kWaves)), stream) !=
+  if (do_shrink && launch_shrink(K, dtype, launch_grid(d->cus * d->occ_shrink[di], ceil_div64(bs, kWaves)), stream) !=
                        hipSuccess)
     return LORA_ERR_HIP;
-  if (do_expand && launch_expand(K, dtype, grid_for(d->cus * d->occ_expand[di], ceil_div64(be, kWaves)), stream) !=
+  if (do_expand && launch_expand(K, dtype, launch_grid(d->cus * d->occ_expand[di], ceil_div64(be, kWaves)), stream) !=
                        hipSuccess)
     return LORA_ERR_HIP;
   return LORA_OK;

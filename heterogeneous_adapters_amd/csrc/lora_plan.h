@@ -159,6 +159,21 @@ LORA_HD inline PlanLayout plan_layout(int T, int N) {
 // items: no work-group barrier couples the waves.
 LORA_HD inline int xcd_count(int grid) { return (grid % 8 == 0) ? 8 : 1; }
 
+// Grid of a persistent launch: enough work-groups for the items (bound), at
+// most `resident` (compute units x work-groups per unit), rounded to a
+// multiple of 8 when that stays within `resident` (so every XCD gets the same
+// share), else down to one.  Never above `resident`: the single-launch
+// kernel's phase barrier needs every work-group of its grid resident at once.
+LORA_HD inline int launch_grid(int resident, long long bound) {
+  if (resident < 1) resident = 1;
+  long long g = bound < 1 ? 1 : bound;
+  if (g > resident) g = resident;
+  const long long up = (g + 7) / 8 * 8;
+  if (up <= resident) return (int)up;
+  const long long down = g / 8 * 8;
+  return (int)(down >= 8 ? down : g);
+}
+
 struct WaveWalk {
   int i, end, stride, lo;
   // `walkers` items are taken per work-group at a time (kWaves: one per wave;

@@ -596,8 +596,9 @@ def test_segment_buffer_larger_than_the_batch():
     """A segment buffer laid out for a larger batch (capacity T + 37 tokens,
     N + 5 adapters) serves the batch through every entry point, bit-identical
     to a buffer of the batch's own size.  Prebuilt segments reused with
-    another token count, and a buffer that was never built, are not walked:
-    nothing is written and LORA_FLAG_SEGMENTS is raised."""
+    another token count, a buffer that was never built, and one whose item
+    totals exceed its capacity are not walked: nothing is written and
+    LORA_FLAG_SEGMENTS is raised."""
     w = W.make_workload(2, dict(T=300, N=9, ranks_override=[8, 16, 64, 24, 1, 32, 128, 40, 8], page_width=512,
                                 projs=(("a", 1024, 1536), ("b", 1536, 1024))), keep_dense=False)
     Yref, segref = gpu_apply(w)
@@ -662,6 +663,20 @@ def test_segment_buffer_larger_than_the_batch():
     assert int(fresh.counts()[lora.COUNT_FLAGS]) & lora.FLAG_SEGMENTS
     for p in range(w.n_projs):
         assert bool((b.Y[p].float() == 7.0).all()), p
+    # built, then one item total (index 4..7: shrink MBGMM / MBGMV, expand
+    # MBGMM / MBGMV) pushed past the buffer's capacity: not walked either
+    for idx in range(4, 8):
+        segs_c = lora.Segments(w.T, w.N)
+        lora.lora_build_segments(b.ids, b.adapters, segs_c, ws)
+        torch.cuda.synchronize()
+        segs_c.counts()[idx] = 1 << 29
+        lora.lora_apply(None, segs_c, w.T, projs, b.adapters, b.pool, ws)
+        lora.lora_shrink(projs, b.adapters, segs_c, b.pool, vs, stride)
+        lora.lora_expand(projs, b.adapters, segs_c, b.pool, vs, 0, stride)
+        torch.cuda.synchronize()
+        assert int(segs_c.counts()[lora.COUNT_FLAGS]) & lora.FLAG_SEGMENTS, idx
+        for p in range(w.n_projs):
+            assert bool((b.Y[p].float() == 7.0).all()), (idx, p)
 
 
 def test_single_launch_wait_give_up_is_flagged_and_recovers():

@@ -1,6 +1,7 @@
 """Host check of the persistent grids' work walks (csrc/lora_plan.h): for
 every grid size and item totals tried, the waves' walks take every shrink and
-expand item exactly once.  The single-launch apply kernel relies on this: a
+expand item exactly once, and the launch grid never exceeds the resident
+work-groups it is given.  The single-launch apply kernel relies on this: a
 wave finishes all of its shrink items before it arrives at the phase
 barrier, so once every work-group of the grid has arrived, every shrink item
 (every partial sum of v) has been written.  Compiled with the host compiler
@@ -50,7 +51,23 @@ static void expand(int grid, int tm, int tv) {
   expect_once(hm, "expand mbgmm", grid, tm, tv);
   expect_once(hv, "expand mbgmv", grid, tm, tv);
 }
+static void grid(int resident, long long bound) {
+  const int g = launch_grid(resident, bound);
+  const int res = resident < 1 ? 1 : resident;
+  const long long want = bound < 1 ? 1 : bound;
+  const long long need = want < res ? want : res;
+  // resident, a multiple of 8 whenever 8 fit, and short of the items' bound
+  // (or of the resident count) by less than 8
+  const bool ok = g >= 1 && g <= res && (res < 8 || g % 8 == 0) && g > need - 8;
+  if (!ok) {
+    if (bad < 10) printf("FAIL launch_grid(%d, %lld) = %d\n", resident, bound, g);
+    ++bad;
+  }
+}
 int main() {
+  for (int r = 0; r <= 2100; ++r)
+    for (long long b : {-1LL, 0LL, 1LL, 5LL, 7LL, 8LL, 9LL, 100LL, 767LL, 768LL, 769LL, 2047LL, 5000LL, 1LL << 40})
+      grid(r, b);
   const int grids[] = {1, 3, 8, 16, 24, 40, 64, 96, 256, 768, 1280, 2048};
   const int totals[] = {0, 1, 5, 7, 8, 9, 63, 64, 100, 777, 4096, 20000, 150000};
   for (int g : grids)
