@@ -191,11 +191,22 @@ __device__ __forceinline__ uint4 keep_first(uint4 w, int kn, F32) {
   return make_uint4(kn > 0 ? w.x : 0u, kn > 1 ? w.y : 0u, kn > 2 ? w.z : 0u, kn > 3 ? w.w : 0u);
 }
 
-// B vectors (kEpv consecutive ranks of one output column; the 16 rank slots
-// of a column are one 32- or 64-byte row of its page) are loaded
-// unconditionally from valid addresses -- ranks past r from the same column
-// row, a rank group past the adapter's from its last group, a page outside
-// the pool from page 0 -- and zeroed where they are used.  A skipped load
+// In-page element offset of the B vector holding ranks kin..kin+kEpv-1
+// (kin = rank - 16g, a multiple of kEpv) of page column jp: half kin/8 at
+// kin/8 * 8*pw, then 8 ranks per column.  `upper` (the group has more than 8
+// ranks) false reads the lower half instead (see the note above).
+__device__ __forceinline__ int b_off(int jp, int kin, int pw, bool upper) {
+  return (upper ? (kin >> 3) * 8 * pw : 0) + jp * 8 + (kin & 7);
+}
+
+// B vectors (kEpv consecutive ranks of one output column; a B page holds
+// its 16 rank slots as two halves of 8, so the 8 ranks of a column in one
+// half are one 16- or 32-byte run) are loaded unconditionally from valid
+// addresses -- the upper half of a rank group with at most 8 ranks from the
+// same column's lower half (bytes the lower half's own load fetches, so such
+// a group moves only its used half), a rank group past the adapter's from
+// its last group, a page outside the pool from page 0 -- and zeroed where
+// they are used.  A skipped load
 // would write zeros into registers that an older load may still target, and
 // the compiler then waits for that older load.
 
@@ -985,9 +996,10 @@ __device__ __forceinline__ uint32_t pack_cols(const float (&y)[1]) { return __fl
 
 // MBGMV expand item (one wave): (segment, part of a column block, chunk of
 // <= kValuExpandTokens of the segment's tokens).  A column block is kValuSubBlocks = 4 sub-blocks
-// of 64 lanes x CPL adjacent columns (2 in bf16, 1 in fp32); the 16 ranks of
-// a column are adjacent in the B page, so a lane reads 64 contiguous bytes
-// per sub-block and rank group.  A segment with 1, 2 or more rank groups
+// of 64 lanes x CPL adjacent columns (2 in bf16, 1 in fp32); the 8 ranks of
+// a column in each half of the B page are adjacent, so a lane reads 32
+// contiguous bytes from each half per sub-block and rank group (the lower
+// half only, for a group of at most 8 ranks).  A segment with 1, 2 or more rank groups
 // covers the block in 1, 2 or 4 parts of nsub = 4, 2 or 1 sub-blocks, so
 // every item holds four (sub-block, rank group) pairs -- 16 KiB of B per wave
 // in bf16 -- all requested at once with the Y_base rows of every token of
@@ -1044,8 +1056,10 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
         const int jcol = nsub == 4 ? jc[i] : (nsub == 2 ? jc[i & 1] : jc[0]);
         // a group past the adapter's has page id 0 here (never used)
         const T* pg = page_base<E>(K, gi == 0 ? pid0 : gi == 1 ? pid1 : gi == 2 ? pid2 : pid3, okp[i]);
+        const bool up = r - 16 * (g0 + gi) > 8;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) b[i][q] = ldg16(pg + (jcol & (pw - 1)) * 16 + (q / (16 / EPV)) * 16 + (q % (16 / EPV)) * EPV);
+        for (int q = 0; q < 4; ++q)
+          b[i][q] = ldg16(pg + b_off((jcol & (pw - 1)) + q / (16 / EPV), (q % (16 / EPV)) * EPV, pw, up));
       }
     } else {  // per-lane page ids, all requested before the first data load
       int pl[NP];
@@ -1060,8 +1074,10 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
       for (int i = 0; i < NP; ++i) {
         const int jcol = nsub == 4 ? jc[i] : (nsub == 2 ? jc[i & 1] : jc[0]);
         const T* pg = page_base<E>(K, pl[i], okp[i]);
+        const bool up = r - 16 * (g0 + i / nsub) > 8;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) b[i][q] = ldg16(pg + (jcol & (pw - 1)) * 16 + (q / (16 / EPV)) * 16 + (q % (16 / EPV)) * EPV);
+        for (int q = 0; q < 4; ++q)
+          b[i][q] = ldg16(pg + b_off((jcol & (pw - 1)) + q / (16 / EPV), (q % (16 / EPV)) * EPV, pw, up));
       }
     }
   };
@@ -1303,7 +1319,7 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
         // reads the last group and is skipped at the product
         bool ok = okk[ks];
         const T* pg = one_page ? pgk[ks] : page_base<E>(K, P.b_pages[bbase + g * ncolB + (j >> K.pw_log2)], ok);
-        bv[ct][ks] = ldg16(pg + (j & (pw - 1)) * 16 + (k0 & 15));
+        bv[ct][ks] = ldg16(pg + b_off(j & (pw - 1), k0 & 15, pw, r - 16 * g > 8));
         okc[ct][ks] = ok;
       }
     }

@@ -117,8 +117,11 @@ typedef struct {
  *      (rows) x inputs c*PW..c*PW+PW-1 (columns): element (rank k, input i)
  *      at in-page offset (k-16g)*PW + (i-c*PW).
  *   B: page b_pages[b_indptr[a] + g*ceil(d_out/PW) + c] holds outputs
- *      c*PW..c*PW+PW-1 (rows) x ranks 16g..16g+15 (columns): element
- *      (output j, rank k) at in-page offset (j-c*PW)*16 + (k-16g).
+ *      c*PW..c*PW+PW-1 x ranks 16g..16g+15 as two halves of 8 ranks each:
+ *      element (output j, rank k) at in-page offset
+ *      h*8*PW + (j-c*PW)*8 + (k-16g-8h), h = (k-16g)/8.  The 8 ranks of an
+ *      output column in one half are contiguous (16 bytes in bf16), and a
+ *      rank group with at most 8 ranks uses only the first half.
  * Adapter a owns ceil(r_a/16)*ceil(d/PW) slots of each table.  Page rows or
  * columns beyond r_a or d are never read. */
 typedef struct {

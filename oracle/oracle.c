@@ -33,7 +33,8 @@
  * Page format (see the generator): page = 16 x PW elements.  A element
  * (input i, rank k) lives in A-table slot (k/16)*ceil(d_in/PW) + i/PW at
  * offset (k%16)*PW + i%PW.  B element (rank k, output j) lives in B-table slot
- * (k/16)*ceil(d_out/PW) + j/PW at offset (j%PW)*16 + k%16.
+ * (k/16)*ceil(d_out/PW) + j/PW at offset ((k%16)/8)*8*PW + (j%PW)*8 + k%8
+ * (two halves of 8 ranks, each holding PW columns of 8 contiguous ranks).
  *
  * Token classes: ids[t] == -1 is a base-model token ([MLSA] "What vLLM
  * actually gives you": base-model requests share the server); any other id
@@ -157,7 +158,8 @@ static int b_elem(const oracle_tables* tb, int32_t a, int32_t k, int32_t j, floa
   int64_t slot = (int64_t)tb->b_indptr[a] + (k / 16) * ncol + j / tb->pw;
   int32_t page = tb->b_pages[slot];
   if (page < 0 || page >= tb->num_pages) return -1;
-  int64_t off = (int64_t)page * 16 * tb->pw + (int64_t)(j % tb->pw) * 16 + (k % 16);
+  int64_t off = (int64_t)page * 16 * tb->pw + (int64_t)((k % 16) / 8) * 8 * tb->pw + (int64_t)(j % tb->pw) * 8 +
+                (k % 8);
   *out = load_elem(tb->pool, tb->dtype, off);
   return 0;
 }

@@ -19,8 +19,12 @@ MUTANTS = [
     ("drop the scale alpha/r", "y = yb + s * acc;", "y = yb + acc;"),
     ("subtract the update", "y = yb + s * acc;", "y = yb - s * acc;"),
     ("scale r/alpha", "alpha[a] / (float)r", "(float)r / alpha[a]"),
-    ("B page read rank-rows (transposed)", "(int64_t)(j % tb->pw) * 16 + (k % 16)",
+    ("B page read rank-rows (transposed)",
+     "(int64_t)((k % 16) / 8) * 8 * tb->pw + (int64_t)(j % tb->pw) * 8 +\n                (k % 8)",
      "(int64_t)(k % 16) * tb->pw + (j % tb->pw)"),
+    ("B page read as 16 contiguous ranks per column",
+     "(int64_t)((k % 16) / 8) * 8 * tb->pw + (int64_t)(j % tb->pw) * 8 +\n                (k % 8)",
+     "(int64_t)(j % tb->pw) * 16 + (k % 16)"),
     ("A page read column-major (transposed)", "(int64_t)(k % 16) * tb->pw + (i % tb->pw)",
      "(int64_t)(i % 16) * tb->pw + (k % tb->pw)"),
     ("B column page ignored", "(k / 16) * ncol + j / tb->pw;", "(k / 16) * ncol;"),

@@ -27,8 +27,9 @@ Pool page format (the same format the C header documents):
     (rank k, input i) at in-page offset (k-16g)*PW + (i-c*PW);
   * B of adapter a (r x d_out) is stored as its d_out x r transpose (again the
     [MLSA] orientation), cut into PW-row blocks c and 16-rank groups g; slot
-    g*ceil(d_out/PW) + c holds the page, element (output j, rank k) at
-    in-page offset (j-c*PW)*16 + (k-16g);
+    g*ceil(d_out/PW) + c holds the page as two halves of 8 ranks, element
+    (output j, rank k) at in-page offset h*8*PW + (j-c*PW)*8 + (k-16g-8h),
+    h = (k-16g)//8;
   * elements of a page that belong to no rank (< r) or feature (< d) are
     filled with NaN so that any read of padding shows in the results.
 """
@@ -171,7 +172,9 @@ def pack_b_pages(B: np.ndarray, pw: int, fill) -> np.ndarray:
     G, nco = n_groups(r), n_blocks(d_out, pw)
     pad = np.full((nco * pw, G * PAGE_ROWS), fill, dtype=B.dtype)
     pad[:d_out, :r] = B.T
-    return pad.reshape(nco, pw, G, PAGE_ROWS).transpose(2, 0, 1, 3).reshape(G * nco, pw * PAGE_ROWS)
+    # [c, j', g, h, k'] -> page (g, c) = [h][j'][k']
+    half = PAGE_ROWS // 2
+    return pad.reshape(nco, pw, G, 2, half).transpose(2, 0, 3, 1, 4).reshape(G * nco, pw * PAGE_ROWS)
 
 
 @dataclass

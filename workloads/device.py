@@ -108,10 +108,12 @@ def make_device_workload(k: int, device="cuda", overrides=None, chunk_pages: int
                         v = sub.view(-1, PAGE_ROWS, pw)
                         v[:, int(r_ok):, :] = nan
                         v[:, :, int(f_ok):] = nan
-                    else:         # B page: [PW outputs][16 ranks]
-                        v = sub.view(-1, pw, PAGE_ROWS)
-                        v[:, :, int(r_ok):] = nan
-                        v[:, int(f_ok):, :] = nan
+                    else:         # B page: [2 halves][PW outputs][8 ranks]
+                        half = PAGE_ROWS // 2
+                        v = sub.view(-1, 2, pw, half)
+                        v[:, 0, :, min(int(r_ok), half):] = nan
+                        v[:, 1, :, max(int(r_ok) - half, 0):] = nan
+                        v[:, :, int(f_ok):, :] = nan
                     pool.index_copy_(0, idx, sub)
     # share_x: groups of projection names that read one input inside a layer
     # (q/k/v, gate/up of a transformer block); their X is one tensor
