@@ -44,7 +44,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 struct Bf16 {
   typedef uint16_t T;
   static constexpr int kEpv = 8;  // elements per 16-byte vector
-  static constexpr int kShrinkBlocks = 5;  // occupancy targets (work-groups per CU)
+  static constexpr int kShrinkBlocks = 4;  // occupancy targets (work-groups per CU)
   static constexpr int kExpandBlocks = 3;
 };
 struct F32 {
@@ -543,10 +543,13 @@ __device__ __forceinline__ void shrink_mfma(const KArgs& K, const KProj& P, int 
   constexpr int STEP = 4 * EPV;
   constexpr int NSTEP = kKSlice / STEP;
   constexpr int TILE = 16 * NTT;                          // tokens per item
-  // K steps in flight: 8 (A + NTT X) operand pairs with one group; with
-  // groups sharing X, one step (GG A + NTT X operands) keeps the kernel
-  // within the shrink's register budget
-  constexpr int SIF = GG == 1 ? 8 / NTT : 1;
+  // K steps in flight: 8 (A + NTT X) operand pairs with one group, two with
+  // groups sharing X (GG A + NTT X operands each).  A K step reads 64 bytes
+  // of every operand row, so two steps request each 128-byte line whole in
+  // one burst: requested one step apart, the line's second half was often
+  // fetched again, evicted by the other waves' loads in between (the prefill
+  // shrink read 1.31x its bytes with one step, 1.06x with two)
+  constexpr int SIF = GG == 1 ? 8 / NTT : 2;
   static_assert(NSTEP % SIF == 0, "steps in flight divide the slice");
   const int a = d0.x, r = d0.y, t0 = d0.z, n = d0.w;
   const int G = rank_groups(r);
@@ -693,9 +696,11 @@ __device__ __forceinline__ void shrink_items(const KArgs& K, Walk walk, int tota
     }
     const int s = cld(K.shr_item_m + u);
     const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
-    if (shrink_tile_tokens(d0.w) == kMfmaShrinkTokensLong)
-      shrink_mfma<E, WIDE, kMfmaShrinkTokensLong / 16, kMfmaShrinkGroupsLong, CO>(K, K.p[p], q, d0, d1, u - d1.y,
-                                                                                   lane);
+    const int gg = shrink_item_groups(d0.w, d0.y);  // uniform
+    if (gg == 2)
+      shrink_mfma<E, WIDE, kMfmaShrinkTokensLong / 16, 2, CO>(K, K.p[p], q, d0, d1, u - d1.y, lane);
+    else if (gg == 4)
+      shrink_mfma<E, WIDE, kMfmaShrinkTokensShort / 16, 4, CO>(K, K.p[p], q, d0, d1, u - d1.y, lane);
     else
       shrink_mfma<E, WIDE, kMfmaShrinkTokensShort / 16, 1, CO>(K, K.p[p], q, d0, d1, u - d1.y, lane);
   }

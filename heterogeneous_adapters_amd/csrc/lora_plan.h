@@ -36,16 +36,15 @@ constexpr int kValuTokens = 2;            // tokens per MBGMV shrink item
 constexpr int kValuExpandTokens = 2;
 constexpr int kCopyTokens = 8;            // rows per copy item (tokens without an adapter)
 constexpr int kMfmaExpandTokens = 16;     // tokens per MBGMM expand item (one tile)
-// Tokens per MBGMM shrink item (16-token MFMA tiles sharing each A operand):
-// 64 for segments of at least kMfmaLongSegment tokens (prefill sequences: A
-// is re-read from L2 once per 64 tokens), 32 for shorter ones (a decode
-// batch's hot adapters and prefill chunks of a mixed batch: items of half
-// the load rounds, twice as many).
+// MBGMM shrink items: 16-token MFMA tiles x 16-rank groups, each A operand
+// shared by the item's token tiles and each activation operand by its rank
+// groups.  Segments shorter than kMfmaLongSegment (a decode batch's hot
+// adapters, prefill chunks of a mixed batch): 32 tokens x 1 group.  Longer
+// ones (prefill sequences): 64 tokens x 2 groups for ranks up to 32, and
+// 32 tokens x 4 groups above, so that a token tile's activations are read
+// once per item for every rank up to 64 (the same accumulator and operand
+// registers either way).
 constexpr int kMfmaShrinkTokensShort = 32, kMfmaShrinkTokensLong = 64, kMfmaLongSegment = 512;
-// Rank groups per MBGMM shrink item: the 64-token items of long segments
-// share each activation operand between 2 rank groups (the tile's
-// activations are read from L2 once per 2 groups), the short ones take one.
-constexpr int kMfmaShrinkGroupsLong = 2;
 constexpr int kProjsPerLaunch = 16;       // projection descriptors per launch
 constexpr int kSegChunk = 1024;           // tokens per segment-builder block
 constexpr int kMfmaMinTokens = 16;       // segment length that switches to MFMA (one full tile)
@@ -60,7 +59,6 @@ LORA_HD inline int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 LORA_HD inline int rank_groups(int r) { return (r + 15) >> 4; }
 
 LORA_HD inline bool is_mfma_segment(int n) { return n >= kMfmaMinTokens; }
-LORA_HD inline int shrink_tile_tokens(int n) { return n >= kMfmaLongSegment ? kMfmaShrinkTokensLong : kMfmaShrinkTokensShort; }
 
 // Work items of one segment, per 512-column shrink slice or per expand
 // column block.  MBGMV shrink: (rank group, <= kValuTokens tokens); MBGMM
@@ -71,9 +69,14 @@ LORA_HD inline int shrink_tile_tokens(int n) { return n >= kMfmaLongSegment ? kM
 LORA_HD inline int shrink_items_valu(int n, int r) {
   return is_mfma_segment(n) ? 0 : rank_groups(r) * ceil_div_i(n, kValuTokens);
 }
-LORA_HD inline int shrink_item_groups(int n) { return n >= kMfmaLongSegment ? kMfmaShrinkGroupsLong : 1; }
+LORA_HD inline int shrink_item_groups(int n, int r) {
+  return n < kMfmaLongSegment ? 1 : rank_groups(r) <= 2 ? 2 : 4;
+}
+LORA_HD inline int shrink_tile_tokens(int n, int r) {
+  return shrink_item_groups(n, r) == 2 ? kMfmaShrinkTokensLong : kMfmaShrinkTokensShort;
+}
 LORA_HD inline int shrink_items_mfma(int n, int r) {
-  return is_mfma_segment(n) ? ceil_div_i(rank_groups(r), shrink_item_groups(n)) * ceil_div_i(n, shrink_tile_tokens(n))
+  return is_mfma_segment(n) ? ceil_div_i(rank_groups(r), shrink_item_groups(n, r)) * ceil_div_i(n, shrink_tile_tokens(n, r))
                             : 0;
 }
 LORA_HD inline int valu_expand_parts(int r) { return rank_groups(r) == 1 ? 1 : rank_groups(r) == 2 ? 2 : 4; }
