@@ -1141,6 +1141,37 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
   } else {
     stage_v<CO>(K, P, d1.x, r, tb, n, vs, lane);
   }
+  // Masks of a loaded batch, applied once in place (the token loop reuses the
+  // registers): a page outside the pool reads as zeros, and in the last
+  // group of a rank below a multiple of 16 the ranks >= r are zeroed.  With
+  // wave-uniform page ids the page test is a branch, not a select per word.
+  auto mask_batch = [&](int g0) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int g = g0 + i / nsub;
+      if (g >= G) continue;
+      uint4 (&w)[4] = b[i];
+      if constexpr (ONE_PAGE) {
+        if (!okp[i]) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) w[q] = zero4();
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = okp[i] ? w[q] : zero4();
+      }
+      if (r - g * 16 < 16) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int v = 0; v < 16 / EPV; ++v) {
+            const int kn = r - g * 16 - v * EPV;
+            w[c * (16 / EPV) + v] = kn >= EPV ? w[c * (16 / EPV) + v] : keep_first(w[c * (16 / EPV) + v], kn, E());
+          }
+      }
+    }
+  };
+  mask_batch(0);
   for (int t = 0; t < n; ++t) {
     uint32_t (&yb)[NP] = ybt[0];  // token t's row; the rows move up one slot per token
     float acc[NP][CPL];  // per pair
@@ -1160,6 +1191,7 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
           pid3 = g0 + 3 < G ? cld(P.b_pages + base + (g0 + 3) * ncolB) : 0;
         }
         load_batch(g0);
+        mask_batch(g0);
       }
       uint4 vv[4];  // v of the current group: bf16 ranks {0-7, 8-15}; fp32 ranks 0-15
 #pragma unroll
@@ -1177,23 +1209,17 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
             for (int q = 0; q < 4; ++q) vv[q] = vt[q];
           }
         }
-        // masked in place: the masks do not depend on the token, so masking
-        // the registers again for the next token changes nothing
-        uint4 (&w)[4] = b[i];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = okp[i] ? w[q] : zero4();
-        if (r - g * 16 < 16) {  // the last group of a rank below a multiple of 16: mask ranks >= r
-#pragma unroll
-          for (int c = 0; c < CPL; ++c)
-#pragma unroll
-            for (int v = 0; v < 16 / EPV; ++v) {
-              const int kn = r - g * 16 - v * EPV;
-              w[c * (16 / EPV) + v] = kn >= EPV ? w[c * (16 / EPV) + v] : keep_first(w[c * (16 / EPV) + v], kn, E());
-            }
-        }
+        const uint4 (&w)[4] = b[i];
         if constexpr (EPV == 8) {  // bf16: packed B against packed bf16 v (see stage_v_split)
+          // a group of at most 8 ranks has only zeros in its upper half:
+          // its products would add exact zeros, and are skipped
+          if (r - g * 16 > 8) {
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) acc[i][c] = dot8(w[c * 2 + 1], vv[1], dot8(w[c * 2], vv[0], acc[i][c]));
+            for (int c = 0; c < CPL; ++c) acc[i][c] = dot8(w[c * 2 + 1], vv[1], dot8(w[c * 2], vv[0], acc[i][c]));
+          } else {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[i][c] = dot8(w[c * 2], vv[0], acc[i][c]);
+          }
         } else {
 #pragma unroll
           for (int k4 = 0; k4 < 4; ++k4)
