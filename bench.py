@@ -414,7 +414,7 @@ def main():
         summarize_profile(args.summarize_profile, args.profile_command)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the adapter branch is measured on one GPU; --gpus {args.gpus} is not supported "
               "(tokens shard across GPUs with no exchange; see the sharding design)", file=sys.stderr)
         sys.exit(2)
 
