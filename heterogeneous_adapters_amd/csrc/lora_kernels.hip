@@ -1165,8 +1165,12 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
         for (int c = 0; c < CPL; ++c)
 #pragma unroll
           for (int v = 0; v < 16 / EPV; ++v) {
+            // bf16: a vector wholly past r is an upper half, whose products
+            // are skipped (see the token loop), so only a partly used vector
+            // is masked; fp32 multiplies every vector
             const int kn = r - g * 16 - v * EPV;
-            w[c * (16 / EPV) + v] = kn >= EPV ? w[c * (16 / EPV) + v] : keep_first(w[c * (16 / EPV) + v], kn, E());
+            if (kn < EPV && (kn > 0 || EPV != 8))
+              w[c * (16 / EPV) + v] = keep_first(w[c * (16 / EPV) + v], kn, E());
           }
       }
     }

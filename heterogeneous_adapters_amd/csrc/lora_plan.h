@@ -161,6 +161,11 @@ LORA_HD inline PlanLayout plan_layout(int T, int N) {
 // adapter slice are read through the same L2.  Every wave walks its own
 // items: no work-group barrier couples the waves.
 LORA_HD inline int xcd_count(int grid) { return (grid % 8 == 0) ? 8 : 1; }
+// log2 of xcd_count: the walks split ranges with shifts, not divisions (a
+// 64-bit division is a long scalar sequence in every wave's prologue)
+LORA_HD inline int xcd_shift(int grid) { return (grid % 8 == 0) ? 3 : 0; }
+// start of XCD part x of [0, total): floor(total * x / 2^sh)
+LORA_HD inline int xcd_part(int total, int x, int sh) { return (int)(((long long)total * x) >> sh); }
 
 // Grid of a persistent launch: enough work-groups for the items (bound), at
 // most `resident` (compute units x work-groups per unit), rounded to a
@@ -182,12 +187,12 @@ struct WaveWalk {
   // `walkers` items are taken per work-group at a time (kWaves: one per wave;
   // 1: whole-block items), `w` is this walker's index in the work-group.
   LORA_HD WaveWalk(int total, int w, int walkers, int grid, int block) {
-    const int nx = xcd_count(grid);
-    const int x = block % nx;
-    lo = (int)(((long long)total * x) / nx);
-    end = (int)(((long long)total * (x + 1)) / nx);
-    i = lo + (block / nx) * walkers + w;
-    stride = (grid / nx) * walkers;
+    const int sh = xcd_shift(grid);
+    const int x = block & ((1 << sh) - 1);
+    lo = xcd_part(total, x, sh);
+    end = xcd_part(total, x + 1, sh);
+    i = lo + (block >> sh) * walkers + w;
+    stride = (grid >> sh) * walkers;
   }
 };
 
@@ -199,11 +204,11 @@ struct TwoClassWalk {
   int i, end, nV, W, ib, ka;  // ka: first-phase items left after the current one (-1: second phase)
   int lo;                     // start of this XCD's part of the range
   LORA_HD TwoClassWalk(int total, int Wm, int R, int wv, int grid, int block) {
-    const int nx = xcd_count(grid);
-    const int x = block % nx, G = grid / nx;
-    const int w = (block / nx) * kWaves + wv;  // walker index inside the XCD
-    lo = (int)(((long long)total * x) / nx);
-    end = (int)(((long long)total * (x + 1)) / nx);
+    const int sh = xcd_shift(grid);
+    const int x = block & ((1 << sh) - 1), G = grid >> sh;
+    const int w = (block >> sh) * kWaves + wv;  // walker index inside the XCD
+    lo = xcd_part(total, x, sh);
+    end = xcd_part(total, x + 1, sh);
     W = G * kWaves;
     Wm = Wm < W ? Wm : W;
     nV = W - Wm;
@@ -263,11 +268,11 @@ struct ExpandSplit {
 LORA_HD inline ExpandSplit expand_walk_split(int total_m, int total_v, int grid, int block) {
   ExpandSplit e{0, 0, 0, 0, 0, 1};
   if (total_m <= 0) return e;
-  const int nx = xcd_count(grid);
-  const int x = block % nx, beta = block / nx, G = grid / nx;
-  const int lo_m = (int)(((long long)total_m * x) / nx);
+  const int sh = xcd_shift(grid);
+  const int x = block & ((1 << sh) - 1), beta = block >> sh, G = grid >> sh;
+  const int lo_m = xcd_part(total_m, x, sh);
   e.lo_m = lo_m;
-  e.end_m = (int)(((long long)total_m * (x + 1)) / nx);
+  e.end_m = xcd_part(total_m, x + 1, sh);
   const int m = e.end_m - lo_m;
   const int third = G / 3 > 1 ? G / 3 : 1;
   e.Gm = m <= 0 ? 0 : 8 * (long long)total_m >= total_v ? G : (third < m ? third : m);
