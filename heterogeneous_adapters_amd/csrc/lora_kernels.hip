@@ -955,8 +955,11 @@ struct ValuItem {
   int pg[kValuGroupBatch];
 };
 
+// Items per column block of a projection: Uv, plus the copy items when Y is
+// not Y_base; dUv divides by Uv (every column block of a batch without
+// tokens to copy).
 template <class E>
-__device__ __forceinline__ ValuItem fetch_valu_item(const KArgs& K, int i, int Uv, int ncopy) {
+__device__ __forceinline__ ValuItem fetch_valu_item(const KArgs& K, int i, int Uv, int ncopy, const FastDiv& dUv) {
   ValuItem it;
   int rem = i, p = 0;
   int Up = Uv + (K.p[0].Y != K.p[0].Yb ? ncopy : 0);
@@ -967,7 +970,7 @@ __device__ __forceinline__ ValuItem fetch_valu_item(const KArgs& K, int i, int U
   }
   const KProj& P = K.p[p];
   it.p = p;
-  it.jb = rem / Up;
+  it.jb = Up == Uv ? dUv.div(rem) : rem / Up;
   const int u = rem - it.jb * Up;
   it.copy = u >= Uv;
   if (it.copy) {
@@ -984,8 +987,13 @@ __device__ __forceinline__ ValuItem fetch_valu_item(const KArgs& K, int i, int U
     const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
     const int base = cld(P.b_indptr + it.d0.x) + ((it.jb * CB) >> K.pw_log2);
     const int G = rank_groups(it.d0.y);
+    const int32_t* pt = P.b_pages + base;
+    it.pg[0] = cld(pt);
 #pragma unroll
-    for (int g = 0; g < kValuGroupBatch; ++g) it.pg[g] = g < G ? cld(P.b_pages + base + g * ncolB) : 0;
+    for (int g = 1; g < kValuGroupBatch; ++g) {
+      it.pg[g] = 0;
+      if (g < G) it.pg[g] = cld(pt + g * ncolB);  // uniform
+    }
   }
   return it;
 }
@@ -1024,7 +1032,11 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
   // item = (part, chunk): chunks of one part are consecutive items, so they
   // run side by side on one XCD and re-read the part's B from its L2
   const int nch = valu_expand_chunks(d0.w);
-  const int part = item.local / nch, chunk = item.local - part * nch;
+  // part = local / nch with nch <= 8 and local < 32 (an MBGMV segment has
+  // under 16 tokens): (local + 1/2) / nch lies at least 1/16 from an
+  // integer, far beyond the reciprocal's error, so the floor is exact
+  const int part = (int)(((float)item.local + 0.5f) * __builtin_amdgcn_rcpf((float)nch));
+  const int chunk = item.local - part * nch;
   const int tb = chunk * kValuExpandTokens;
   const int t0 = d0.z + tb, n = min(kValuExpandTokens, d0.w - tb);
   const float scale = __int_as_float(d1.w) / (float)r;
@@ -1517,7 +1529,8 @@ __device__ __forceinline__ void expand_valu_items(const KArgs& K, Walk walk, con
                                                   float* vs, int lane, PhaseWait& sw) {
   const int i0 = walk.first();
   if (i0 < 0) return;
-  ValuItem cur = fetch_valu_item<E>(K, i0, Uv, ncopy);
+  const FastDiv dUv(Uv);
+  ValuItem cur = fetch_valu_item<E>(K, i0, Uv, ncopy, dUv);
   for (;;) {
     walk.issue();
     int ni = -1;
@@ -1525,12 +1538,12 @@ __device__ __forceinline__ void expand_valu_items(const KArgs& K, Walk walk, con
     if (cur.copy) {
       expand_copy<E>(K, K.p[cur.p], cur.jb, cur.local, pc.t_valid, pc.T, lane);
       ni = walk.resolve();
-      if (ni >= 0) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy);
+      if (ni >= 0) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy, dUv);
     } else {
       const bool fresh = !CO || sw.ready();
       expand_valu_body<E, WIDE, CO>(K, K.p[cur.p], cur, vs, lane, sw, fresh, [&]() {
         ni = walk.resolve();
-        if (ni >= 0) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy);
+        if (ni >= 0) nxt = fetch_valu_item<E>(K, ni, Uv, ncopy, dUv);
       });
       wave_sync();
     }

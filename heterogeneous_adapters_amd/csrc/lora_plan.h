@@ -56,6 +56,25 @@ constexpr int kValuSubBlocks = 4;
 LORA_HD inline int expand_cols(bool bf16) { return kValuSubBlocks * 64 * (bf16 ? 2 : 1); }
 
 LORA_HD inline int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+
+// Exact quotient n / d for 0 <= n < 2^31 and 1 <= d < 2^31: one multiply-
+// high, an add and a shift, with the divisor's multiplier m = floor(2^32 *
+// (2^s - d) / d) + 1, s = ceil(log2 d), built once (the round-up method of
+// division by invariant integers; n < 2^31 keeps mulhi(n, m) + n in 32 bits).
+// A run-time division is a long instruction sequence; this one is per item.
+struct FastDiv {
+  unsigned m;
+  int s;
+  LORA_HD FastDiv() : m(1u), s(0) {}
+  LORA_HD explicit FastDiv(int d) : m(1u), s(0) {
+    while ((1u << s) < (unsigned)d) ++s;
+    m = (unsigned)(((((unsigned long long)1) << 32) * ((((unsigned long long)1) << s) - (unsigned)d)) / (unsigned)d + 1u);
+  }
+  LORA_HD int div(int n) const {
+    const unsigned hi = (unsigned)(((unsigned long long)(unsigned)n * m) >> 32);
+    return (int)((hi + (unsigned)n) >> s);
+  }
+};
 LORA_HD inline int rank_groups(int r) { return (r + 15) >> 4; }
 
 LORA_HD inline bool is_mfma_segment(int n) { return n >= kMfmaMinTokens; }

@@ -1,7 +1,7 @@
 """Host check of the persistent grids' work walks (csrc/lora_plan.h): for
 every grid size and item totals tried, the waves' walks take every shrink and
-expand item exactly once, and the launch grid never exceeds the resident
-work-groups it is given.  The single-launch apply kernel relies on this: a
+expand item exactly once, the launch grid never exceeds the resident
+work-groups it is given, and the item decoder's divider is exact.  The single-launch apply kernel relies on this: a
 wave finishes all of its shrink items before it arrives at the phase
 barrier, so once every work-group of the grid has arrived, every shrink item
 (every partial sum of v) has been written.  Compiled with the host compiler
@@ -64,7 +64,26 @@ static void grid(int resident, long long bound) {
     ++bad;
   }
 }
+static void fastdiv(int d, int n) {
+  const FastDiv f(d);
+  if (f.div(n) != n / d) {
+    if (bad < 10) printf("FAIL FastDiv %d / %d = %d, want %d\n", n, d, f.div(n), n / d);
+    ++bad;
+  }
+}
 int main() {
+  for (int d = 1; d <= 3000; ++d) {
+    for (int n = 0; n <= 3 * d + 5; ++n) fastdiv(d, n);
+    for (int n : {1 << 20, (1 << 30) - 1, 1 << 30, 2147483647, 2147483647 - d, 2147483646}) fastdiv(d, n);
+  }
+  unsigned long long x = 88172645463325252ull;
+  for (int k = 0; k < 2000000; ++k) {  // xorshift draws of large divisors and dividends
+    x ^= x << 13; x ^= x >> 7; x ^= x << 17;
+    const int d = 1 + (int)((x >> 5) % 2147483647u), n = (int)((x >> 33) & 0x7fffffff);
+    fastdiv(d, n);
+    fastdiv(1 + (int)(x % 100000), n);
+  }
+  for (int d : {1, 2, 3, 7, 1 << 30, 2147483647}) fastdiv(d, 2147483647);
   for (int r = 0; r <= 2100; ++r)
     for (long long b : {-1LL, 0LL, 1LL, 5LL, 7LL, 8LL, 9LL, 100LL, 767LL, 768LL, 769LL, 2047LL, 5000LL, 1LL << 40})
       grid(r, b);
