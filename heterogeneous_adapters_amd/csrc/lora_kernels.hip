@@ -1529,7 +1529,7 @@ __device__ __forceinline__ void expand_valu_items(const KArgs& K, Walk walk, con
                                                   float* vs, int lane, PhaseWait& sw) {
   const int i0 = walk.first();
   if (i0 < 0) return;
-  const FastDiv dUv(Uv);
+  const FastDiv dUv(Uv > 0 ? Uv : 1);  // (Uv = 0: only copy items, divided by Up)
   ValuItem cur = fetch_valu_item<E>(K, i0, Uv, ncopy, dUv);
   for (;;) {
     walk.issue();
