@@ -1042,8 +1042,11 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
   const float scale = __int_as_float(d1.w) / (float)r;
   const int G = rank_groups(r);
   const int rs = G * 16;
-  const int nsub = kValuSubBlocks / valu_expand_parts(r);
-  const int ngb = NP / nsub;  // rank groups per batch of loads
+  // sub-blocks per part: 4, 2 or 1 for 1, 2 or more rank groups (as a shift:
+  // the pair index is split with shifts and masks, not run-time divisions)
+  const int nsh = G == 1 ? 2 : (G == 2 ? 1 : 0);
+  const int nsub = 1 << nsh;
+  const int ngb = NP >> nsh;  // rank groups per batch of loads
   const int pw = 1 << K.pw_log2;
   const int ncolB = (P.d_out + pw - 1) >> K.pw_log2;
   const int jblk = item.jb * (kValuSubBlocks * SUBW);
@@ -1069,7 +1072,7 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
     if constexpr (ONE_PAGE) {  // page ids are wave-uniform scalars: all 16 loads go out back to back
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        const int gi = i / nsub;
+        const int gi = i >> nsh;
         const int jcol = nsub == 4 ? jc[i] : (nsub == 2 ? jc[i & 1] : jc[0]);
         // a group past the adapter's has page id 0 here (never used)
         const T* pg = page_base<E>(K, gi == 0 ? pid0 : gi == 1 ? pid1 : gi == 2 ? pid2 : pid3, okp[i]);
@@ -1083,7 +1086,7 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
       const int base = cld(P.b_indptr + a);
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        const int g = min(g0 + i / nsub, G - 1);
+        const int g = min(g0 + (i >> nsh), G - 1);
         const int jcol = nsub == 4 ? jc[i] : (nsub == 2 ? jc[i & 1] : jc[0]);
         pl[i] = P.b_pages[base + g * ncolB + (jcol >> K.pw_log2)];
       }
@@ -1091,7 +1094,7 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
       for (int i = 0; i < NP; ++i) {
         const int jcol = nsub == 4 ? jc[i] : (nsub == 2 ? jc[i & 1] : jc[0]);
         const T* pg = page_base<E>(K, pl[i], okp[i]);
-        const bool up = r - 16 * (g0 + i / nsub) > 8;
+        const bool up = r - 16 * (g0 + (i >> nsh)) > 8;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           b[i][q] = ldg16(pg + b_off((jcol & (pw - 1)) + q / (16 / EPV), (q % (16 / EPV)) * EPV, pw, up));
@@ -1160,7 +1163,7 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
   auto mask_batch = [&](int g0) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int g = g0 + i / nsub;
+      const int g = g0 + (i >> nsh);
       if (g >= G) continue;
       uint4 (&w)[4] = b[i];
       if constexpr (ONE_PAGE) {
@@ -1212,9 +1215,9 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
       uint4 vv[4];  // v of the current group: bf16 ranks {0-7, 8-15}; fp32 ranks 0-15
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        const int g = g0 + i / nsub;
+        const int g = g0 + (i >> nsh);
         if (g >= G) continue;
-        if (i % nsub == 0) {  // first pair of a group: its v, once
+        if ((i & (nsub - 1)) == 0) {  // first pair of a group: its v, once
           if constexpr (EPV == 8) {
             const uint4* vt = reinterpret_cast<const uint4*>(reinterpret_cast<const uint32_t*>(vs) + t * (G * 8) + g * 8);
             vv[0] = vt[0];
