@@ -848,7 +848,7 @@ struct SplitStage {
   static constexpr int SF = M >= 8 ? 1 : 8 / M;  // slices per round
   float acc[M][2];
   float x[SF][M][2];
-  int e[M], kk[M], dst[M];
+  int e[M], kk[M];  // the pair's LDS slot is its index p0 + lane + 64 m
 };
 
 template <int M>
@@ -860,7 +860,6 @@ __device__ __forceinline__ void split_setup(SplitStage<M>& st, int p0, int np, i
     const int t = p / hp, kp = p - t * hp;  // pair kp = ranks 2kp, 2kp+1
     st.kk[m] = p < np ? 2 * kp : LORA_MAX_RANK;  // past the end: nothing loaded or stored
     st.e[m] = t * r + 2 * kp;
-    st.dst[m] = t * (G * 8) + kp;
     st.acc[m][0] = st.acc[m][1] = 0.0f;
   }
 }
@@ -890,11 +889,12 @@ __device__ __forceinline__ void split_add(SplitStage<M>& st) {
     }
 }
 
+// Pair p (token t, pair kp) goes to LDS dword t * (G * 8) + kp, which is p.
 template <int M>
-__device__ __forceinline__ void split_store(const SplitStage<M>& st, uint32_t* vs) {
+__device__ __forceinline__ void split_store(const SplitStage<M>& st, int p0, int lane, uint32_t* vs) {
 #pragma unroll
   for (int m = 0; m < M; ++m)
-    if (st.kk[m] < LORA_MAX_RANK) vs[st.dst[m]] = pack_bf2(st.acc[m][0], st.acc[m][1]);
+    if (st.kk[m] < LORA_MAX_RANK) vs[p0 + lane + 64 * m] = pack_bf2(st.acc[m][0], st.acc[m][1]);
 }
 
 template <int M, bool CO>
@@ -906,7 +906,7 @@ __device__ __forceinline__ void stage_v_split_pass(const KArgs& K, const KProj& 
     split_load<M, CO>(K, P, src, q, r, st);
     split_add<M>(st);
   }
-  split_store<M>(st, vs);
+  split_store<M>(st, p0, lane, vs);
 }
 
 template <bool CO>
@@ -1148,7 +1148,7 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
         split_load<1, CO>(K, P, vsrc, q, r, st1);
         split_add<1>(st1);
       }
-      split_store<1>(st1, reinterpret_cast<uint32_t*>(vs));
+      split_store<1>(st1, 0, lane, reinterpret_cast<uint32_t*>(vs));
       wave_sync();
     } else {
       stage_v_split<CO>(K, P, d1.x + tb * r, r, n, reinterpret_cast<uint32_t*>(vs), lane);
