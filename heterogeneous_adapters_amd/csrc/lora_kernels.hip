@@ -1142,8 +1142,18 @@ __device__ __forceinline__ void expand_valu_body(const KArgs& K, const KProj& P,
   if constexpr (CO) sw.wait(K);
   if constexpr (EPV == 8) {
     if (early) {
-      if (!fresh) split_load<1, CO>(K, P, vsrc, 0, r, st1);
-      split_add<1>(st1);
+      // Each path sums its own loads: summed after the paths join, the sum's
+      // wait would cover the longer path, and the early round (issued before
+      // the weights) would wait for every weight load too.  The empty asm
+      // statements keep the sums apart (the compiler does not merge them).
+      if (fresh) {
+        split_add<1>(st1);
+        asm volatile("" : "+v"(st1.acc[0][0]), "+v"(st1.acc[0][1]));
+      } else {
+        split_load<1, CO>(K, P, vsrc, 0, r, st1);
+        split_add<1>(st1);
+        asm volatile("" : "+v"(st1.acc[0][0]), "+v"(st1.acc[0][1]));
+      }
       for (int q = SplitStage<1>::SF; q < P.nv; q += SplitStage<1>::SF) {
         split_load<1, CO>(K, P, vsrc, q, r, st1);
         split_add<1>(st1);
