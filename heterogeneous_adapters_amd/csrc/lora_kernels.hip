@@ -699,8 +699,6 @@ __device__ __forceinline__ void shrink_items(const KArgs& K, Walk walk, int tota
     const int gg = shrink_item_groups(d0.w, d0.y);  // uniform
     if (gg == 2)
       shrink_mfma<E, WIDE, kMfmaShrinkTokensLong / 16, 2, CO>(K, K.p[p], q, d0, d1, u - d1.y, lane);
-    else if (gg == 4)
-      shrink_mfma<E, WIDE, kMfmaShrinkTokensShort / 16, 4, CO>(K, K.p[p], q, d0, d1, u - d1.y, lane);
     else
       shrink_mfma<E, WIDE, kMfmaShrinkTokensShort / 16, 1, CO>(K, K.p[p], q, d0, d1, u - d1.y, lane);
   }

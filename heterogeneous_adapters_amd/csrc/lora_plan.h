@@ -40,10 +40,9 @@ constexpr int kMfmaExpandTokens = 16;     // tokens per MBGMM expand item (one t
 // shared by the item's token tiles and each activation operand by its rank
 // groups.  Segments shorter than kMfmaLongSegment (a decode batch's hot
 // adapters, prefill chunks of a mixed batch): 32 tokens x 1 group.  Longer
-// ones (prefill sequences): 64 tokens x 2 groups for ranks up to 32, and
-// 32 tokens x 4 groups above, so that a token tile's activations are read
-// once per item for every rank up to 64 (the same accumulator and operand
-// registers either way).
+// ones (prefill sequences): 64 tokens x 2 groups, so that two of every three
+// operand loads in flight are activations (ranks above 32 take two items
+// per tile, which run side by side and meet the tile's activations in L2).
 constexpr int kMfmaShrinkTokensShort = 32, kMfmaShrinkTokensLong = 64, kMfmaLongSegment = 512;
 constexpr int kProjsPerLaunch = 16;       // projection descriptors per launch
 constexpr int kSegChunk = 1024;           // tokens per segment-builder block
@@ -89,7 +88,7 @@ LORA_HD inline int shrink_items_valu(int n, int r) {
   return is_mfma_segment(n) ? 0 : rank_groups(r) * ceil_div_i(n, kValuTokens);
 }
 LORA_HD inline int shrink_item_groups(int n, int r) {
-  return n < kMfmaLongSegment ? 1 : rank_groups(r) <= 2 ? 2 : 4;
+  return n < kMfmaLongSegment ? 1 : 2;
 }
 LORA_HD inline int shrink_tile_tokens(int n, int r) {
   return shrink_item_groups(n, r) == 2 ? kMfmaShrinkTokensLong : kMfmaShrinkTokensShort;
