@@ -148,10 +148,10 @@ _TILE_RANKS = [8, 16, 24, 32, 64, 128, 1, 40, 17, 96, 8, 16, 32, 64, 128]
 def _long_tile_ids():
     """Adapters 0-6 hold 511, 512, 513, 575, 576, 577 and 639 tokens (both
     sides of the segment length that switches the MBGMM shrink to its long
-    items, and of their 64-token tiles for ranks up to 32 and 32-token tiles
-    of four rank groups above: ranks 64, 128 and 40 sit on 576, 577 and 639
-    tokens), adapters 7-8 one and two (MBGMV), interleaved by a seeded
-    shuffle."""
+    items, and of their 64-token tiles of two rank groups: ranks 64, 128 and
+    40 sit on 576, 577 and 639 tokens, so a tile takes two, four and two
+    items, the last with one group past the rank), adapters 7-8 one and two
+    (MBGMV), interleaved by a seeded shuffle."""
     counts = [511, 512, 513, 575, 576, 577, 639, 1, 2]
     ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
     return np.random.default_rng(13).permutation(ids).astype(np.int32)
