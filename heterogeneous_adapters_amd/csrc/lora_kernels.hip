@@ -1357,12 +1357,16 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
   const int G = rank_groups(r);
   // page of each of this lane's K steps; a step past the last rank group
   // reads the last group and is zeroed by the rank mask
+  // A wave with no columns in the item (jend <= 0: past d_out in the item's
+  // last column block) looks up page column 0: its own column may lie past
+  // the adapter's last page column, i.e. past its row of the page table.
+  const int jpage = (jend > 0 ? j0 : 0) >> K.pw_log2;
   const T* pgk[NKS];
   bool okk[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const int g = min((ks * KSTEP + qq * EPV) >> 4, G - 1);
-    pgk[ks] = page_base<E>(K, one_page ? cld(P.b_pages + bbase + g * ncolB + (j0 >> K.pw_log2)) : 0, okk[ks]);
+    pgk[ks] = page_base<E>(K, one_page ? cld(P.b_pages + bbase + g * ncolB + jpage) : 0, okk[ks]);
   }
   auto load_part = [&](int part, uint4 (&bv)[CT][NKS], uint4 (&ybv)[ROUNDS], bool (&okc)[CT][NKS]) {
 #pragma unroll

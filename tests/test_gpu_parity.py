@@ -159,6 +159,13 @@ def _long_tile_ids():
 
 _LONG_TILE_RANKS = [8, 16, 24, 32, 64, 128, 40, 16, 64]
 
+
+def _last_adapter_long_ids():
+    """300 tokens of the last adapter (an MBGMM segment whose page-table row
+    is the table's last) among 100 spread over the others, shuffled."""
+    ids = np.concatenate([np.full(300, 4, np.int32), np.arange(100, dtype=np.int32) % 4])
+    return np.random.default_rng(17).permutation(ids).astype(np.int32)
+
 PARITY_CASES = {
     "cfg0": (0, {}),
     "cfg1": (1, {}),
@@ -172,6 +179,11 @@ PARITY_CASES = {
     "hot_segments": (2, dict(T=700, N=3, ranks_override=[8, 64, 128], page_width=512,
                              projs=(("a", 4096, 1032),))),
     "pw64_contig": (1, dict(T=96, N=5, page_width=64, projs=(("q", 512, 512),))),
+    # an output narrower than an MBGMM expand item's columns (4 waves x 128):
+    # two waves of each item have no columns, and their page column lies past
+    # the table row of the last adapter
+    "small_dout_last_adapter": (2, dict(N=5, ranks_override=[8, 16, 40, 64, 128], ids_override=_last_adapter_long_ids(),
+                                        page_width=256, scatter=False, projs=(("a", 648, 136),))),
     # segment lengths on both sides of the MBGMM tile sizes; page width 256 puts
     # the fp32 case on the wide kernel with MBGMM items as wide as a page
     "tile_lengths_bf16": (2, dict(N=15, ranks_override=_TILE_RANKS, ids_override=_tile_boundary_ids(),
@@ -735,3 +747,62 @@ def test_launch_modes_match_split_entry_points(k, mode):
     assert seg["flags"] == 0
     for p in range(w.n_projs):
         assert np.array_equal(Ya[p], Ys[p]), p
+
+
+def _random_case(seed):
+    """One seeded draw over the shapes the boundary admits: dtype, batch size
+    (decode sizes, the single-launch limit and beyond it), adapter count,
+    ranks 1-128 (multiples of 16 and ragged ones), page width, one to three
+    projections with ragged or wide dimensions (multiples of 8), pool layout,
+    base-only and out-of-range ids, and a run of one adapter long enough for
+    the MFMA path."""
+    rng = np.random.default_rng(5000 + seed)
+    dtype = "f32" if seed % 4 == 3 else "bf16"
+    T = int(rng.choice([1, 2, 7, 40, 130, 300, 700, 1500, 2100, 2600]))
+    N = int(rng.integers(1, 65))
+    ranks = np.where(rng.random(N) < 0.6, rng.choice([8, 16, 32, 64, 128], N),
+                     rng.integers(1, 129, N)).astype(np.int32)
+    pw = int(rng.choice([64, 128, 256, 512, 1024, 4096]))
+    nproj = int(rng.integers(1, 4))
+    # keep the oracle's work (tokens x rank x dims) to a few seconds
+    dmax = 4096 if T <= 700 else 1536
+    projs = tuple((f"p{i}", 8 * int(rng.integers(1, dmax // 8 + 1)), 8 * int(rng.integers(1, dmax // 8 + 1)))
+                  for i in range(nproj))
+    p_ad = rng.dirichlet(np.full(N, 0.3))
+    ids = rng.choice(N, size=T, p=p_ad).astype(np.int32)
+    if T >= 40:  # a run of one adapter: an MBGMM segment (or a long one)
+        n_long = int(rng.integers(16, max(17, T // 2)))
+        ids[rng.choice(T, n_long, replace=False)] = int(rng.integers(0, N))
+    special = rng.random(T)
+    ids[special < 0.05] = -1                    # base-only tokens
+    ids[(special >= 0.05) & (special < 0.07)] = N + 3  # out of range: excluded and counted
+    mode = [lora.LORA_LAUNCH_AUTO, lora.LORA_LAUNCH_SINGLE, lora.LORA_LAUNCH_TWO][seed % 3]
+    kw = dict(T=T, N=N, dtype=dtype, page_width=pw, projs=projs, scatter=bool(seed % 2), seed=100 + seed,
+              ids_override=ids, ranks_override=ranks)
+    return kw, mode
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes_match_oracle(seed):
+    """Seeded random draws (see _random_case) through lora_apply in a drawn
+    launch mode, against the oracle: segments bit-exact, Y within the mode's
+    tolerance, rows of base-only and excluded tokens equal to Y_base."""
+    kw, mode = _random_case(seed)
+    print(f"random case {seed}: T={kw['T']} N={kw['N']} dtype={kw['dtype']} pw={kw['page_width']} "
+          f"projs={[p[1:] for p in kw['projs']]} ranks<= {int(kw['ranks_override'].max())} mode={mode}", flush=True)
+    w = W.make_workload(2, kw, keep_dense=False)
+    try:
+        lora.lora_set_launch_mode(mode)
+        Ys, seg = gpu_apply(w)
+    finally:
+        lora.lora_set_launch_mode(lora.LORA_LAUNCH_AUTO)
+    check_segments(seg, oracle.segments(w.ids, w.ranks))
+    base = (w.ids < 0) | (w.ids >= w.N)
+    for p in range(w.n_projs):
+        ref = oracle_Y(w, p)
+        got = W.as_f64(Ys[p], w.dtype)
+        assert np.isfinite(got).all()
+        err = rowwise_rel(got, W.as_f64(ref, w.dtype))
+        print(f"  proj {p}: rowwise rel err {err:.3e}", flush=True)
+        assert err < TOL[w.dtype]
+        assert np.array_equal(got[base], W.as_f64(w.Y_base[p], w.dtype)[base])
