@@ -26,10 +26,22 @@ def rowwise_rel(Y, Yref):
     return float((np.abs(Y - Yref).max(axis=1) / den).max())
 
 
+def fence_tables(b, num_pages):
+    """Give each page table a tail of ids past the pool, read through views of
+    the table's own length, so that a read past a table's end takes such an
+    id and raises LORA_FLAG_PAGE_RANGE (which every parity case checks)."""
+    def fenced(t):
+        f = torch.full((t.numel() + 64,), num_pages + 7, dtype=t.dtype, device=t.device)
+        f[:t.numel()] = t
+        return f[:t.numel()]
+    b.tables = [(ai, fenced(ap), bi, fenced(bp)) for ai, ap, bi, bp in b.tables]
+
+
 def gpu_apply(w, in_place=False, pool=None, ids=None, via="apply"):
     """Run the whole branch on the GPU; returns host Y per projection and
-    the segment arrays."""
+    the segment arrays.  Page tables are fenced (fence_tables)."""
     b = batch.to_device(w, pool=pool)
+    fence_tables(b, w.num_pages)
     if ids is not None:
         b.ids = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
     segs = lora.Segments(w.T, w.N)
