@@ -818,3 +818,81 @@ def test_random_shapes_match_oracle(seed):
         print(f"  proj {p}: rowwise rel err {err:.3e}", flush=True)
         assert err < TOL[w.dtype]
         assert np.array_equal(got[base], W.as_f64(w.Y_base[p], w.dtype)[base])
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_layouts_match_contiguous(seed):
+    """Seeded random draws run twice: contiguous rows through lora_apply
+    (itself checked against the oracle by the draws above), and again with
+    every layout option the boundary offers drawn at random -- rows inside
+    wider tensors (ldx, ldyb, ldy), Y written in place over Y_base, one X
+    tensor shared by projections of equal d_in, and the entry point
+    (lora_apply in a drawn launch mode, or lora_shrink + lora_expand for the
+    group or per projection).  Y must be bit-identical, and no column outside
+    the rows' slices may be written."""
+    kw, mode = _random_case(200 + seed)
+    rng = np.random.default_rng(9000 + seed)
+    share = bool(rng.integers(0, 2)) and len(kw["projs"]) > 1
+    if share:
+        d_in = kw["projs"][0][1]
+        kw["projs"] = tuple((n, d_in, do) for n, _, do in kw["projs"])
+    in_place = bool(rng.integers(0, 2))
+    via = ["apply", "split_group", "split_each"][int(rng.integers(0, 3))]
+    pads = [8 * int(rng.integers(0, 5)) for _ in range(3)]  # extra columns of X, Y_base and Y rows
+    print(f"layout case {seed}: T={kw['T']} N={kw['N']} {kw['dtype']} pw={kw['page_width']} "
+          f"projs={[p[1:] for p in kw['projs']]} share={share} in_place={in_place} via={via} pads={pads} "
+          f"mode={mode}", flush=True)
+    w = W.make_workload(2, kw, keep_dense=False)
+    if share:  # one activation for every projection, in the reference run as well (as separate copies)
+        w.X = [w.X[0]] * w.n_projs
+    Yref, _ = gpu_apply(w)
+    for p in range(w.n_projs):  # the contiguous run against the oracle as well
+        assert rowwise_rel(W.as_f64(Yref[p], w.dtype), W.as_f64(oracle_Y(w, p), w.dtype)) < TOL[w.dtype]
+    b = batch.to_device(w)
+    fence_tables(b, w.num_pages)
+    T, dt, P = w.T, b.X[0].dtype, w.n_projs
+    d_ins = [t.d_in for t in w.tables]
+    d_outs = [t.d_out for t in w.tables]
+    off = 8 if pads[0] else 0
+    if share:
+        Xs = torch.zeros(T, d_ins[0] + pads[0], dtype=dt, device="cuda")
+        Xs[:, off:off + d_ins[0]] = b.X[0]
+        Xv = [Xs[:, off:off + d_ins[0]]] * P
+    else:
+        Xw = [torch.zeros(T, d_ins[p] + pads[0], dtype=dt, device="cuda") for p in range(P)]
+        for p in range(P):
+            Xw[p][:, off:off + d_ins[p]] = b.X[p]
+        Xv = [Xw[p][:, off:off + d_ins[p]] for p in range(P)]
+    Ybw = [torch.empty(T, d_outs[p] + pads[1], dtype=dt, device="cuda") for p in range(P)]
+    for p in range(P):
+        Ybw[p][:, :d_outs[p]] = b.Y_base[p]
+    Yw = [torch.full((T, d_outs[p] + pads[2]), 5.0, dtype=dt, device="cuda") for p in range(P)]
+    Ybv = [Ybw[p][:, :d_outs[p]] for p in range(P)]
+    outv = Ybv if in_place else [Yw[p][:, :d_outs[p]] for p in range(P)]
+    projs = [lora.Proj(Xv[p], Ybv[p], outv[p], *b.tables[p]) for p in range(P)]
+    segs = lora.Segments(T, w.N)
+    ws = lora.workspace(T, w.N, P, max(d_ins))
+    stride = max(T, 1) * lora.LORA_MAX_RANK
+    try:
+        lora.lora_set_launch_mode(mode)
+        if via == "apply":
+            lora.lora_apply(b.ids, segs, T, projs, b.adapters, b.pool, ws)
+        else:
+            lora.lora_build_segments(b.ids, b.adapters, segs, ws)
+            vs = [torch.empty(lora.lora_v_slices(d) * stride, dtype=torch.float32, device="cuda") for d in d_ins]
+            if via == "split_group":
+                lora.lora_shrink(projs, b.adapters, segs, b.pool, vs, stride)
+                lora.lora_expand(projs, b.adapters, segs, b.pool, vs, 0, stride)
+            else:
+                for p in range(P):
+                    lora.lora_shrink(projs[p], b.adapters, segs, b.pool, vs[p], stride)
+                    lora.lora_expand(projs[p], b.adapters, segs, b.pool, vs[p], lora.lora_v_slices(d_ins[p]), stride)
+        torch.cuda.synchronize()
+    finally:
+        lora.lora_set_launch_mode(lora.LORA_LAUNCH_AUTO)
+    assert segs.arrays()["flags"] == 0
+    for p in range(P):
+        got = batch.device_to_host(outv[p])
+        assert np.array_equal(got, Yref[p]), p
+        if not in_place and pads[2]:
+            assert bool((Yw[p][:, d_outs[p]:].float() == 5.0).all()), p
