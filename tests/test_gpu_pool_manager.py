@@ -75,6 +75,60 @@ def test_managed_pool_batches_match_full_pool(dtype):
     assert mp.evictions > 0 and mp.misses > 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_managed_pool_async_serving_loop(dtype):
+    """A serving loop with no synchronisation between batches: each batch's
+    adapters are made resident (uploads on the pool's side stream, evicting
+    adapters that earlier batches still being computed read), its lora_apply
+    is enqueued on the compute stream, and its adapters are unpinned at once.
+    Every batch's Y, checked after one final synchronisation, equals the same
+    batch run on the generator's full pool, bit for bit."""
+    ranks = [8, 16, 64, 24, 32, 8, 1, 40, 128, 16, 64, 8]
+    w = W.make_workload(2, dict(T=96, N=len(ranks), ranks_override=ranks, page_width=512, dtype=dtype,
+                                projs=(("a", 1024, 768), ("b", 768, 1096))))
+    tier = host_tier_from_pool(_host_pool_tensor(w), w.tables, w.N)
+    cap = 64
+    mp = ManagedPool([(t.a_indptr, t.b_indptr) for t in w.tables], tier, w.page_width, capacity=cap)
+    sizes = [mp.n_pages(a) for a in range(w.N)]
+    full = batch.to_device(w)
+    rng = np.random.default_rng(23)
+    stream = torch.cuda.current_stream()
+    kept = []  # per batch: its ids, both Y sets and both segment buffers (alive until the final check)
+    for step in range(20):
+        order = rng.permutation(w.N)
+        chosen, used = [], 0
+        for a in order:
+            if used + sizes[a] <= cap and len(chosen) < 3:
+                chosen.append(int(a))
+                used += sizes[a]
+        ids = torch.from_numpy(rng.choice(np.asarray(chosen + [-1], np.int32), size=w.T).astype(np.int32)).cuda()
+        mp.ensure(chosen, stream)
+        out = {}
+        for which in ("managed", "full"):
+            Y = [torch.empty_like(y) for y in full.Y_base]
+            if which == "managed":
+                projs = [mp.proj(p, full.X[p], full.Y_base[p], Y[p]) for p in range(w.n_projs)]
+                pool = mp.pool
+            else:
+                projs = [lora.Proj(full.X[p], full.Y_base[p], Y[p], *full.tables[p]) for p in range(w.n_projs)]
+                pool = full.pool
+            segs = lora.Segments(w.T, w.N)
+            ws = lora.workspace(w.T, w.N, w.n_projs, max(t.d_in for t in w.tables))
+            lora.lora_apply(ids, segs, w.T, projs, full.adapters, pool, ws)
+            out[which] = (Y, segs, ws)
+        mp.unpin(chosen)
+        kept.append((step, chosen, ids, out))
+    torch.cuda.synchronize()
+    assert mp.evictions > 0 and mp.misses > 0
+    for step, chosen, _, out in kept:
+        for which in ("managed", "full"):
+            assert int(out[which][1].counts().cpu()[lora.COUNT_FLAGS]) == 0, (step, which)
+        for p in range(w.n_projs):
+            got = batch.device_to_host(out["managed"][0][p])
+            want = batch.device_to_host(out["full"][0][p])
+            assert np.array_equal(got, want), (step, chosen, p)
+
+
 def test_upload_coalesces_runs_and_scatters():
     """lora_upload_pages to scattered and consecutive page ids: every page
     lands where its id says, the other pages are untouched."""
