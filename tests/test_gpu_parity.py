@@ -896,3 +896,43 @@ def test_random_layouts_match_contiguous(seed):
         assert np.array_equal(got, Yref[p]), p
         if not in_place and pads[2]:
             assert bool((Yw[p][:, d_outs[p]:].float() == 5.0).all()), p
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_graph_replays_match_eager(seed):
+    """Seeded random draws (as test_random_shapes_match_oracle, in a drawn
+    launch mode) captured in a HIP graph with their segment build: three
+    replays, with eager work and a synchronisation before each, all equal the
+    eager run bit for bit."""
+    kw, mode = _random_case(440 + seed)  # batches of 7 to 2100 tokens, one and two launches
+    print(f"graph case {seed}: T={kw['T']} N={kw['N']} {kw['dtype']} pw={kw['page_width']} "
+          f"projs={[p[1:] for p in kw['projs']]} mode={mode}", flush=True)
+    w = W.make_workload(2, kw, keep_dense=False)
+    try:
+        lora.lora_set_launch_mode(mode)
+        Yref, _ = gpu_apply(w)
+        b = batch.to_device(w)
+        fence_tables(b, w.num_pages)
+        segs = lora.Segments(w.T, w.N)
+        projs = [b.proj(p) for p in range(w.n_projs)]
+        ws = lora.workspace(w.T, w.N, w.n_projs, max(t.d_in for t in w.tables))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            lora.lora_apply(b.ids, segs, w.T, projs, b.adapters, b.pool, ws, side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            lora.lora_apply(b.ids, segs, w.T, projs, b.adapters, b.pool, ws, side)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for y in b.Y:
+                y.fill_(7.0)  # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert segs.arrays()["flags"] == 0, rep
+            for p in range(w.n_projs):
+                assert np.array_equal(batch.device_to_host(b.Y[p]), Yref[p]), (rep, p)
+    finally:
+        lora.lora_set_launch_mode(lora.LORA_LAUNCH_AUTO)
