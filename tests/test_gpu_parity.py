@@ -26,12 +26,13 @@ def rowwise_rel(Y, Yref):
     return float((np.abs(Y - Yref).max(axis=1) / den).max())
 
 
-def fence_tables(b, num_pages):
-    """Give each page table a tail of ids past the pool, read through views of
-    the table's own length, so that a read past a table's end takes such an
-    id and raises LORA_FLAG_PAGE_RANGE (which every parity case checks)."""
+def fence_tables(b):
+    """Give each page table a tail of ids past any pool (INT32_MAX), read
+    through views of the table's own length, so that a read past a table's
+    end takes such an id and raises LORA_FLAG_PAGE_RANGE (which every parity
+    case checks)."""
     def fenced(t):
-        f = torch.full((t.numel() + 64,), num_pages + 7, dtype=t.dtype, device=t.device)
+        f = torch.full((t.numel() + 64,), 2 ** 31 - 1, dtype=t.dtype, device=t.device)
         f[:t.numel()] = t
         return f[:t.numel()]
     b.tables = [(ai, fenced(ap), bi, fenced(bp)) for ai, ap, bi, bp in b.tables]
@@ -41,7 +42,7 @@ def gpu_apply(w, in_place=False, pool=None, ids=None, via="apply"):
     """Run the whole branch on the GPU; returns host Y per projection and
     the segment arrays.  Page tables are fenced (fence_tables)."""
     b = batch.to_device(w, pool=pool)
-    fence_tables(b, w.num_pages)
+    fence_tables(b)
     if ids is not None:
         b.ids = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
     segs = lora.Segments(w.T, w.N)
@@ -849,7 +850,7 @@ def test_random_layouts_match_contiguous(seed):
     for p in range(w.n_projs):  # the contiguous run against the oracle as well
         assert rowwise_rel(W.as_f64(Yref[p], w.dtype), W.as_f64(oracle_Y(w, p), w.dtype)) < TOL[w.dtype]
     b = batch.to_device(w)
-    fence_tables(b, w.num_pages)
+    fence_tables(b)
     T, dt, P = w.T, b.X[0].dtype, w.n_projs
     d_ins = [t.d_in for t in w.tables]
     d_outs = [t.d_out for t in w.tables]
@@ -912,7 +913,7 @@ def test_random_graph_replays_match_eager(seed):
         lora.lora_set_launch_mode(mode)
         Yref, _ = gpu_apply(w)
         b = batch.to_device(w)
-        fence_tables(b, w.num_pages)
+        fence_tables(b)
         segs = lora.Segments(w.T, w.N)
         projs = [b.proj(p) for p in range(w.n_projs)]
         ws = lora.workspace(w.T, w.N, w.n_projs, max(t.d_in for t in w.tables))
