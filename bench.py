@@ -193,6 +193,40 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
+def derived_counter_lines(per):
+    """Ratios of counters read in one pass, per kernel (mean over dispatches):
+    instructions per wave (SQ_INSTS_* / SQ_WAVES), the L2 read latency seen
+    by the vector caches (TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ, in
+    cycles), the share of L2 cycles with reads to DRAM stalled for credits,
+    reads to DRAM in flight per L2 channel (RDREQ_LEVEL / TCC_CYCLE, both
+    summed over the channels), and the L2 hit rate."""
+    import numpy as np
+    mean = {}
+    for (name, ctr), disp in per.items():
+        mean.setdefault(name, {})[ctr] = float(np.mean(list(disp.values())))
+    out = []
+    for name, m in sorted(mean.items()):
+        if "lora::" not in name and "neg_kernel" not in name:
+            continue
+        short = name[:90]
+        ratios = []
+        if m.get("SQ_WAVES"):
+            for ctr in sorted(c for c in m if c.startswith("SQ_INSTS_")):
+                ratios.append((f"per_wave_{ctr[9:].lower()}", m[ctr] / m["SQ_WAVES"]))
+        if m.get("TCP_TCC_READ_REQ_sum"):
+            if "TCP_TCC_READ_REQ_LATENCY_sum" in m:
+                ratios.append(("l2_read_latency_cycles", m["TCP_TCC_READ_REQ_LATENCY_sum"] / m["TCP_TCC_READ_REQ_sum"]))
+        if m.get("TCC_CYCLE_sum"):
+            if "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum" in m:
+                ratios.append(("dram_credit_stall_share", m["TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum"] / m["TCC_CYCLE_sum"]))
+            if "TCC_EA0_RDREQ_LEVEL_sum" in m:
+                ratios.append(("dram_reads_in_flight_per_channel", m["TCC_EA0_RDREQ_LEVEL_sum"] / m["TCC_CYCLE_sum"]))
+        if m.get("TCC_HIT_sum", 0) + m.get("TCC_MISS_sum", 0) > 0 and "TCC_HIT_sum" in m and "TCC_MISS_sum" in m:
+            ratios.append(("l2_hit_rate", m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"])))
+        out.extend(f"{key} {val:.4g}  {short}" for key, val in ratios)
+    return out
+
+
 def summarize_profile(dirs, command):
     """Text summary of rocprofv3 CSV output under the directories in dirs
     (kernel stats, and/or FETCH_SIZE / WRITE_SIZE counter runs that end with
@@ -216,12 +250,16 @@ def summarize_profile(dirs, command):
     per = {}
     for path in found("*counter_collection.csv"):
         for r in _read_csv(path):
+            # a dispatch is (file, id): ids restart in every profiled run, and
+            # a counter read in several runs must not add up across them
+            # (within one run, the rows of one dispatch's counter are summed)
             d = per.setdefault((r["Kernel_Name"], r["Counter_Name"]), {})
-            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+            key = (path, r["Dispatch_Id"])
+            d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
     if per:
         calib = {}
         for (name, ctr), disp in per.items():
-            if "neg_kernel" in name:
+            if "neg_kernel" in name and ctr in ("FETCH_SIZE", "WRITE_SIZE"):  # the byte counters (KiB)
                 calib[ctr] = (CALIB_BYTES / 1024) / float(np.median(list(disp.values())))
         lines.append("counters (rocprofv3 --pmc), per dispatch as read (FETCH_SIZE and WRITE_SIZE in KiB)"
                      + (f"; calibration: a plain elementwise copy (torch.neg) of {CALIB_BYTES >> 20} MiB fp32 reads "
@@ -239,6 +277,7 @@ def summarize_profile(dirs, command):
             if "lora::" in name and ctr in ("MfmaUtil", "MfmaFlopsBF16"):
                 key = "mfma_util_pct" if ctr == "MfmaUtil" else "mfma_bf16_flops_per_dispatch"
                 lines.append(f"{key} {float(np.mean(list(disp.values()))):.4g}  {name[:90]}")
+        lines.extend(derived_counter_lines(per))
         for kname, key in ((APPLY_KERNEL, "apply"), (SHRINK_KERNEL, "shrink"), (EXPAND_KERNEL, "expand")):
             tot, have = 0.0, 0
             for (name, ctr), disp in per.items():

@@ -110,6 +110,55 @@ def test_summary_of_kernel_stats_and_mfma_counters(tmp_path, capsys):
     assert "lora::" in out and "neg_kernel" not in out.split("kernel stats")[1].split("counters")[0]
 
 
+def test_derived_counter_ratios():
+    """Per-wave instruction counts, L2 read latency, credit-stall share, reads
+    in flight per channel and hit rate, from the per-dispatch counter means
+    of each kernel (two dispatches of the apply kernel averaged)."""
+    per = {
+        (APPLY, "SQ_WAVES"): {1: 3000.0, 2: 3000.0},
+        (APPLY, "SQ_INSTS_VALU"): {1: 6.0e6, 2: 12.0e6},
+        (APPLY, "SQ_INSTS_SALU"): {1: 3.0e6, 2: 3.0e6},
+        (APPLY, "TCP_TCC_READ_REQ_LATENCY_sum"): {1: 2.0e9},
+        (APPLY, "TCP_TCC_READ_REQ_sum"): {1: 1.0e6},
+        (APPLY, "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum"): {1: 50.0},
+        (APPLY, "TCC_EA0_RDREQ_LEVEL_sum"): {1: 1.0e7},
+        (APPLY, "TCC_CYCLE_sum"): {1: 1.0e5},
+        (APPLY, "TCC_HIT_sum"): {1: 600.0},
+        (APPLY, "TCC_MISS_sum"): {1: 400.0},
+        ("some::other_kernel()", "SQ_WAVES"): {1: 1.0},
+    }
+    got = {line.split()[0]: float(line.split()[1]) for line in bench.derived_counter_lines(per)}
+    assert got == {"per_wave_salu": 1000.0, "per_wave_valu": 3000.0, "l2_read_latency_cycles": 2000.0,
+                   "dram_credit_stall_share": 5e-4, "dram_reads_in_flight_per_channel": 100.0, "l2_hit_rate": 0.6}
+
+
+def test_counter_read_in_two_runs_is_averaged_not_added(tmp_path, capsys):
+    """Dispatch ids restart in every profiled run: SQ_WAVES read in two runs
+    (dispatch 1 in each) averages to its value, and per-wave ratios use it."""
+    for i, ctr in enumerate(("SQ_INSTS_VALU", "SQ_INSTS_SALU")):
+        d = tmp_path / f"run{i}"
+        d.mkdir()
+        _write_csv(d / "r_counter_collection.csv", ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"],
+                   [[1, APPLY, "SQ_WAVES", 3000.0], [1, APPLY, ctr, 6e6 * (i + 1)]])
+    bench.summarize_profile([str(tmp_path / "run0"), str(tmp_path / "run1")], "")
+    out = capsys.readouterr().out
+    assert f"per_wave_valu 2000  {APPLY}" in out and f"per_wave_salu 4000  {APPLY}" in out
+
+
+def test_only_byte_counters_are_calibrated(tmp_path, capsys):
+    """Counters other than FETCH_SIZE / WRITE_SIZE read on the calibration
+    copy are reported as read, never turned into bytes."""
+    d = tmp_path / "prof"
+    d.mkdir()
+    _write_csv(d / "c_counter_collection.csv", ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"],
+               [[1, COPY, "TCC_CYCLE_sum", 1e6], [2, APPLY, "TCC_CYCLE_sum", 5e5],
+                [1, COPY, "TCC_HIT_sum", 10.0], [2, APPLY, "TCC_HIT_sum", 3.0]])
+    bench.summarize_profile([str(d)], "")
+    out = capsys.readouterr().out
+    assert "_scale" not in out and "bytes_per_launch" not in out
+    assert "TCC_CYCLE_sum" in out
+
+
 def test_kernel_hash_ignores_comments_but_not_code(tmp_path):
     for rel in bench.KERNEL_SOURCES:
         os.makedirs(tmp_path / os.path.dirname(rel), exist_ok=True)
