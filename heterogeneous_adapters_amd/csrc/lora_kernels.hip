@@ -1447,12 +1447,19 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f4*>(cw + li * LDC + ct * 16 + qq * 4) = acc[ct];
     wave_sync();
-    const int colp = part * PART + ch * EPC;
+    // Every lane stores, so the loop has no conditional store: a store
+    // skipped on some paths makes the compiler wait for every store at the
+    // part's end (vmcnt(0)) before the next part's operands count as
+    // arrived.  A lane past the tile's tokens takes the last token's row and
+    // a lane past the wave's columns the last chunk (as its Y_base load
+    // did): its value and address are those of a lane inside, so the
+    // duplicate writes are identical.
+    const int colp = min(part * PART + ch * EPC, jend - EPC);  // jend is a multiple of 8
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd) {
-      const int tk = rd * TPR + lane / CPR;
-      if (tk < nt && colp < jend) {
-        const float* c = cw + tk * LDC + ch * EPC;
+      const int tk = min(rd * TPR + lane / CPR, nt - 1);
+      {
+        const float* c = cw + tk * LDC + (colp - part * PART);
         uint4 out;
         if constexpr (EPC == 8) {
           const f4 c0 = *reinterpret_cast<const f4*>(c), c1 = *reinterpret_cast<const f4*>(c + 4);
