@@ -1315,10 +1315,10 @@ constexpr int kExpandRowFloats = kMfmaExpandTokens * (LORA_MAX_RANK + 4);
 // ranks of an output column contiguously, so each lane's operand is one
 // 16-byte load, and a lane's four C values are four adjacent columns of one
 // token (one 8- or 16-byte Y access).
-template <class E, int NKS, bool WIDE, bool CO>
+template <class E, int NKS, bool WIDE, bool CO, class Next>
 __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P, int j0, int jend, int wc, int a,
                                                  int r, int t0, int nt, float scale, float* vs, float* cw, int voff,
-                                                 int tb, int lane) {
+                                                 int tb, int lane, Next&& next) {
   typedef typename E::T T;
   constexpr int EPV = E::kEpv;
   constexpr int KSTEP = 4 * EPV;
@@ -1421,6 +1421,7 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
     stage_v_rows<kThreads, CO>(K, P, voff, r, tb, nt, vs, threadIdx.x);
   }
   __syncthreads();
+  next();  // the block's next item, requested while this one runs
   uint4 vv[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
@@ -1495,10 +1496,12 @@ __device__ __forceinline__ void expand_mfma_body(const KArgs& K, const KProj& P,
 
 // MBGMM expand item (one block): (segment, 16-token tile, 4*wc columns).  The
 // block stages v of the tile once into shared LDS rows; wave w then produces
-// columns [w*wc, (w+1)*wc) of the item.
-template <class E, bool WIDE, bool CO>
+// columns [w*wc, (w+1)*wc) of the item.  next() runs once v is staged,
+// publish() just before the block's last barrier of the item.
+template <class E, bool WIDE, bool CO, class Next, class Publish>
 __device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int jb, int wc, int4 d0, int4 d1,
-                                            int local, float* vs, float* cw, int wave, int lane) {
+                                            int local, float* vs, float* cw, int wave, int lane, Next&& next,
+                                            Publish&& publish) {
   constexpr int KSTEP = 4 * E::kEpv;
   constexpr int MAXKS = LORA_MAX_RANK / KSTEP;
   const int a = d0.x, r = d0.y;
@@ -1512,11 +1515,27 @@ __device__ __forceinline__ void expand_mfma(const KArgs& K, const KProj& P, int 
   // every rank; the choice is the same for the whole block (one segment)
   const int nks = ceil_div_i(r, KSTEP);
   if (WIDE && nks <= MAXKS / 4)  // bf16: one K step (r <= 32), so twice the columns per part
-    expand_mfma_body<E, MAXKS / 4, WIDE, CO>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
+    expand_mfma_body<E, MAXKS / 4, WIDE, CO>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane, next);
   else if (nks <= MAXKS / 2)
-    expand_mfma_body<E, MAXKS / 2, WIDE, CO>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
-  else expand_mfma_body<E, MAXKS, WIDE, CO>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane);
+    expand_mfma_body<E, MAXKS / 2, WIDE, CO>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane, next);
+  else expand_mfma_body<E, MAXKS, WIDE, CO>(K, P, j0, jend, wc, a, r, t0, nt, scale, vs, cw, d1.x, tb, lane, next);
+  publish();
   __syncthreads();  // the rows are restaged by the block's next item
+}
+
+// Item index i of the MBGMM expand list -> (projection p, column block jb,
+// item u of the segment tables); nb(p) is the column blocks of projection p.
+__device__ __forceinline__ void expand_mfma_item(const KArgs& K, int i, int wc, int Um, int& p, int& jb, int& u) {
+  int rem = i;
+  p = 0;
+  int nb = ceil_div_i(K.p[0].d_out, kWaves * wc);
+  while (rem >= nb * Um) {
+    rem -= nb * Um;
+    ++p;
+    nb = ceil_div_i(K.p[p].d_out, kWaves * wc);
+  }
+  jb = rem / Um;
+  u = rem - jb * Um;
 }
 
 // Rows of tokens without an adapter: Y = Y_base (only when Y is not Y_base),
@@ -1595,30 +1614,76 @@ __device__ __forceinline__ void expand_phase(const KArgs& K, const PlanCounts& p
   for (int p = 0; p < K.np; ++p) total_v += K.p[p].njs * (Uv + (K.p[p].Y != K.p[p].Yb ? ncopy : 0));
   int total = 0, wc = 0;
   if (Um > 0) wc = expand_mfma_cols(K.np, [&](int p) { return K.p[p].d_out; }, K.pw_log2, Um, grid, total);
-  const ExpandSplit es = expand_walk_split(total, total_v, grid, block);
-  if (Um > 0) {
-    // apply kernel: the block's MBGMM items read v from their start (the
-    // tile's staging overlaps its first B loads), so their waves wait for
-    // the phase barrier before the first one
-    if constexpr (CO) {
-      if (es.first < es.end_m) sw.wait(K);
-    }
-    for (int i = es.first; i < es.end_m; i += es.step) {
-      int rem = i, p = 0;
-      int nb = ceil_div_i(K.p[0].d_out, kWaves * wc);
-      while (rem >= nb * Um) {
-        rem -= nb * Um;
-        ++p;
-        nb = ceil_div_i(K.p[p].d_out, kWaves * wc);
+  // The expand kernel with at least kQueueItems MBGMM items per work-group
+  // of the grid (prefill batches) takes them from per-XCD queues; otherwise
+  // (and always in the apply kernel, whose phase barrier holds the grid) the
+  // items of an XCD's part go round robin.
+  constexpr int kQueueItems = 3;
+  if (CO || !(Um > 0 && 8LL * total >= total_v && total >= kQueueItems * grid)) {
+    // each XCD takes a contiguous part of the list (for a decode batch,
+    // whole column blocks: every XCD reads its own columns of B)
+    const ExpandSplit es = expand_walk_split(total, total_v, grid, block);
+    if (Um > 0) {
+      // apply kernel: the block's MBGMM items read v from their start (the
+      // tile's staging overlaps its first B loads), so their waves wait for
+      // the phase barrier before the first one
+      if constexpr (CO) {
+        if (es.first < es.end_m) sw.wait(K);
       }
-      const int jb = rem / Um;
-      const int u = rem - jb * Um;
-      const int s = cld(K.exp_item_m + u);
-      const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
-      expand_mfma<E, WIDE, CO>(K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[kWaves], vs_all[wave], wave, lane);
+      for (int i = es.first; i < es.end_m; i += es.step) {
+        int p, jb, u;
+        expand_mfma_item(K, i, wc, Um, p, jb, u);
+        const int s = cld(K.exp_item_m + u);
+        const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
+        expand_mfma<E, WIDE, CO>(K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[kWaves], vs_all[wave], wave, lane,
+                                 [] {}, [] {});
+      }
     }
+    expand_valu_items<E, WIDE, CO>(K, StaticWalk(total_v, es.Gm * kWaves, es.R, wave), pc, Uv, ncopy, vs, lane, sw);
+  } else {
+    // Queues: the items go to the XCDs in blocks of consecutive items dealt
+    // round robin (an eighth of the list per XCD would tie an XCD's load to
+    // the ranks of the segments there).  Work-group beta of an XCD starts
+    // with its item beta; later items come from the XCD's queue, one at a
+    // time per work-group, so that blocks that drew slow items (high rank)
+    // take fewer of them.  Thread 0 takes the next ticket while the current
+    // item runs and hands it to the block through LDS.  Every work-group of
+    // the grid takes part (Gm = the XCD's work-groups).
+    const QueueSplit qs = expand_queue_split(total, total_v, grid, block);
+    if (qs.beta < qs.Gm) {
+      __shared__ int ticket;
+      const int sh = xcd_shift(grid);
+      int* tq = K.sync + queue_line(qs.x);
+      int* dq = K.sync + queue_line(8 + qs.x);
+      int t = qs.beta;
+      int tk = 0;
+      while (t < qs.m) {
+        int p, jb, u;
+        expand_mfma_item(K, xcd_block_item(t, qs.x, sh), wc, Um, p, jb, u);
+        const int s = cld(K.exp_item_m + u);
+        const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
+        expand_mfma<E, WIDE, CO>(
+            K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[kWaves], vs_all[wave], wave, lane,
+            [&] {
+              if (threadIdx.x == 0)
+                tk = qs.Gm + __hip_atomic_fetch_add(tq, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            },
+            [&] {
+              if (threadIdx.x == 0) ticket = tk;
+            });
+        t = uniform(ticket);  // written before the item's last barrier
+      }
+      // every work-group of the XCD's set arrives once, after its last
+      // ticket (or none, past the XCD's items); the last one finds no block
+      // still taking tickets
+      if (threadIdx.x == 0 &&
+          __hip_atomic_fetch_add(dq, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == qs.Gm - 1) {
+        __hip_atomic_store(tq, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dq, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    expand_valu_items<E, WIDE, CO>(K, StaticWalk(total_v, qs.Gm * kWaves, qs.R, wave), pc, Uv, ncopy, vs, lane, sw);
   }
-  expand_valu_items<E, WIDE, CO>(K, StaticWalk(total_v, es.Gm * kWaves, es.R, wave), pc, Uv, ncopy, vs, lane, sw);
 }
 
 template <class E, bool WIDE>

@@ -133,10 +133,17 @@ constexpr int kValuItemInts = 8;
 // A launch zeroes the other bank at its start and flips E when its last
 // work-group arrives, so every launch finds its bank zeroed without any
 // reset between launches; the segment builder zeroes the whole area.
+// After the banks, the expand kernel's MBGMM item queues:
+//   queue line x         items of XCD x handed out from its queue so far
+//   queue line 8 + x     work-groups of XCD x done with their MBGMM items
+// The last work-group of an XCD to finish puts both back to zero, so every
+// launch finds them zeroed.
 constexpr int kSyncLine = 32;
 constexpr int kSyncBankLines = 9;
-constexpr int kSyncInts = kSyncLine * (1 + 2 * kSyncBankLines);
+constexpr int kQueueLines = 16;
+constexpr int kSyncInts = kSyncLine * (1 + 2 * kSyncBankLines + kQueueLines);
 LORA_HD inline int sync_bank(int b) { return kSyncLine * (1 + kSyncBankLines * b); }
+LORA_HD inline int queue_line(int l) { return kSyncLine * (1 + 2 * kSyncBankLines + l); }
 
 struct PlanLayout {
   long long seg_desc, shrink_mfma, shrink_valu, expand_mfma, expand_valu, sync, total;
@@ -297,6 +304,45 @@ LORA_HD inline ExpandSplit expand_walk_split(int total_m, int total_v, int grid,
   e.R = e.Gm > 0 ? ceil_div_i(6 * m, 10 * e.Gm) : 0;  // an MBGMM item took ~0.6 MBGMV item times
   e.first = beta < e.Gm ? lo_m + beta : e.end_m;
   e.step = e.Gm > 0 ? e.Gm : 1;
+  return e;
+}
+
+// The expand kernel's MBGMM items go to the XCDs in blocks of
+// kExpandItemBlock consecutive items (token tiles of one segment and column
+// block, which re-read the same B from that XCD's L2), block k to XCD
+// k mod 2^sh.  Handing each XCD a contiguous eighth of the list instead
+// ties its load to the ranks of the segments there: segments of rank 64
+// take twice the time of rank <= 32 ones per item.
+constexpr int kExpandItemBlock = 16;
+// items of XCD x
+LORA_HD inline int xcd_block_items(int total, int x, int sh) {
+  const int nx = 1 << sh;
+  const int nblocks = ceil_div_i(total, kExpandItemBlock);
+  if (nblocks <= x) return 0;
+  int n = ((nblocks - 1 - x) / nx + 1) * kExpandItemBlock;
+  const int rem = total % kExpandItemBlock;
+  if (rem > 0 && (nblocks - 1) % nx == x) n -= kExpandItemBlock - rem;  // the last block is short
+  return n;
+}
+// the l-th item of XCD x (l < xcd_block_items(total, x, sh))
+LORA_HD inline int xcd_block_item(int l, int x, int sh) {
+  return (((l / kExpandItemBlock) << sh) + x) * kExpandItemBlock + l % kExpandItemBlock;
+}
+// The expand kernel's split: MBGMM items of XCD x by xcd_block_items (the
+// work-groups Gm of the XCD take them from its queue), the rest as in
+// expand_walk_split.
+struct QueueSplit {
+  int Gm, R, m, x, beta;
+};
+LORA_HD inline QueueSplit expand_queue_split(int total_m, int total_v, int grid, int block) {
+  const int sh = xcd_shift(grid);
+  QueueSplit e{0, 0, 0, block & ((1 << sh) - 1), block >> sh};
+  if (total_m <= 0) return e;
+  const int G = grid >> sh;
+  e.m = xcd_block_items(total_m, e.x, sh);
+  const int third = G / 3 > 1 ? G / 3 : 1;
+  e.Gm = e.m <= 0 ? 0 : 8 * (long long)total_m >= total_v ? G : (third < e.m ? third : e.m);
+  e.R = e.Gm > 0 ? ceil_div_i(6 * e.m, 10 * e.Gm) : 0;
   return e;
 }
 

@@ -309,6 +309,68 @@ def test_plan_capacities_bound_every_item_table(tmp_path):
     assert res.returncode == 0 and res.stdout.strip().endswith("OK"), res.stdout
 
 
+QUEUE_CHECK = r"""
+#include <cstdio>
+#include <vector>
+#include "lora_plan.h"
+using namespace lora;
+int main() {
+  int bad = 0;
+  for (int sh : {0, 3}) {
+    for (int total = 0; total < 3000; total += (total < 300 ? 1 : 37)) {
+      std::vector<int> seen(total, 0);
+      const int nx = 1 << sh;
+      int sum = 0, lo = 1 << 30, hi = 0;
+      for (int x = 0; x < nx; ++x) {
+        const int m = xcd_block_items(total, x, sh);
+        sum += m; lo = m < lo ? m : lo; hi = m > hi ? m : hi;
+        for (int l = 0; l < m; ++l) {
+          const int i = xcd_block_item(l, x, sh);
+          if (i < 0 || i >= total) { printf("FAIL range sh=%d total=%d x=%d l=%d i=%d\n", sh, total, x, l, i); bad++; break; }
+          // whole blocks of consecutive items stay on one XCD
+          if ((i / kExpandItemBlock) % nx != x) { printf("FAIL xcd sh=%d total=%d\n", sh, total); bad++; break; }
+          seen[i]++;
+        }
+      }
+      for (int i = 0; i < total; ++i)
+        if (seen[i] != 1) { printf("FAIL cover sh=%d total=%d i=%d seen=%d\n", sh, total, i, seen[i]); bad++; break; }
+      if (sum != total || hi - lo > kExpandItemBlock) { printf("FAIL share sh=%d total=%d\n", sh, total); bad++; }
+      // every work-group of an XCD's MBGMM set finds the same split
+      for (int grid : {8, 64, 768}) {
+        if ((grid % 8 == 0 ? 3 : 0) != sh) continue;
+        for (int tv : {0, total / 2, 100 * total + 1}) {
+          for (int x = 0; x < nx; ++x) {
+            const QueueSplit a = expand_queue_split(total, tv, grid, x), b = expand_queue_split(total, tv, grid, grid - nx + x);
+            if (a.Gm != b.Gm || a.m != b.m || a.x != x || b.x != x || (a.m > 0) != (a.Gm > 0) || a.Gm > grid / nx) {
+              printf("FAIL split total=%d tv=%d grid=%d x=%d\n", total, tv, grid, x); bad++;
+            }
+          }
+        }
+      }
+    }
+  }
+  printf(bad ? "FAILED\n" : "OK\n");
+  return bad != 0;
+}
+"""
+
+
+def test_expand_queue_blocks_cover_every_item_once(tmp_path):
+    """The expand kernel's MBGMM item queues: the blocks dealt over the XCDs
+    cover every item of the list exactly once, whole blocks stay on one XCD,
+    the XCDs' shares differ by at most one block, and every work-group of an
+    XCD computes the same split (the queue's arrival count relies on it).
+    Compiled from the plan header with the host compiler."""
+    import subprocess
+    src = tmp_path / "queue_check.cpp"
+    src.write_text(QUEUE_CHECK)
+    exe = tmp_path / "queue_check"
+    inc = os.path.join(ROOT, "heterogeneous_adapters_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O1", f"-I{inc}", str(src), "-o", str(exe)], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert res.returncode == 0 and res.stdout.strip().endswith("OK"), res.stdout
+
+
 def test_noalloc_refuses_batches_beyond_its_array():
     """lora_apply_noalloc sizes the call before anything else: a batch whose
     workspace exceeds the library's fixed array is refused with WORKSPACE

@@ -576,6 +576,49 @@ def test_graph_capture_replays_match_eager():
             assert np.array_equal(batch.device_to_host(b.Y[p]), Yref[p]), (rep, p)
 
 
+def test_prefill_item_queues_repeat_and_replay():
+    """A prefill batch (32 sequences, 38,781 tokens: about six MBGMM expand
+    items per work-group) takes the expand kernel's per-XCD item queues,
+    whose counters the last work-group of each XCD puts back to zero.  Calls
+    in a row on one segment buffer built once (the builder would zero the
+    counters), and graph replays of the call, must each produce every row: Y
+    is overwritten with NaN before every call and must come out bit-identical
+    to the first call's."""
+    w = W.make_workload(3, keep_dense=False)
+    b = batch.to_device(w)
+    segs = lora.Segments(w.T, w.N)
+    projs = [b.proj(p) for p in range(w.n_projs)]
+    ws = lora.workspace(w.T, w.N, w.n_projs, max(t.d_in for t in w.tables))
+    lora.lora_build_segments(b.ids, b.adapters, segs, lora.workspace(w.T, w.N, 0, 0))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    first = None
+    for rep in range(3):
+        for y in b.Y:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            lora.lora_apply(None, segs, w.T, projs, b.adapters, b.pool, ws, side)
+        torch.cuda.synchronize()
+        got = [y.clone() for y in b.Y]
+        if first is None:
+            first = got
+            assert all(not torch.isnan(y.float()).any() for y in got)
+        else:
+            assert all(torch.equal(a.view(torch.int16), c.view(torch.int16)) for a, c in zip(got, first)), rep
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        lora.lora_apply(None, segs, w.T, projs, b.adapters, b.pool, ws, side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for y in b.Y:
+            y.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a.view(torch.int16), c.view(torch.int16)) for a, c in zip(b.Y, first)), ("replay", rep)
+
+
 def test_padded_slot_layout_matches_unpadded():
     """The fixed-rank (padded) layout through the same kernels gives the same
     Y as the heterogeneous-rank layout, within the bf16 tolerance, and both
