@@ -223,6 +223,13 @@ PARITY_CASES = {
     # continuous batching: prefill chunks (MBGMM) beside decode tokens (MBGMV)
     "mixed": (5, dict(nchunks=3, chunk_lo=40, chunk_hi=120, ndecode=300, N=50, page_width=512,
                       projs=(("a", 1024, 1536),))),
+    # prefill batches with more than three MBGMM expand items per block of the
+    # grid (the expand kernel's per-XCD queues): fp32 (2196 items for 512
+    # blocks), and bf16 with a ragged last column block (2525 items for 768)
+    "prefill_queues_f32": (3, dict(dtype="f32", nseq=8, len_lo=600, len_hi=900, N=6, page_width=1024,
+                                   projs=(("a", 512, 11008),))),
+    "prefill_queues_ragged_bf16": (3, dict(nseq=12, len_lo=500, len_hi=900, N=7, page_width=512,
+                                           projs=(("a", 520, 9000),))),
 }
 
 
