@@ -193,13 +193,18 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
+MI355X_CUS, MI355X_XCDS = 256, 8  # compute units, and the XCDs they sit in
+
+
 def derived_counter_lines(per):
     """Ratios of counters read in one pass, per kernel (mean over dispatches):
     instructions per wave (SQ_INSTS_* / SQ_WAVES), the L2 read latency seen
     by the vector caches (TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ, in
     cycles), the share of L2 cycles with reads to DRAM stalled for credits,
     reads to DRAM in flight per L2 channel (RDREQ_LEVEL / TCC_CYCLE, both
-    summed over the channels), and the L2 hit rate."""
+    summed over the channels), the L2 hit rate, and the share of a CU's busy
+    cycles its vector L1 / texture units spent stalled (per CU, over
+    GRBM_GUI_ACTIVE per XCD)."""
     import numpy as np
     mean = {}
     for (name, ctr), disp in per.items():
@@ -223,6 +228,17 @@ def derived_counter_lines(per):
                 ratios.append(("dram_reads_in_flight_per_channel", m["TCC_EA0_RDREQ_LEVEL_sum"] / m["TCC_CYCLE_sum"]))
         if m.get("TCC_HIT_sum", 0) + m.get("TCC_MISS_sum", 0) > 0 and "TCC_HIT_sum" in m and "TCC_MISS_sum" in m:
             ratios.append(("l2_hit_rate", m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"])))
+        if m.get("GRBM_GUI_ACTIVE"):
+            # per-CU counters (summed over the CUs) over the dispatch's busy
+            # cycles (GRBM_GUI_ACTIVE, summed over the XCDs)
+            cyc = m["GRBM_GUI_ACTIVE"] / MI355X_XCDS
+            for ctr, key in (("TCP_PENDING_STALL_CYCLES", "tcp_pending_stall_share"),
+                             ("TCP_TCP_TA_DATA_STALL_CYCLES", "tcp_ta_data_stall_share"),
+                             ("TD_TC_STALL", "td_tc_stall_share"), ("TD_TD_BUSY", "td_busy_share"),
+                             ("TA_DATA_STALLED_BY_TC_CYCLES", "ta_data_stalled_by_tc_share"),
+                             ("TA_ADDR_STALLED_BY_TC_CYCLES", "ta_addr_stalled_by_tc_share")):
+                if ctr in m:
+                    ratios.append((key, m[ctr] / MI355X_CUS / cyc))
         out.extend(f"{key} {val:.4g}  {short}" for key, val in ratios)
     return out
 

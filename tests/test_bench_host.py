@@ -145,6 +145,17 @@ def test_counter_read_in_two_runs_is_averaged_not_added(tmp_path, capsys):
     assert f"per_wave_valu 2000  {APPLY}" in out and f"per_wave_salu 4000  {APPLY}" in out
 
 
+def test_per_cu_stall_shares(tmp_path, capsys):
+    """Per-CU stall counters are summed over 256 CUs and GRBM_GUI_ACTIVE over
+    8 XCDs: 256 CUs each stalled half of 1000 busy cycles read as 0.5."""
+    _write_csv(tmp_path / "r_counter_collection.csv", ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"],
+               [[1, APPLY, "GRBM_GUI_ACTIVE", 8 * 1000.0], [1, APPLY, "TCP_PENDING_STALL_CYCLES", 256 * 500.0],
+                [1, APPLY, "TD_TD_BUSY", 256 * 250.0]])
+    bench.summarize_profile([str(tmp_path)], "")
+    out = capsys.readouterr().out
+    assert f"tcp_pending_stall_share 0.5  {APPLY}" in out and f"td_busy_share 0.25  {APPLY}" in out
+
+
 def test_only_byte_counters_are_calibrated(tmp_path, capsys):
     """Counters other than FETCH_SIZE / WRITE_SIZE read on the calibration
     copy are reported as read, never turned into bytes."""
