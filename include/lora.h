@@ -237,7 +237,11 @@ lora_status_t lora_shrink(const lora_proj_t* projs, int32_t n_projs, const lora_
  * v as written by lora_shrink.  v_slices: 0 -> lora_v_slices(d_in_i) slices
  * for projection i (what lora_shrink wrote); k >= 1 -> k slices for every
  * projection (k = 1: v given whole).  Rows of tokens without an adapter
- * receive Y_base.  Errors as lora_shrink. */
+ * receive Y_base.  With at least three MBGMM expand items per work-group of
+ * the grid (prefill batches) the launch hands out its items through queues
+ * in the segment buffer, which its last work-groups put back to zero: calls
+ * that share one segment buffer must not run concurrently.  Errors as
+ * lora_shrink. */
 lora_status_t lora_expand(const lora_proj_t* projs, int32_t n_projs, const lora_adapters_t* adapters,
                           const lora_segments_t* segs, const lora_pool_t* pool, const float* const* v,
                           int32_t v_slices, int64_t v_stride, void* stream);
@@ -254,8 +258,10 @@ lora_status_t lora_expand(const lora_proj_t* projs, int32_t n_projs, const lora_
  * grid's, and run the expand) or the two launches of lora_shrink and
  * lora_expand -- see lora_set_launch_mode; the arithmetic, and Y, are the
  * same bit for bit.  The single launch keeps its wait's bookkeeping in the
- * segment buffer, so calls that share one segment buffer must not run
- * concurrently (issue them on one stream).
+ * segment buffer, and so does the expand launch of a large batch (per-XCD
+ * item queues, from three MBGMM expand items per work-group of its grid),
+ * so calls that share one segment buffer must not run concurrently (issue
+ * them on one stream).
  *   ids != NULL, segs != NULL : build segments into *segs, then apply
  *   ids != NULL, segs == NULL : build segments inside the workspace
  *   ids == NULL, segs != NULL : reuse prebuilt segments (built by
