@@ -1655,15 +1655,25 @@ __device__ __forceinline__ void expand_phase(const KArgs& K, const PlanCounts& p
       const int sh = xcd_shift(grid);
       int* tq = K.sync + queue_line(qs.x);
       int* dq = K.sync + queue_line(8 + qs.x);
+      // The XCD's last Gm items (about one per block: the last round) are
+      // handed out in halves of their columns, so that the blocks finish
+      // within about half an item of each other: tickets [0, split) are
+      // items, tickets from split are half items.
+      const int split = qs.m - min(qs.Gm, qs.m);
+      const int tickets = 2 * qs.m - split;
       int t = qs.beta;
       int tk = 0;
-      while (t < qs.m) {
+      while (t < tickets) {
         int p, jb, u;
-        expand_mfma_item(K, xcd_block_item(t, qs.x, sh), wc, Um, p, jb, u);
+        const int h = t < split ? -1 : (t - split) & 1;
+        const int li = t < split ? t : split + ((t - split) >> 1);
+        expand_mfma_item(K, xcd_block_item(li, qs.x, sh), wc, Um, p, jb, u);
         const int s = cld(K.exp_item_m + u);
         const int4 d0 = cld4(K.seg_desc + 2 * s), d1 = cld4(K.seg_desc + 2 * s + 1);
+        // half h of column block jb at width wc is column block 2 jb + h at wc / 2
         expand_mfma<E, WIDE, CO>(
-            K, K.p[p], jb, wc, d0, d1, u - d1.z, vs_all[kWaves], vs_all[wave], wave, lane,
+            K, K.p[p], h < 0 ? jb : 2 * jb + h, h < 0 ? wc : wc >> 1, d0, d1, u - d1.z, vs_all[kWaves], vs_all[wave],
+            wave, lane,
             [&] {
               if (threadIdx.x == 0)
                 tk = qs.Gm + __hip_atomic_fetch_add(tq, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
