@@ -179,6 +179,14 @@ def _last_adapter_long_ids():
     ids = np.concatenate([np.full(300, 4, np.int32), np.arange(100, dtype=np.int32) % 4])
     return np.random.default_rng(17).permutation(ids).astype(np.int32)
 
+def _prefill_base_only_ids():
+    """14 sequences of 600 tokens over 7 adapters, two of them base-model
+    sequences (id -1), plus 40 scattered base-model tokens."""
+    ids = np.concatenate([np.full(600, -1 if q in (3, 9) else q % 7, np.int32) for q in range(14)])
+    ids[np.random.default_rng(23).choice(len(ids), 40, replace=False)] = -1
+    return ids
+
+
 PARITY_CASES = {
     "cfg0": (0, {}),
     "cfg1": (1, {}),
@@ -230,6 +238,9 @@ PARITY_CASES = {
                                    projs=(("a", 512, 11008),))),
     "prefill_queues_ragged_bf16": (3, dict(nseq=12, len_lo=500, len_hi=900, N=7, page_width=512,
                                            projs=(("a", 520, 9000),))),
+    # the same queues beside copy items: base-model rows written out of place
+    "prefill_queues_base_only": (3, dict(N=7, page_width=512, ids_override=_prefill_base_only_ids(),
+                                         projs=(("a", 520, 11008),))),
 }
 
 
